@@ -1,0 +1,141 @@
+"""Rotary position embedding (RoPE): frequencies, the FP32 table, rotations.
+
+Test infrastructure only (see the package header).
+
+What the pages fix and what this module reads into them:
+
+* RoPE runs in FP32 and is cast back to the activation dtype before QK^T
+  ("Fixes the medium DiT's FP16-mixed ONNX ..." discussion, section "The bug").
+* The cos/sin values come from a table computed on the host in FP32 and frozen
+  ahead of time, with no trig in the graph (sa3_trt README, section "DiT
+  precision", fp8 tier). The table is sized to a maximum length.
+* A bf16 angle at about 4155 rad has a spacing of 32 rad, more than 2*pi, which
+  destroys position information; this is why RoPE must stay FP32 (sa3_trt README,
+  section "DiT precision", the retired bf16 tier; TensorRT engines README,
+  section "Other things worth knowing").
+
+Readings where the pages are silent (each listed in the design notes):
+
+* pairs are adjacent, (x[2i], x[2i+1]), over the full head dim;
+* theta_i = base ** (-2 i / D), i = 0 .. D/2-1, base 10000;
+* positions are m = 0 .. L-1 with no offset;
+* the FP32 table is one rounding of the fp64 value cos(fp64(m) * theta_i);
+* the FP32 rotation is r0 = fl(fl(x0 c) - fl(x1 s)), r1 = fl(fl(x0 s) + fl(x1 c)),
+  each product and sum rounded to FP32 separately (no fused multiply-add);
+* the cast back to the IO dtype rounds to nearest-even.
+
+Parity: rope_frequencies, rope_table_f32, rotate_def and rotate_method are pinned in
+tests/test_oracle_rope.py by closed forms (theta_0 = 1, theta_31 = 10^-3.875 at D=64,
+m = 0 is the identity, D = 2 rotates by m rad), by invariants (each pair's norm is
+preserved; <R_m q, R_n k> depends only on n - m), by the pure-Python brute force
+(math.cos / exact Fraction rounding), and by the bf16-angle negative control.
+"""
+
+import numpy as np
+
+from .rounding import f32, round_io, f32_to_bf16_bits, bf16_bits_to_f64
+
+__all__ = [
+    "rope_frequencies",
+    "rope_angles",
+    "rope_table_f32",
+    "rope_table_bf16_angle",
+    "rotate_def",
+    "rotate_f32",
+    "rotate_method",
+]
+
+
+def rope_frequencies(D, base=10000.0):
+    """theta_i = base ** (-2 i / D) for i = 0 .. D/2 - 1, in fp64."""
+    if D < 2 or D % 2:
+        raise ValueError("D must be even and >= 2")
+    i = np.arange(D // 2, dtype=np.float64)
+    return np.power(np.float64(base), -2.0 * i / D)
+
+
+def rope_angles(L, D, base=10000.0):
+    """phi[m, i] = m * theta_i for m = 0 .. L-1, fp64, shape [L, D/2]."""
+    m = np.arange(L, dtype=np.float64)
+    return m[:, None] * rope_frequencies(D, base)[None, :]
+
+
+def rope_table_f32(L, D, base=10000.0):
+    """The host FP32 cos/sin table: fp32(cos(phi)), fp32(sin(phi)), each [L, D/2].
+
+    One rounding from the fp64 value (sa3_trt README, section "DiT precision":
+    position cos/sin computed host-side and frozen as a constant).
+    """
+    phi = rope_angles(L, D, base)
+    return f32(np.cos(phi)), f32(np.sin(phi))
+
+
+def rope_table_bf16_angle(L, D, base=10000.0):
+    """Negative control: the table a bf16-evaluated angle produces.
+
+    Position, frequency and their product are each rounded to bf16 before the
+    trig, as a weakly typed bf16 graph would do (sa3_trt README, section "DiT
+    precision", retired bf16 tier). Returned as fp32 cos/sin plus the bf16 angle.
+    """
+    def bf(x):
+        return bf16_bits_to_f64(f32_to_bf16_bits(f32(x)))
+
+    m = bf(np.arange(L, dtype=np.float64))
+    th = bf(rope_frequencies(D, base))
+    phi = bf(m[:, None] * th[None, :])
+    return f32(np.cos(phi)), f32(np.sin(phi)), phi
+
+
+def _pairs(x):
+    return x[..., 0::2], x[..., 1::2]
+
+
+def _interleave(r0, r1):
+    out = np.empty(r0.shape[:-1] + (2 * r0.shape[-1],), dtype=r0.dtype)
+    out[..., 0::2] = r0
+    out[..., 1::2] = r1
+    return out
+
+
+def rotate_def(x, cos, sin):
+    """Exact-math rotation of adjacent pairs in fp64.
+
+    x: [..., L, D] fp64; cos, sin: [>=L, D/2] (any float dtype, widened to fp64).
+    r[2i] = x[2i] c - x[2i+1] s ; r[2i+1] = x[2i] s + x[2i+1] c.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    L = x.shape[-2]
+    c = np.asarray(cos, dtype=np.float64)[:L]
+    s = np.asarray(sin, dtype=np.float64)[:L]
+    x0, x1 = _pairs(x)
+    return _interleave(x0 * c - x1 * s, x0 * s + x1 * c)
+
+
+def rotate_f32(x, cos32, sin32):
+    """The method's FP32 rotation, before the cast back: returns float32 [..., L, D].
+
+    x: [..., L, D] values exactly representable in FP32 (fp64 array); cos32, sin32:
+    the FP32 table [>=L, D/2]. Every product and sum is an FP32 operation rounded on
+    its own (numpy float32 ufuncs, no fusion):
+    r0 = fl(fl(x0 c) - fl(x1 s)), r1 = fl(fl(x0 s) + fl(x1 c)).
+    """
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    L = x32.shape[-2]
+    c = np.asarray(cos32, dtype=np.float32)[:L]
+    s = np.asarray(sin32, dtype=np.float32)[:L]
+    x0, x1 = _pairs(x32)
+    a = np.multiply(x0, c, dtype=np.float32)
+    b = np.multiply(x1, s, dtype=np.float32)
+    r0 = np.subtract(a, b, dtype=np.float32)
+    a = np.multiply(x0, s, dtype=np.float32)
+    b = np.multiply(x1, c, dtype=np.float32)
+    r1 = np.add(a, b, dtype=np.float32)
+    return _interleave(r0, r1)
+
+
+def rotate_method(x, cos32, sin32, io):
+    """The method's rotation: FP32 arithmetic (rotate_f32), then RNE cast to ``io``.
+
+    Returns the IO-dtype values widened to fp64.
+    """
+    return round_io(rotate_f32(x, cos32, sin32), io)
