@@ -1,0 +1,143 @@
+/*
+ * sa3attn.h -- C ABI of the fused RoPE attention core for AMD MI355X (gfx950).
+ *
+ * The operation is the attention core of the Stable Audio 3 transformers:
+ *
+ *   q' = cast_io(RoPE_fp32(q)),  k' = cast_io(RoPE_fp32(k))
+ *   out = softmax(scale * q' k'^T + M) v                        (plain)
+ *   out = softmax(scale * q1' k1'^T + M) v
+ *         - lambda * softmax(scale * q2' k2'^T + M) v           (differential)
+ *
+ * Sources (the pages describing the method):
+ *  - RoPE is computed in FP32 and cast back to the activation dtype before QK^T;
+ *    attention then runs on FP16 inputs with the softmax accumulated in FP32
+ *    inside the fused kernel ("Fixes the medium DiT's FP16-mixed ONNX so the
+ *    attention core runs FP16" discussion, sections "The bug" and "The fix").
+ *  - The cos/sin table is computed on the host in FP32 and frozen as a constant,
+ *    sized to a maximum length (sa3_trt README, section "DiT precision").
+ *  - M is a sliding window of half-width w, "+-WINDOW" around each query
+ *    (Stable Audio 3 TensorRT engines README, section "Building your own").
+ *  - The differential variant shares V between two softmax branches and subtracts
+ *    in FP32 on FP32 accumulators (same README, section "How the kernels differ").
+ *  - The forward must be capturable into a stream graph with no host callbacks
+ *    (same README, section "Why JIT breaks on sm_120").
+ *
+ * Conventions shared by every entry point
+ *  - Layout: every tensor is row-major contiguous [B][H][L][D], D fastest.
+ *    Differential q and k are stacked [2][B][H][L][D] (branch 1, then branch 2);
+ *    v is [B][H][L][D] and shared by both branches.
+ *  - RoPE rotates adjacent pairs (x[2i], x[2i+1]) at position m = 0..L-1 of each
+ *    (b, h) slab: r0 = fl(fl(x0 c) - fl(x1 s)), r1 = fl(fl(x0 s) + fl(x1 c)) in FP32,
+ *    then rounds to nearest-even to the IO dtype.
+ *  - cos, sin: FP32 tables [L_tab][D/2], L_tab >= L; row m holds cos(m theta_i) and
+ *    sin(m theta_i), shared across B and H. Only rows < L are read. The library
+ *    cannot check L_tab: passing a shorter table is a caller error.
+ *  - window: half-width w; key j is masked for query i when |i - j| > w.
+ *    window < 0 means full attention. There is no causal mask.
+ *  - scale multiplies the FP32 QK^T accumulator (not folded into q).
+ *  - Ownership: the caller allocates and owns every buffer (device memory for
+ *    q, k, v, cos, sin, out). The library never allocates, frees or synchronises
+ *    and keeps no pointer after returning. Work is enqueued on `stream`
+ *    (a hipStream_t; NULL = the default stream) and can be captured into a graph.
+ *  - out must not overlap any input.
+ *  - Errors: validation runs before any launch; on error nothing is enqueued and
+ *    `out` is untouched. Status codes are below; sa3attn_status_string() names them.
+ *  - Thread safety: calls may be made from several threads; the only shared state
+ *    is a per-device capability cache filled once.
+ *  - Supported: D = 64, IO dtype fp16 or bf16, out dtype fp16, bf16 or fp32,
+ *    1 <= L <= 16777216, and grid size (ceil(L/tile) * B * H) below 2^31.
+ *  - Numerics: QK^T and P.V run on MFMA with FP32 accumulation; the running
+ *    softmax max and sum are FP32. P is rounded to fp16 before P.V for both IO
+ *    dtypes; with bf16 inputs V is converted to fp16 as it is staged, which is
+ *    exact for |v| in [2^-14, 65504]; a bf16 |v| above 65504 overflows to inf and
+ *    makes the affected outputs non-finite.
+ */
+#ifndef SA3ATTN_H
+#define SA3ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SA3ATTN_VERSION_MAJOR 0
+#define SA3ATTN_VERSION_MINOR 1
+
+/* Status codes. */
+enum {
+    SA3_OK = 0,
+    SA3_ERR_NULL = -1,         /* a required pointer is NULL                          */
+    SA3_ERR_SHAPE = -2,        /* B, H, L or D < 1, D odd, or a size overflows        */
+    SA3_ERR_UNSUPPORTED = -3,  /* D != 64, or an unknown dtype                         */
+    SA3_ERR_ARG = -4,          /* non-finite scale or lambda, or out overlaps an input */
+    SA3_ERR_DEVICE = -5,       /* no HIP device, or the current device is not gfx950  */
+    SA3_ERR_LAUNCH = -6        /* the kernel launch failed (hipGetLastError)          */
+};
+
+/* Element types. */
+enum { SA3_F16 = 0, SA3_BF16 = 1, SA3_F32 = 2 };
+
+/*
+ * sa3attn_forward -- fp16 q/k/v in, fp16 out.
+ * Differential exactly when lambda != 0; then q and k point to stacked
+ * [2][B][H][L][D] buffers. Returns a status code.
+ */
+int sa3attn_forward(const void *q, const void *k, const void *v,
+                    const float *cos, const float *sin, void *out,
+                    int B, int H, int L, int D,
+                    int window, float lambda, float scale, void *stream);
+
+/* sa3attn_forward_bf16 -- the same arguments and rules, bf16 in and bf16 out. */
+int sa3attn_forward_bf16(const void *q, const void *k, const void *v,
+                         const float *cos, const float *sin, void *out,
+                         int B, int H, int L, int D,
+                         int window, float lambda, float scale, void *stream);
+
+/*
+ * sa3attn_desc / sa3attn_forward_ex -- the explicit form.
+ *   dtype:        SA3_F16 or SA3_BF16 (q, k, v)
+ *   out_dtype:    SA3_F16, SA3_BF16 or SA3_F32
+ *   differential: 0 = plain; 1 = two branches (q, k stacked), independent of
+ *                 lambda, so lambda = 0 still runs both branches.
+ * Other fields as in sa3attn_forward.
+ */
+typedef struct sa3attn_desc {
+    const void *q;
+    const void *k;
+    const void *v;
+    const float *cos;
+    const float *sin;
+    void *out;
+    int B, H, L, D;
+    int window;
+    float lambda;
+    float scale;
+    int dtype;
+    int out_dtype;
+    int differential;
+    void *stream;
+} sa3attn_desc;
+
+int sa3attn_forward_ex(const sa3attn_desc *desc);
+
+/*
+ * sa3attn_rope_table -- fill a host FP32 cos/sin table [L][D/2].
+ * theta_i = base^(-2i/D) (the double nearest the real value, from an
+ * extended-precision power); entry [m][i] = fp32(cos(m * theta_i)) and
+ * fp32(sin(m * theta_i)), each one rounding of the fp64 value (sa3_trt README,
+ * section "DiT precision": host-computed FP32 table). cos and sin are host
+ * pointers to L*D/2 floats owned by the caller. Returns SA3_OK, SA3_ERR_NULL,
+ * SA3_ERR_SHAPE (L < 1, D < 2 or odd) or SA3_ERR_ARG (base not finite and > 0).
+ */
+int sa3attn_rope_table(float *cos, float *sin, int L, int D, double base);
+
+/* sa3attn_status_string -- a static, human-readable name for a status code. */
+const char *sa3attn_status_string(int status);
+
+/* sa3attn_version -- (major << 16) | minor of the library that is loaded. */
+int sa3attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SA3ATTN_H */

@@ -17,7 +17,8 @@ What the pages fix and what this module reads into them:
 Readings where the pages are silent (each listed in the design notes):
 
 * pairs are adjacent, (x[2i], x[2i+1]), over the full head dim;
-* theta_i = base ** (-2 i / D), i = 0 .. D/2-1, base 10000;
+* theta_i = base ** (-2 i / D), i = 0 .. D/2-1, base 10000, as the fp64 value
+  nearest the real number;
 * positions are m = 0 .. L-1 with no offset;
 * the FP32 table is one rounding of the fp64 value cos(fp64(m) * theta_i);
 * the FP32 rotation is r0 = fl(fl(x0 c) - fl(x1 s)), r1 = fl(fl(x0 s) + fl(x1 c)),
@@ -30,6 +31,8 @@ m = 0 is the identity, D = 2 rotates by m rad), by invariants (each pair's norm 
 preserved; <R_m q, R_n k> depends only on n - m), by the pure-Python brute force
 (math.cos / exact Fraction rounding), and by the bf16-angle negative control.
 """
+
+import decimal
 
 import numpy as np
 
@@ -47,11 +50,19 @@ __all__ = [
 
 
 def rope_frequencies(D, base=10000.0):
-    """theta_i = base ** (-2 i / D) for i = 0 .. D/2 - 1, in fp64."""
+    """theta_i = base ** (-2 i / D) for i = 0 .. D/2 - 1: the fp64 value nearest the real one.
+
+    Evaluated with 50-digit decimal arithmetic and rounded once to fp64, so the value
+    does not depend on which libm pow() is at hand (two common ones differ in the last
+    bit for some i, which moves fp32 table entries at large positions).
+    """
     if D < 2 or D % 2:
         raise ValueError("D must be even and >= 2")
-    i = np.arange(D // 2, dtype=np.float64)
-    return np.power(np.float64(base), -2.0 * i / D)
+    with decimal.localcontext() as ctx:
+        ctx.prec = 50
+        b = decimal.Decimal(float(base))
+        return np.array([float(b ** (decimal.Decimal(-2 * i) / decimal.Decimal(D))) for i in range(D // 2)],
+                        dtype=np.float64)
 
 
 def rope_angles(L, D, base=10000.0):

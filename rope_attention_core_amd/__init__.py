@@ -1,0 +1,196 @@
+"""Fused RoPE attention core for AMD MI355X (gfx950): Python binding.
+
+The work happens in libsa3attn.so (hand-written HIP kernels behind a C ABI, see
+include/sa3attn.h). This module only marshals torch tensors into that ABI: device
+pointers, sizes and the current HIP stream. PyTorch provides device memory and
+streams; it computes nothing on this path. If the library has not been built the
+calls raise; there is no fallback implementation.
+
+    import rope_attention_core_amd as sa3
+    cos, sin = sa3.rope_table(L, 64)                  # host FP32 table
+    out = sa3.forward(q, k, v, cos.cuda(), sin.cuda())
+"""
+
+import ctypes
+import os
+
+__all__ = [
+    "forward", "forward_short", "rope_table", "status_string", "version", "library_path",
+    "load_library", "SA3Error", "F16", "BF16", "F32", "EXPORTS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libsa3attn.so")
+
+F16, BF16, F32 = 0, 1, 2
+EXPORTS = (
+    "sa3attn_forward",
+    "sa3attn_forward_bf16",
+    "sa3attn_forward_ex",
+    "sa3attn_rope_table",
+    "sa3attn_status_string",
+    "sa3attn_version",
+)
+
+
+class SA3Error(RuntimeError):
+    """A non-zero status returned by the library."""
+
+    def __init__(self, code, what):
+        self.code = code
+        super().__init__(f"{what}: {status_string(code)} ({code})")
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("cos", ctypes.c_void_p), ("sin", ctypes.c_void_p), ("out", ctypes.c_void_p),
+        ("B", ctypes.c_int), ("H", ctypes.c_int), ("L", ctypes.c_int), ("D", ctypes.c_int),
+        ("window", ctypes.c_int), ("lambda_", ctypes.c_float), ("scale", ctypes.c_float),
+        ("dtype", ctypes.c_int), ("out_dtype", ctypes.c_int), ("differential", ctypes.c_int),
+        ("stream", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libsa3attn.so (once) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                           "`python -c 'import __graft_entry__ as g; g.build()'` "
+                           "or `python -m rope_attention_core_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    for name in ("sa3attn_forward", "sa3attn_forward_bf16"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, f, vp]
+        fn.restype = i
+    lib.sa3attn_forward_ex.argtypes = [ctypes.POINTER(_Desc)]
+    lib.sa3attn_forward_ex.restype = i
+    lib.sa3attn_rope_table.argtypes = [vp, vp, i, i, ctypes.c_double]
+    lib.sa3attn_rope_table.restype = i
+    lib.sa3attn_status_string.argtypes = [i]
+    lib.sa3attn_status_string.restype = ctypes.c_char_p
+    lib.sa3attn_version.argtypes = []
+    lib.sa3attn_version.restype = i
+    _lib = lib
+    return lib
+
+
+def status_string(code):
+    return load_library().sa3attn_status_string(int(code)).decode()
+
+
+def version():
+    v = load_library().sa3attn_version()
+    return (v >> 16, v & 0xFFFF)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dt_code(dtype):
+    torch = _torch()
+    if dtype == torch.float16:
+        return F16
+    if dtype == torch.bfloat16:
+        return BF16
+    if dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {dtype}")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream_handle(stream, device):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def rope_table(L, D=64, base=10000.0):
+    """Host FP32 cos/sin table [L, D/2] filled by the library (sa3attn_rope_table)."""
+    torch = _torch()
+    cos = torch.empty((L, D // 2), dtype=torch.float32)
+    sin = torch.empty((L, D // 2), dtype=torch.float32)
+    rc = load_library().sa3attn_rope_table(_ptr(cos), _ptr(sin), int(L), int(D), float(base))
+    if rc != 0:
+        raise SA3Error(rc, "sa3attn_rope_table")
+    return cos, sin
+
+
+def forward(q, k, v, cos, sin, *, window=-1, lam=0.0, scale=None, out=None, out_dtype=None,
+            differential=None, stream=None):
+    """Run the fused core through sa3attn_forward_ex.
+
+    q, k: [B, H, L, D] (plain) or [2, B, H, L, D] (differential), fp16 or bf16, on the
+    GPU and contiguous; v: [B, H, L, D], same dtype; cos, sin: FP32 [>=L, D/2] on the
+    GPU. ``differential`` defaults to q.dim() == 5. ``out_dtype`` defaults to the IO
+    dtype; ``scale`` to 1/sqrt(D). Returns ``out`` (allocated if not given).
+    """
+    torch = _torch()
+    if differential is None:
+        differential = q.dim() == 5
+    B, H, L, D = v.shape
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else v.dtype
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    if out is None:
+        out = torch.empty((B, H, L, D), dtype=out_dtype, device=v.device)
+    want_qk = (2, B, H, L, D) if differential else (B, H, L, D)
+    for name, t, shape in (("q", q, want_qk), ("k", k, want_qk), ("out", out, (B, H, L, D))):
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+    for name, t in (("q", q), ("k", k), ("v", v), ("cos", cos), ("sin", sin), ("out", out)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dtype != v.dtype or k.dtype != v.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    if cos.dtype != torch.float32 or sin.dtype != torch.float32:
+        raise TypeError("cos and sin must be float32")
+    if cos.dim() != 2 or cos.shape[0] < L or cos.shape[1] != D // 2 or tuple(sin.shape) != tuple(cos.shape):
+        raise ValueError(f"cos/sin must be [>= {L}, {D // 2}]")
+    if out.dtype != out_dtype:
+        raise TypeError("out dtype does not match out_dtype")
+    d = _Desc(_ptr(q), _ptr(k), _ptr(v), _ptr(cos), _ptr(sin), _ptr(out),
+              B, H, L, D, int(window), float(lam), float(scale),
+              _dt_code(v.dtype), _dt_code(out.dtype), 1 if differential else 0,
+              _stream_handle(stream, v.device))
+    rc = load_library().sa3attn_forward_ex(ctypes.byref(d))
+    if rc != 0:
+        raise SA3Error(rc, "sa3attn_forward_ex")
+    return out
+
+
+def forward_short(q, k, v, cos, sin, out, *, window=-1, lam=0.0, scale=None, stream=None):
+    """Call the short entry points (sa3attn_forward / sa3attn_forward_bf16) directly.
+
+    Output dtype equals the IO dtype; differential exactly when lam != 0.
+    """
+    torch = _torch()
+    B, H, L, D = v.shape
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    lib = load_library()
+    fn = lib.sa3attn_forward_bf16 if v.dtype == torch.bfloat16 else lib.sa3attn_forward
+    rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(cos), _ptr(sin), _ptr(out), B, H, L, D,
+            int(window), float(lam), float(scale), _stream_handle(stream, v.device))
+    if rc != 0:
+        raise SA3Error(rc, fn.__name__)
+    return out

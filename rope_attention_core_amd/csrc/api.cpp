@@ -1,0 +1,163 @@
+// C-ABI entry points of the fused RoPE attention core (declared in include/sa3attn.h):
+// argument validation, device capability check, dispatch to the gfx950 kernels.
+//
+// Validation happens before anything touches the GPU so that a bad call enqueues
+// nothing and leaves `out` untouched; a failure is never reported as zeros (the
+// Stable Audio 3 TensorRT engines README, section "Building your own", lists
+// silent-zero and wrong-argument-order failures of the kernels it describes).
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "sa3attn.h"
+#include "sa3attn_internal.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int kMaxL = 1 << 24;
+// 0 = not checked yet, 1 = gfx950, 2 = something else
+std::atomic<int> g_dev_ok[kMaxDevices];
+
+int check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return SA3_ERR_DEVICE;
+    }
+    if (dev >= kMaxDevices) return SA3_ERR_DEVICE;
+    int s = g_dev_ok[dev].load(std::memory_order_acquire);
+    if (s == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return SA3_ERR_DEVICE;
+        }
+        s = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_dev_ok[dev].store(s, std::memory_order_release);
+    }
+    return s == 1 ? SA3_OK : SA3_ERR_DEVICE;
+}
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+int forward_impl(const sa3attn_desc *d) {
+    if (!d) return SA3_ERR_NULL;
+    if (!d->q || !d->k || !d->v || !d->cos || !d->sin || !d->out) return SA3_ERR_NULL;
+    if (d->B < 1 || d->H < 1 || d->L < 1 || d->D < 1 || (d->D & 1)) return SA3_ERR_SHAPE;
+    if (d->L > kMaxL) return SA3_ERR_SHAPE;
+    if (d->D != 64) return SA3_ERR_UNSUPPORTED;
+    if (d->dtype != SA3_F16 && d->dtype != SA3_BF16) return SA3_ERR_UNSUPPORTED;
+    if (d->out_dtype != SA3_F16 && d->out_dtype != SA3_BF16 && d->out_dtype != SA3_F32)
+        return SA3_ERR_UNSUPPORTED;
+    if (d->differential != 0 && d->differential != 1) return SA3_ERR_ARG;
+    if (!std::isfinite(d->scale) || !std::isfinite(d->lambda)) return SA3_ERR_ARG;
+
+    // sizes in elements / bytes, with overflow checks
+    const unsigned long long bh = (unsigned long long)d->B * (unsigned long long)d->H;
+    const unsigned long long elems = bh * (unsigned long long)d->L * 64ull;
+    if (bh > (1ull << 31) || elems > (1ull << 56)) return SA3_ERR_SHAPE;
+    const size_t in_bytes = (size_t)elems * 2 * (d->differential ? 2 : 1);
+    const size_t v_bytes = (size_t)elems * 2;
+    const size_t out_bytes = (size_t)elems * (d->out_dtype == SA3_F32 ? 4 : 2);
+    const size_t tab_bytes = (size_t)d->L * 32 * sizeof(float);
+    if (overlaps(d->out, out_bytes, d->q, in_bytes) || overlaps(d->out, out_bytes, d->k, in_bytes) ||
+        overlaps(d->out, out_bytes, d->v, v_bytes) || overlaps(d->out, out_bytes, d->cos, tab_bytes) ||
+        overlaps(d->out, out_bytes, d->sin, tab_bytes))
+        return SA3_ERR_ARG;
+
+    sa3::LaunchArgs a;
+    a.q = d->q;
+    a.k = d->k;
+    a.v = d->v;
+    a.cos = d->cos;
+    a.sin = d->sin;
+    a.out = d->out;
+    a.B = d->B;
+    a.H = d->H;
+    a.L = d->L;
+    // a window reaching every key is full attention: |i - j| <= L - 1 always holds
+    a.window = (d->window < 0 || d->window >= d->L - 1) ? -1 : d->window;
+    a.lam = d->lambda;
+    a.scale_log2 = (float)(std::fabs((double)d->scale) * 1.4426950408889634074);
+    a.neg_scale = d->scale < 0.0f ? 1 : 0;
+    a.dtype = d->dtype;
+    a.out_dtype = d->out_dtype;
+    a.diff = d->differential;
+    a.stream = d->stream;
+    if (!std::isfinite(a.scale_log2)) return SA3_ERR_ARG;
+
+    const unsigned long long tiles = ((unsigned long long)d->L + sa3::tile_rows(a) - 1) / sa3::tile_rows(a);
+    if (tiles * bh >= (1ull << 31)) return SA3_ERR_SHAPE;
+
+    const int dev = check_device();
+    if (dev != SA3_OK) return dev;
+
+    const int e = sa3::launch_forward(a);
+    return e == (int)hipSuccess ? SA3_OK : SA3_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sa3attn_forward_ex(const sa3attn_desc *desc) { return forward_impl(desc); }
+
+static int forward_short(const void *q, const void *k, const void *v, const float *cos, const float *sin,
+                         void *out, int B, int H, int L, int D, int window, float lambda, float scale,
+                         void *stream, int dtype) {
+    sa3attn_desc d;
+    d.q = q;
+    d.k = k;
+    d.v = v;
+    d.cos = cos;
+    d.sin = sin;
+    d.out = out;
+    d.B = B;
+    d.H = H;
+    d.L = L;
+    d.D = D;
+    d.window = window;
+    d.lambda = lambda;
+    d.scale = scale;
+    d.dtype = dtype;
+    d.out_dtype = dtype;
+    d.differential = lambda != 0.0f ? 1 : 0;
+    d.stream = stream;
+    return forward_impl(&d);
+}
+
+int sa3attn_forward(const void *q, const void *k, const void *v, const float *cos, const float *sin, void *out,
+                    int B, int H, int L, int D, int window, float lambda, float scale, void *stream) {
+    return forward_short(q, k, v, cos, sin, out, B, H, L, D, window, lambda, scale, stream, SA3_F16);
+}
+
+int sa3attn_forward_bf16(const void *q, const void *k, const void *v, const float *cos, const float *sin,
+                         void *out, int B, int H, int L, int D, int window, float lambda, float scale,
+                         void *stream) {
+    return forward_short(q, k, v, cos, sin, out, B, H, L, D, window, lambda, scale, stream, SA3_BF16);
+}
+
+const char *sa3attn_status_string(int status) {
+    switch (status) {
+        case SA3_OK: return "SA3_OK";
+        case SA3_ERR_NULL: return "SA3_ERR_NULL: a required pointer is NULL";
+        case SA3_ERR_SHAPE: return "SA3_ERR_SHAPE: B, H, L or D out of range, D odd, or a size overflows";
+        case SA3_ERR_UNSUPPORTED: return "SA3_ERR_UNSUPPORTED: head dim or dtype not supported";
+        case SA3_ERR_ARG: return "SA3_ERR_ARG: non-finite scale or lambda, or out overlaps an input";
+        case SA3_ERR_DEVICE: return "SA3_ERR_DEVICE: no HIP device, or the current device is not gfx950";
+        case SA3_ERR_LAUNCH: return "SA3_ERR_LAUNCH: kernel launch failed";
+        default: return "unknown sa3attn status";
+    }
+}
+
+int sa3attn_version(void) { return (SA3ATTN_VERSION_MAJOR << 16) | SA3ATTN_VERSION_MINOR; }
+
+}  // extern "C"

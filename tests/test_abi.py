@@ -1,0 +1,166 @@
+"""C-ABI checks that need no GPU: exports, status strings, validation, host table.
+
+Validation runs before the library touches the device, so every error path below is
+exercised with placeholder (never dereferenced) pointers. A call that passes
+validation on a machine without a GPU must report SA3_ERR_DEVICE, not crash.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import rope_attention_core_amd as sa3
+from oracle import rope as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sa3attn.h")
+
+SA3_OK, SA3_ERR_NULL, SA3_ERR_SHAPE, SA3_ERR_UNSUPPORTED, SA3_ERR_ARG, SA3_ERR_DEVICE = 0, -1, -2, -3, -4, -5
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sa3attn_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return sa3.load_library()
+
+
+def test_library_exports_every_declared_function(lib):
+    names = _declared_functions()
+    assert len(names) >= 6
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in sa3attn.h but not exported"
+    assert set(names) == set(sa3.EXPORTS)
+
+
+def test_status_strings_and_version(lib):
+    assert sa3.status_string(0) == "SA3_OK"
+    for code in range(-6, 0):
+        s = sa3.status_string(code)
+        assert s.startswith("SA3_ERR_"), s
+    assert "unknown" in sa3.status_string(12345)
+    assert sa3.version() == (0, 1)
+
+
+@pytest.mark.parametrize("L,D", [(1, 2), (37, 8), (8192, 16), (8192, 64), (8192, 128)])
+def test_rope_table_matches_oracle_table(L, D):
+    """The library's host table and the oracle's own table agree bit for bit.
+
+    Both define theta_i as the fp64 value nearest base^(-2i/D) and round
+    cos/sin(fp64(m) * theta_i) once to fp32; the two are computed independently.
+    """
+    c, s = sa3.rope_table(L, D)
+    c0, s0 = P.rope_table_f32(L, D)
+    np.testing.assert_array_equal(c.numpy(), c0)
+    np.testing.assert_array_equal(s.numpy(), s0)
+
+
+def test_rope_table_argument_errors(lib):
+    buf = (ctypes.c_float * 64)()
+    assert lib.sa3attn_rope_table(None, buf, 4, 8, 1e4) == SA3_ERR_NULL
+    assert lib.sa3attn_rope_table(buf, buf, 0, 8, 1e4) == SA3_ERR_SHAPE
+    assert lib.sa3attn_rope_table(buf, buf, 4, 7, 1e4) == SA3_ERR_SHAPE
+    assert lib.sa3attn_rope_table(buf, buf, 4, 8, -1.0) == SA3_ERR_ARG
+    assert lib.sa3attn_rope_table(buf, buf, 4, 8, float("nan")) == SA3_ERR_ARG
+
+
+# Placeholder addresses, far apart so that no range overlaps unless a test wants it.
+def _fake(i):
+    return ctypes.c_void_p((i + 1) << 40)
+
+
+def _desc(**kw):
+    d = dict(q=_fake(1), k=_fake(2), v=_fake(3), cos=_fake(4), sin=_fake(5), out=_fake(6),
+             B=1, H=2, L=64, D=64, window=-1, lambda_=0.0, scale=0.125, dtype=0, out_dtype=0,
+             differential=0, stream=None)
+    d.update(kw)
+    return sa3._Desc(**d)
+
+
+def _call(lib, **kw):
+    return lib.sa3attn_forward_ex(ctypes.byref(_desc(**kw)))
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "cos", "sin", "out"])
+def test_null_pointers_rejected(lib, field):
+    assert _call(lib, **{field: ctypes.c_void_p(0)}) == SA3_ERR_NULL
+
+
+def test_null_descriptor_rejected(lib):
+    assert lib.sa3attn_forward_ex(None) == SA3_ERR_NULL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), SA3_ERR_SHAPE), (dict(H=-1), SA3_ERR_SHAPE), (dict(L=0), SA3_ERR_SHAPE),
+    (dict(D=0), SA3_ERR_SHAPE), (dict(D=63), SA3_ERR_SHAPE), (dict(L=(1 << 24) + 1), SA3_ERR_SHAPE),
+    (dict(B=1 << 20, H=1 << 12), SA3_ERR_SHAPE),
+    (dict(D=128), SA3_ERR_UNSUPPORTED), (dict(D=32), SA3_ERR_UNSUPPORTED),
+    (dict(dtype=2), SA3_ERR_UNSUPPORTED), (dict(dtype=7), SA3_ERR_UNSUPPORTED),
+    (dict(out_dtype=3), SA3_ERR_UNSUPPORTED),
+    (dict(scale=float("nan")), SA3_ERR_ARG), (dict(scale=float("inf")), SA3_ERR_ARG),
+    (dict(lambda_=float("nan")), SA3_ERR_ARG), (dict(differential=2), SA3_ERR_ARG),
+    (dict(scale=3e38), SA3_ERR_ARG),
+])
+def test_bad_arguments_rejected(lib, kw, code):
+    assert _call(lib, **kw) == code
+
+
+def test_argument_swap_is_caught(lib):
+    """Distinct prime sizes: a caller that swaps B/H/L/D lands on D != 64."""
+    assert _call(lib, B=3, H=5, L=64, D=7) == SA3_ERR_SHAPE
+    assert _call(lib, B=64, H=5, L=7, D=3) == SA3_ERR_SHAPE
+    assert _call(lib, B=3, H=64, L=5, D=7) == SA3_ERR_SHAPE
+
+
+@pytest.mark.parametrize("alias", ["q", "k", "v", "cos", "sin"])
+def test_out_overlapping_an_input_rejected(lib, alias):
+    base = _fake(9).value
+    kw = {alias: ctypes.c_void_p(base), "out": ctypes.c_void_p(base + 64)}
+    assert _call(lib, **kw) == SA3_ERR_ARG
+
+
+def test_out_overlapping_second_branch_rejected(lib):
+    # differential q spans two branches: out placed inside branch 2 must be caught
+    base = _fake(9).value
+    branch = 1 * 2 * 64 * 64 * 2
+    assert _call(lib, differential=1, q=ctypes.c_void_p(base),
+                 out=ctypes.c_void_p(base + branch + 128)) == SA3_ERR_ARG
+
+
+def _gpu_present():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+# Calls below pass validation; with a GPU present they would launch on placeholder
+# pointers, so they only run where there is none.
+@pytest.mark.skipif(_gpu_present(), reason="placeholder pointers must never reach a real GPU")
+def test_valid_call_without_gpu_reports_device_error(lib):
+    assert _call(lib) == SA3_ERR_DEVICE
+    assert _call(lib, B=3, H=5, L=7, D=64) == SA3_ERR_DEVICE
+    # plain q spans one branch only: out just past it is no overlap
+    base = _fake(9).value
+    assert _call(lib, differential=0, q=ctypes.c_void_p(base),
+                 out=ctypes.c_void_p(base + 2 * 64 * 64 * 2 + 128)) == SA3_ERR_DEVICE
+    f = lib.sa3attn_forward
+    assert f(_fake(1), _fake(2), _fake(3), _fake(4), _fake(5), _fake(6), 1, 2, 64, 64, -1, 0.0, 0.125,
+             None) == SA3_ERR_DEVICE
+    assert lib.sa3attn_forward_bf16(_fake(1), _fake(2), _fake(3), _fake(4), _fake(5), _fake(6), 1, 2, 64, 64,
+                                    -1, 0.0, 0.125, None) == SA3_ERR_DEVICE
+
+
+def test_short_forms_validate_like_ex(lib):
+    f = lib.sa3attn_forward
+    assert f(None, _fake(2), _fake(3), _fake(4), _fake(5), _fake(6), 1, 2, 64, 64, -1, 0.0, 0.125, None) == SA3_ERR_NULL
+    assert f(_fake(1), _fake(2), _fake(3), _fake(4), _fake(5), _fake(6), 1, 2, 64, 32, -1, 0.0, 0.125, None) == SA3_ERR_UNSUPPORTED
+    assert f(_fake(1), _fake(2), _fake(3), _fake(4), _fake(5), _fake(6), 1, 2, 64, 64, -1, float("inf"), 0.125, None) == SA3_ERR_ARG

@@ -1,0 +1,132 @@
+"""GPU parity: the HIP path (through the C-ABI) against the fp64 method-mode oracle.
+
+Bar: max-abs error <= 2e-3 and per-row cosine >= 0.99995 on the same seeded inputs,
+for FP16/BF16 inputs. Small configurations are compared element by element on every
+output; the full-size DiT-long and SAME-L-style configurations run on the GPU at full
+size, in the launch configuration the benchmark times, and are compared on sampled
+rows that the oracle computes one by one.
+"""
+
+import numpy as np
+import pytest
+
+from rope_attention_core_amd import synth
+
+import gpu_common as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["tiny", "dit_short", "dit_2min", "dit_2min_prime"])
+def test_config_full_parity(name):
+    cfg = synth.config(name)
+    inp = synth.make_inputs(cfg)
+    got = G.run_gpu(cfg, inp)
+    want = G.run_oracle(cfg, inp)
+    G.assert_parity(got, want, what=name)
+
+
+def test_dit_long_full_size_sampled():
+    """B=2, H=24, L=4096 bf16, 1% of K rows x8, fp32 out: every row of 3 heads sampled."""
+    cfg = synth.config("dit_long")
+    inp = synth.make_inputs(cfg)
+    got = G.run_gpu(cfg, inp)
+    assert np.all(np.isfinite(got))
+    rng = np.random.default_rng(100)
+    for b, h in ((0, 0), (1, 23), (0, 13)):
+        rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(4088, 4096), rng.integers(0, 4096, 240)]))
+        want = G.run_oracle_rows(cfg, inp, b, h, rows)
+        G.assert_parity(got[b, h, rows], want, what=f"dit_long b{b} h{h}")
+
+
+def test_dit_long_one_head_full():
+    cfg = synth.config("dit_long", B=1, H=2)
+    inp = synth.make_inputs(cfg)
+    G.assert_parity(G.run_gpu(cfg, inp), G.run_oracle(cfg, inp), what="dit_long H2")
+
+
+def test_samel_swa_full_size_sampled():
+    """B=1, H=16, L=8192 bf16 differential, w=256 (513 keys), lambda=0.8, fp32 out."""
+    cfg = synth.config("samel_swa")
+    inp = synth.make_inputs(cfg)
+    got = G.run_gpu(cfg, inp)
+    assert np.all(np.isfinite(got))
+    rng = np.random.default_rng(101)
+    for h in (0, 7, 15):
+        rows = np.unique(np.concatenate([np.arange(0, 300), np.arange(7890, 8192), rng.integers(0, 8192, 400)]))
+        want = G.run_oracle_rows(cfg, inp, 0, h, rows)
+        G.assert_parity(got[0, h, rows], want, what=f"samel_swa h{h}")
+
+
+def test_samel_swa_reduced_full():
+    cfg = synth.config("samel_swa", H=2, L=3000)
+    inp = synth.make_inputs(cfg)
+    G.assert_parity(G.run_gpu(cfg, inp), G.run_oracle(cfg, inp), what="samel_swa H2 L3000")
+
+
+TAILS = [1, 2, 3, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 511, 513, 1291, 1292]
+
+
+@pytest.mark.parametrize("L", TAILS)
+def test_tail_lengths_f16(L):
+    cfg = synth.config("dit_2min", H=3, L=L, seed=1000 + L)
+    inp = synth.make_inputs(cfg)
+    G.assert_parity(G.run_gpu(cfg, inp), G.run_oracle(cfg, inp), what=f"tail L{L}")
+
+
+@pytest.mark.parametrize("L", [1, 17, 64, 65, 200, 257, 1291])
+def test_tail_lengths_bf16_windowed_diff(L):
+    cfg = synth.config("samel_swa", H=2, L=L, window=17, seed=2000 + L)
+    inp = synth.make_inputs(cfg)
+    G.assert_parity(G.run_gpu(cfg, inp), G.run_oracle(cfg, inp), what=f"swa tail L{L}")
+
+
+@pytest.mark.parametrize("w", [0, 1, 15, 16, 17, 63, 64, 65, 255, 256, 257, 698, 699, 700, 5000, -1])
+@pytest.mark.parametrize("io", ["f16", "bf16"])
+def test_window_sweep(w, io):
+    cfg = synth.config("dit_2min", H=2, L=700, window=w, io=io, seed=3000 + max(w, 0),
+                       out="f32" if io == "bf16" else "io")
+    inp = synth.make_inputs(cfg)
+    G.assert_parity(G.run_gpu(cfg, inp), G.run_oracle(cfg, inp), what=f"window {w} {io}")
+
+
+@pytest.mark.parametrize("lam", [0.0, 0.8, -0.5])
+@pytest.mark.parametrize("w", [-1, 17, 256])
+@pytest.mark.parametrize("io", ["f16", "bf16"])
+def test_differential(lam, w, io):
+    cfg = synth.config("samel_swa", H=2, L=1000, window=w, lam=lam, io=io, seed=4000,
+                       out="f32")
+    inp = synth.make_inputs(cfg)
+    G.assert_parity(G.run_gpu(cfg, inp), G.run_oracle(cfg, inp), what=f"diff lam{lam} w{w} {io}")
+
+
+@pytest.mark.parametrize("io,out", [("f16", "f16"), ("f16", "bf16"), ("f16", "f32"),
+                                    ("bf16", "f16"), ("bf16", "bf16"), ("bf16", "f32")])
+def test_out_dtypes(io, out):
+    cfg = synth.config("dit_2min", H=2, L=333, io=io, out=out, std=0.5, seed=5000)
+    inp = synth.make_inputs(cfg)
+    got, want = G.run_gpu(cfg, inp), G.run_oracle(cfg, inp)
+    if out == "bf16":
+        # a bf16 output carries 8 significant bits: allow its rounding on top of the bar
+        err = np.abs(got - want)
+        assert np.all(err <= G.ATOL + np.abs(want) * 2.0 ** -8), err.max()
+        assert G.row_cosines(got, want).min() >= 0.9999
+    else:
+        G.assert_parity(got, want, what=f"{io}->{out}")
+
+
+@pytest.mark.parametrize("scale", [-0.125, 0.0, 0.37])
+def test_scale_values(scale):
+    cfg = synth.config("dit_2min", H=2, L=300, seed=6000)
+    inp = synth.make_inputs(cfg)
+    q, k, v = G.widen(inp, cfg)
+    import oracle
+    c32, s32 = oracle.rope_table_f32(cfg.L, 64)
+    want = oracle.attn_method(q, k, v, c32, s32, "f16", scale)
+    torch = G.torch_mod()
+    c, s = G.device_table(cfg.L)
+    import rope_attention_core_amd as sa3
+    out = sa3.forward(G.to_device(inp["q"], "f16"), G.to_device(inp["k"], "f16"), G.to_device(inp["v"], "f16"),
+                      c, s, scale=scale)
+    torch.cuda.synchronize()
+    G.assert_parity(out.float().cpu().numpy().astype(np.float64), want, what=f"scale {scale}")
