@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused RoPE attention core on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-configs]
+
+One step = one call of the whole fused core (RoPE on Q/K, QK^T, FP32 online softmax,
+P.V) over one batch of synthetic input already resident in HBM. The headline workload
+is the DiT long latent: B=2 (a CFG cond + uncond pair), H=24, L=4096, D=64, bf16 with
+1% of K rows scaled by 8, full attention, FP32 output. Rank 0 prints ONE JSON line with
+the metric (TFLOP/s of algorithmic work, 4*D FLOPs per query-key pair), the roofline of
+the kernel against the MI355X dense bf16 MFMA peak, the CPU oracle timed on the host
+cores as a baseline, and ms/call + TFLOP/s of every other synthetic configuration.
+
+Timing: W untimed warmups, then K calls bracketed by synchronisation, timed with HIP
+events recorded on the stream the library launches on (torch's current stream, which
+the binding passes to the C-ABI). Each call also gets its own event pair so the median
+of the per-call durations is reported next to the mean.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6    # MI355X dense FP16/BF16 MFMA
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+HEAD_CONFIG = "dit_long"
+OTHER_CONFIGS = ["tiny", "dit_short", "dit_2min", "dit_2min_prime", "samel_swa"]
+KERNEL_SOURCE = os.path.join(ROOT, "rope_attention_core_amd", "csrc", "attn_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_dit_long.json")
+
+
+def pairs(cfg):
+    """In-window (query, key) pairs per branch."""
+    L, w = cfg.L, cfg.window
+    per_head = L * L if (w < 0 or w >= L - 1) else L * (2 * w + 1) - w * (w + 1)
+    return cfg.B * cfg.H * per_head
+
+
+def flops(cfg):
+    return 4 * cfg.D * pairs(cfg) * (2 if cfg.diff else 1)
+
+
+def compulsory_bytes(cfg):
+    n = cfg.B * cfg.H * cfg.L * cfg.D
+    qk = 2 * n * 2 * (2 if cfg.diff else 1)
+    v = 2 * n
+    out = n * (4 if cfg.out_dtype == "f32" else 2)
+    table = 2 * cfg.L * (cfg.D // 2) * 4
+    return qk + v + out + table
+
+
+def kernel_source_sha():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic():
+    """HBM bytes per launch from rocprofv3 counters, if taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Bench:
+    def __init__(self, torch, sa3, synth, cfg):
+        import numpy as np
+        self.torch, self.sa3, self.cfg = torch, sa3, cfg
+        inp = synth.make_inputs(cfg)
+
+        def dev(a):
+            if cfg.io == "f16":
+                return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+        self.q, self.k, self.v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+        c, s = sa3.rope_table(cfg.L, cfg.D, cfg.base)
+        self.cos, self.sin = c.cuda(), s.cuda()
+        dt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[cfg.out_dtype]
+        self.out = torch.empty((cfg.B, cfg.H, cfg.L, cfg.D), dtype=dt, device="cuda")
+        self.inputs_host = inp
+
+    def call(self):
+        c = self.cfg
+        self.sa3.forward(self.q, self.k, self.v, self.cos, self.sin, window=c.window, lam=c.lam,
+                         scale=c.scale, out=self.out, differential=c.diff)
+
+    def run(self, steps, warmup):
+        torch = self.torch
+        stream = torch.cuda.current_stream()
+        for _ in range(warmup):
+            self.call()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        t0.record(stream)
+        for a, b in ev:
+            a.record(stream)
+            self.call()
+            b.record(stream)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        per = sorted(a.elapsed_time(b) for a, b in ev)
+        total = t0.elapsed_time(t1)
+        return {"ms_total": total, "ms_mean": total / steps, "ms_median": per[len(per) // 2],
+                "ms_min": per[0], "ms_max": per[-1], "wall_s": wall}
+
+
+def cpu_baseline(cfg, inputs, budget_s=12.0):
+    """Time the fp64 oracle (method mode) on whole heads of the same workload."""
+    import numpy as np
+
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    q = oracle.widen_io(inputs["q"], cfg.io)
+    k = oracle.widen_io(inputs["k"], cfg.io)
+    v = oracle.widen_io(inputs["v"], cfg.io)
+    c32, s32 = oracle.rope_table_f32(cfg.L, cfg.D, cfg.base)
+    heads = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
+    done, t_used = 0, 0.0
+    for b, h in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        t = time.perf_counter()
+        if cfg.diff:
+            oracle.attn_method(q[0][sl], k[0][sl], v[sl], c32, s32, cfg.io, cfg.scale, window=cfg.window,
+                               lam=cfg.lam, q2=q[1][sl], k2=k[1][sl])
+        else:
+            oracle.attn_method(q[sl], k[sl], v[sl], c32, s32, cfg.io, cfg.scale, window=cfg.window)
+        t_used += time.perf_counter() - t
+        done += 1
+        if t_used >= budget_s:
+            break
+    per_head_flops = flops(cfg) / (cfg.B * cfg.H)
+    threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    return {
+        "value": round(per_head_flops * done / t_used / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} of {len(heads)} (b,h) heads of {cfg.name}, full output, numpy fp64 method mode; "
+                  f"{t_used:.1f} s; ms/call extrapolated {t_used / done * len(heads) * 1e3:.0f}",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-config lines")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="after the benchmark, run 3 plain device copies of this many MiB "
+                         "(a known-size reference for the HBM byte counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the fused core shards by "
+                                   "(batch, head) with no exchange, so a multi-GPU figure adds "
+                                   "nothing here; run with --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+
+    import rope_attention_core_amd as sa3
+    from rope_attention_core_amd import synth
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    sa3.load_library()
+    torch.cuda.set_device(0)
+
+    cfg = synth.config(HEAD_CONFIG)
+    bench = Bench(torch, sa3, synth, cfg)
+    t = bench.run(args.steps, args.warmup)
+    fl = flops(cfg)
+    ms = t["ms_mean"]
+    tflops = fl / (ms * 1e-3) / 1e12
+    traffic = load_traffic()
+
+    per_config = {}
+    if not args.no_configs:
+        for name in OTHER_CONFIGS:
+            c = synth.config(name)
+            b = Bench(torch, sa3, synth, c)
+            r = b.run(max(10, args.steps), 3)
+            f = flops(c)
+            per_config[name] = {
+                "shape": f"B{c.B} H{c.H} L{c.L} D{c.D} {c.io}" + (f" w={c.window}" if c.window >= 0 else "")
+                         + (f" diff lam={c.lam}" if c.diff else "") + f" out={c.out_dtype}",
+                "ms_per_call": round(r["ms_mean"], 5),
+                "ms_median": round(r["ms_median"], 5),
+                "tflops": round(f / (r["ms_mean"] * 1e-3) / 1e12, 2),
+                "frac_mfma_peak": round(f / (r["ms_mean"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "gbs_compulsory": round(compulsory_bytes(c) / (r["ms_mean"] * 1e-3) / 1e9, 1),
+            }
+            del b
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, bench.inputs_host)
+
+    line = {
+        "metric": "attention-core TFLOP/s at L=4096 (DiT long latent, fused RoPE attention)",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.io,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: B={cfg.B} H={cfg.H} L={cfg.L} D={cfg.D} bf16 q/k/v ~ N(0,1), "
+                        f"1% of K rows x8, RoPE base 10000 (fp32 table), full attention, scale 1/8, fp32 out",
+            "B": cfg.B, "H": cfg.H, "L": cfg.L, "D": cfg.D, "window": cfg.window, "out_dtype": cfg.out_dtype,
+            "gflop_per_call": round(fl / 1e9, 3),
+            "parallelism": "single GPU",
+        },
+        "ms_median": round(t["ms_median"], 5),
+        "ms_min": round(t["ms_min"], 5),
+        "ms_max": round(t["ms_max"], 5),
+        "frac_of_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu,
+        "per_config": per_config,
+    }
+    print(json.dumps(line), flush=True)
+
+    if args.copy_mb > 0:
+        n = args.copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_reference_bytes_read": n * 4, "copy_reference_bytes_written": n * 4,
+                          "copies": 3}), file=sys.stderr, flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -9,38 +9,45 @@
 // "How the kernels differ" and "Building your own": differential sliding-window
 // attention, window of +-WINDOW keys, FP32 subtraction).
 //
-// Work decomposition (one workgroup = 4 waves = one tile of BM query rows of one
-// (b, h) slab; one wave = QB blocks of 32 query rows):
+// Work decomposition: one workgroup = NW waves = one tile of BM query rows of one
+// (b, h) slab; one wave = QB blocks of 32 query rows; keys in tiles of 64.
 //
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_{f16,bf16}:
-//    A = K tile rows (keys) from LDS, B = the wave's rotated Q held in registers for
+//    A = K tile rows (keys) from LDS, B = the wave's rotated Q, held in registers for
 //    the whole kernel. In the 32x32 accumulator a lane owns ONE query (lane % 32) and
-//    16 keys, so the row max and row sum are per-lane reductions plus one exchange
-//    with lane ^ 32 (v_permlane32_swap).
+//    16 keys of each 32, so row statistics are per-lane plus one exchange with
+//    lane ^ 32 (v_permlane32_swap).
 //  * O^T = V^T P^T with v_mfma_f32_32x32x16_f16: B = P^T comes straight from the
 //    softmax registers (the key order inside an MFMA step is permuted to match the
-//    accumulator layout, and V^T is read with the same permutation), A = V^T is read
-//    from a transposed V tile in LDS.
-//  * K is rotated (FP32, fixed operation order, no contraction) and rounded to the
-//    IO dtype while it is staged into LDS; Q once into registers. V is staged
-//    transposed; for bf16 inputs it is converted to fp16 on the way, so P and V
-//    meet in fp16 (P rounded to fp16 keeps 11 significant bits).
-//  * LDS is double buffered: the global loads of tile t+1 are in flight while tile
-//    t is multiplied; one barrier per tile.
-//  * Softmax in base 2 (scale * log2 e folded into one FMA) with a lazy rescale: the
-//    running maximum used as the exponent base is only raised when a tile's maximum
-//    exceeds it by more than TAU, so P stays below 2^TAU and most tiles skip the
-//    O *= alpha pass. The result is the same softmax (any common base cancels).
-//  * Tiles wholly outside the window are never visited; tiles that meet the window
-//    edge or the end of the sequence are masked element-wise.
-//  * Workgroup ids are remapped so that the workgroups one XCD receives (the
-//    hardware deals them round robin over the 8 XCDs) are consecutive tiles of the
-//    same heads, keeping each head's K/V in one XCD's L2.
+//    accumulator layout and V^T is read with the same permutation); A = V^T from a
+//    transposed V tile in LDS. For bf16 inputs V is converted to fp16 as it is staged,
+//    so P (rounded to fp16, 11 significant bits) and V meet in fp16.
+//  * K is rotated (FP32, fixed operation order, no contraction) and rounded to the IO
+//    dtype while it is staged into LDS; Q once into registers.
+//  * Software pipeline over key tiles with four LDS buffers and one barrier per
+//    tile. In the body for tile t the softmax of tile t (VALU) is independent of the
+//    P.V product of tile t-1 and of the QK^T product of tile t+1 (MFMA) and of the
+//    staging of tile t+2 (VALU + LDS), so the scheduler can overlap them; the global
+//    loads of tile t+3 are in flight meanwhile.
+//  * Online softmax in base 2 (scale * log2 e folded into one FMA) with a lazy
+//    rescale: each row keeps an exponent base m; a tile moves it only when the tile's
+//    maximum exceeds m by more than TAU (and on the row's first valid keys, where m is
+//    set to the exact maximum). So P = 2^(s*c - m) <= 2^TAU fits fp16, and O and the
+//    running sum are rescaled (O *= 2^(m_old - m_new), a wave-uniform branch) only
+//    on those rare tiles. Any common base cancels in O / l, so the result is the same
+//    softmax.
+//  * Out-of-range rows read as zeros through buffer loads (the hardware returns 0
+//    past num_records), so tails need no branches; scores of keys >= L and outside
+//    the window are set to -inf in the tiles that need a mask.
+//  * Workgroup ids are remapped so that the workgroups one XCD receives (dealt round
+//    robin over the 8 XCDs) are consecutive tiles of the same heads, keeping each
+//    head's K/V in one XCD's L2.
 
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "sa3attn_internal.hpp"
 
@@ -55,28 +62,47 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr int IO_F16 = 0;
 constexpr int IO_BF16 = 1;
-constexpr int OUT_F16 = 0;
 constexpr int OUT_BF16 = 1;
 constexpr int OUT_F32 = 2;
 
-constexpr int HD = 64;           // head dim
-constexpr int NPAIR = HD / 2;    // cos/sin row length
-constexpr int BN = 64;           // keys per tile
-constexpr int NT = 256;          // threads per workgroup
-constexpr int KS_STRIDE = 72;    // LDS row stride of the K tile in 16-bit elements
-constexpr int VT_STRIDE = 68;    // LDS row stride of the V^T tile in 16-bit elements
-constexpr float TAU = 8.0f;      // lazy-rescale threshold in log2 units
+constexpr int HD = 64;            // head dim
+constexpr int ROWB = HD * 2;      // bytes per q/k/v row, and per cos/sin row (32 floats)
+constexpr int BN = 64;            // keys per tile
+constexpr int NBUF = 4;           // LDS stages
+constexpr int KS_STRIDE = 72;     // LDS row stride of the K tile in 16-bit elements
+constexpr int VT_STRIDE = 68;     // LDS row stride of the V^T tile in 16-bit elements
+constexpr uint32_t RSRC_WORD3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9)
+#ifndef SA3_PIPE_S
+#define SA3_PIPE_S 0   // QK^T of tile t+1 into a second score set while tile t's softmax runs
+#endif
+#ifndef SA3_SUM_MFMA
+#define SA3_SUM_MFMA 0 // row sums on the MFMA (all-ones row of V^T) instead of FP32 adds
+#endif
+#ifndef SA3_SUM_DOT2
+#define SA3_SUM_DOT2 0 // FP32 row sums of the rounded P with v_dot2_f32_f16 instead of adds
+#endif
+#ifndef SA3_SCHED
+#define SA3_SCHED 0    // instruction-group ordering hints for the tile block (0 = none)
+#endif
+#ifndef SA3_TAU
+#define SA3_TAU 8.0f
+#endif
+#ifndef SA3_NW_PLAIN
+#define SA3_NW_PLAIN 8
+#endif
+constexpr float TAU = SA3_TAU;                   // lazy rescale: the base moves only when a row's max passes it by more
 
 struct Params {
     const uint16_t *q, *k, *v;
     const float *cos, *sin;
     void *out;
-    long long branch_stride;     // elements from branch 1 to branch 2 of q / k
+    long long branch_stride;      // elements from branch 1 to branch 2 of q / k
     int L, window, n_qtiles, out_dtype, neg_scale;
-    float lam, c;                // c = |scale| * log2(e)
+    float lam, c;                 // c = |scale| * log2(e)
 };
 
 // ---- element conversions -------------------------------------------------------
@@ -93,7 +119,7 @@ __device__ __forceinline__ void unpack2(uint32_t u, float &a, float &b) {
     }
 }
 
-// Round two floats to nearest-even in the IO dtype and pack them (a in the low half).
+// Round two floats to nearest-even in the given 16-bit type and pack them (a low).
 template <int IO>
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
     if constexpr (IO == IO_BF16) {
@@ -108,17 +134,19 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 // RoPE on 8 consecutive elements (4 adjacent pairs) with their cos/sin, in FP32 with
 // every product and sum rounded on its own, then rounded to the IO dtype.
 template <int IO>
-__device__ __forceinline__ u32x4 rope8(u32x4 x, f32x4 c, f32x4 s) {
+__device__ __forceinline__ u32x4 rope8(u32x4 x, u32x4 cw, u32x4 sw) {
 #pragma clang fp contract(off)
     u32x4 r;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         float x0, x1;
         unpack2<IO>(x[j], x0, x1);
-        const float a = x0 * c[j];
-        const float b = x1 * s[j];
-        const float e = x0 * s[j];
-        const float f = x1 * c[j];
+        const float c = __uint_as_float(cw[j]);
+        const float s = __uint_as_float(sw[j]);
+        const float a = x0 * c;
+        const float b = x1 * s;
+        const float e = x0 * s;
+        const float f = x1 * c;
         r[j] = pack2<IO>(a - b, e + f);
     }
     return r;
@@ -149,83 +177,124 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ u32x4 ld16(const uint16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
-__device__ __forceinline__ f32x4 ld16f(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, (int)RSRC_WORD3);
+}
+// 16- and 8-byte loads; bytes at or past num_records read as zero.
+__device__ __forceinline__ u32x4 bload(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ u32x2 bload8(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+}
 
-// One branch's running softmax state for one 32-query block.
-struct RowState {
-    f32x16 o[2];     // O^T accumulators for d blocks 0..31 and 32..63
-    float m;         // exponent base in log2 units (-inf before any valid key)
-    float l;         // this lane's partial sum of P (its 16 keys of each 32)
+__device__ __forceinline__ u32x4 lds16(const uint16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
+
+// Validity of the keys of a masked tile for one lane: key offset o (0..63 inside the
+// tile, as laid out in the S^T accumulator) is valid iff lo <= o - 4g <= lo + span,
+// evaluated as one unsigned compare.
+struct TileMask {
+    int lo;           // first valid key offset relative to k0 + 4g
+    uint32_t span;    // number of further valid offsets
 };
 
-// Softmax of one 32-query block over one 64-key tile, S^T layout; rescales the
-// state when needed and returns P^T packed as fp16 MFMA B operands [kb][tt].
+// softmax of one 32-query block of one branch over one 64-key tile against the
+// exponent base -nb: P^T packed as fp16 MFMA B operands [kb][tt].
 template <bool MASK>
-__device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], RowState &st, u32x4 (&p)[2][2], float c,
-                                             int k0, int qi, int L, int window, int g) {
+__device__ __forceinline__ void softmax_p(const f32x16 (&s)[2], float c, float nb, TileMask mk,
+                                          u32x4 (&p)[2][2], float &rowsum) {
     const float NEG_INF = -__builtin_inff();
-    if constexpr (MASK) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int key = k0 + kb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-                const int dist = key - qi;
-                const bool ok = key < L && (window < 0 || (dist <= window && dist >= -window));
-                s[kb][i] = ok ? s[kb][i] : NEG_INF;
-            }
-    }
-    float mx = NEG_INF;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = pair_max(mx);
-    const float mt = (mx == NEG_INF) ? NEG_INF : mx * c;
-    const bool need = mt > st.m + TAU;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-        const float mn = need ? mt : st.m;
-        const float alpha = need ? __builtin_amdgcn_exp2f(st.m - mn) : 1.0f;
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) st.o[db][i] *= alpha;
-        st.l *= alpha;
-        st.m = mn;
-    }
-    const float nb = (st.m == NEG_INF) ? 0.0f : -st.m;
-    float sum = 0.0f;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
         float e[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            float v = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c, nb));
-            if constexpr (MASK) v = (s[kb][i] == NEG_INF) ? 0.0f : v;
-            e[i] = v;
-            sum += v;
+            float t = __builtin_fmaf(s[kb][i], c, nb);
+            if constexpr (MASK) {
+                const int o = kb * 32 + (i >> 2) * 8 + (i & 3);
+                t = ((uint32_t)(o - mk.lo) <= mk.span) ? t : NEG_INF;
+            }
+            e[i] = __builtin_amdgcn_exp2f(t);
         }
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             u32x4 w;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) w[j] = pack2<IO_F16>(e[8 * tt + 2 * j], e[8 * tt + 2 * j + 1]);
+            for (int j = 0; j < 4; ++j) {
+                const f16x2 h = {(_Float16)e[8 * tt + 2 * j], (_Float16)e[8 * tt + 2 * j + 1]};
+                w[j] = __builtin_bit_cast(uint32_t, h);
+                // row sum of the rounded P (what the MFMA multiplies), four chains
+                acc[2 * kb + tt] = __builtin_amdgcn_fdot2(h, f16x2{(_Float16)1.0f, (_Float16)1.0f},
+                                                          acc[2 * kb + tt], false);
+            }
             p[kb][tt] = w;
         }
     }
-    st.l += sum;
+    rowsum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
-template <int IO, bool DIFF, int QB>
-__global__ __launch_bounds__(NT) void attn_fwd_kernel(Params P) {
-    constexpr int BM = 4 * 32 * QB;
+// Maximum of 32 values as a tree of 3-input maxima (depth 4) rather than a chain.
+__device__ __forceinline__ float max32(const float (&v)[32]) {
+    float a[11];
+#pragma unroll
+    for (int i = 0; i < 10; ++i) a[i] = fmaxf(fmaxf(v[3 * i], v[3 * i + 1]), v[3 * i + 2]);
+    a[10] = fmaxf(v[30], v[31]);
+    const float b0 = fmaxf(fmaxf(a[0], a[1]), a[2]);
+    const float b1 = fmaxf(fmaxf(a[3], a[4]), a[5]);
+    const float b2 = fmaxf(fmaxf(a[6], a[7]), a[8]);
+    const float b3 = fmaxf(a[9], a[10]);
+    return fmaxf(fmaxf(b0, b1), fmaxf(b2, b3));
+}
+
+// exact maximum of c * s over the valid keys of this lane pair (log2 units)
+template <bool MASK>
+__device__ __forceinline__ float tile_max(const f32x16 (&s)[2], float c, TileMask mk) {
+    const float NEG_INF = -__builtin_inff();
+    float v[32];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float x = s[kb][i];
+            if constexpr (MASK) {
+                const int o = kb * 32 + (i >> 2) * 8 + (i & 3);
+                x = ((uint32_t)(o - mk.lo) <= mk.span) ? x : NEG_INF;
+            }
+            v[kb * 16 + i] = x;
+        }
+    const float mx = pair_max(max32(v));
+    return (mx == NEG_INF) ? NEG_INF : mx * c;
+}
+
+struct Branch {
+    f32x16 o[2];     // O^T accumulators for d in [0, 32) and [32, 64)
+#if SA3_SUM_MFMA
+    f32x16 l;        // row sums of P: element 0 of lanes 0..31 (an all-ones row of V^T)
+#else
+    float l;         // this lane's partial FP32 sum of P (its 16 keys of each 32)
+#endif
+    float m;         // exponent base in log2 units (-inf: no valid key yet)
+    float a;         // factor taking O and l from the previous base to m
+};
+
+// Two waves per SIMD for the plain instances (registers <= 256 per wave): with 8-wave
+// workgroups they come from one workgroup, with 4-wave workgroups from two.
+template <int IO, bool DIFF, int NW, int QB>
+__global__ __launch_bounds__(NW * 64, DIFF ? 1 : 2) void attn_fwd_kernel(Params P) {
+    constexpr int NT = NW * 64;
+    constexpr int NBR = DIFF ? 2 : 1;
+    constexpr int BM = NW * 32 * QB;
+    constexpr int KC = 512 / NT;             // K chunks of 8 elements per thread per branch
+    constexpr int VD = 4096 / (2 * NT);      // d values per thread in the V^T staging (2 keys each)
+    static_assert(KC >= 1 && (VD == 8 || VD == 4), "unsupported workgroup size");
+    using vraw_t = std::conditional_t<VD == 8, u32x4, u32x2>;
     constexpr int KS_ELEMS = BN * KS_STRIDE;
     constexpr int VT_ELEMS = HD * VT_STRIDE;
-    constexpr int NK = DIFF ? 2 : 1;
-    constexpr int BUF_ELEMS = NK * KS_ELEMS + VT_ELEMS;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BUF_ELEMS];
+    constexpr int BUF_ELEMS = NBR * KS_ELEMS + VT_ELEMS;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[NBUF * BUF_ELEMS];
 
+    const float NEG_INF = -__builtin_inff();
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -244,35 +313,32 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(Params P) {
     const int qt = lid - bh * P.n_qtiles;
 
     const size_t head = (size_t)bh * (size_t)L * HD;
-    const uint16_t *Qh = P.q + head;
-    const uint16_t *Kh = P.k + head;
-    const uint16_t *Vh = P.v + head;
-    const uint16_t *Q2h = P.q + P.branch_stride + head;
-    const uint16_t *K2h = P.k + P.branch_stride + head;
+    const uint32_t nrec = (uint32_t)L * ROWB;
+    rsrc_t rq[NBR], rk[NBR];
+#pragma unroll
+    for (int br = 0; br < NBR; ++br) {
+        rq[br] = make_rsrc(P.q + br * P.branch_stride + head, nrec);
+        rk[br] = make_rsrc(P.k + br * P.branch_stride + head, nrec);
+    }
+    const rsrc_t rv = make_rsrc(P.v + head, nrec);
+    const rsrc_t rc = make_rsrc(P.cos, nrec);
+    const rsrc_t rs = make_rsrc(P.sin, nrec);
 
     const int q0 = qt * BM;
     const int qw = q0 + wave * 32 * QB;
 
-    // ---- Q (and Q2): rotate once into registers, B-operand layout ----------------
-    u32x4 qreg[QB][4];
-    u32x4 q2reg[DIFF ? QB : 1][4];
+    // ---- Q: rotate once into registers (MFMA B-operand layout) -------------------
+    u32x4 qreg[NBR][QB][4];
     const uint32_t qsign = P.neg_scale ? 0x80008000u : 0u;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        const int qi = qw + qb * 32 + r;
+        const uint32_t row = (uint32_t)(qw + qb * 32 + r) * ROWB;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const int d0 = 16 * ks + 8 * g;
-            u32x4 x = {0, 0, 0, 0}, x2 = {0, 0, 0, 0};
-            f32x4 cc = {0.f, 0.f, 0.f, 0.f}, ss = {0.f, 0.f, 0.f, 0.f};
-            if (qi < L) {
-                x = ld16(Qh + (size_t)qi * HD + d0);
-                if constexpr (DIFF) x2 = ld16(Q2h + (size_t)qi * HD + d0);
-                cc = ld16f(P.cos + (size_t)qi * NPAIR + d0 / 2);
-                ss = ld16f(P.sin + (size_t)qi * NPAIR + d0 / 2);
-            }
-            qreg[qb][ks] = rope8<IO>(x, cc, ss) ^ qsign;
-            if constexpr (DIFF) q2reg[qb][ks] = rope8<IO>(x2, cc, ss) ^ qsign;
+            const uint32_t off = row + (uint32_t)(16 * ks + 8 * g) * 2;
+            const u32x4 cc = bload(rc, off), ss = bload(rs, off);
+#pragma unroll
+            for (int br = 0; br < NBR; ++br) qreg[br][qb][ks] = rope8<IO>(bload(rq[br], off), cc, ss) ^ qsign;
         }
     }
 
@@ -286,146 +352,222 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(Params P) {
     const int t_begin = k_lo / BN;
     const int t_end = (k_hi + BN - 1) / BN;
 
-    // ---- tile loaders ------------------------------------------------------------
+    // ---- staging: global -> registers -> (rotate / transpose) -> LDS -------------
     // K: 512 chunks of 8 elements; chunk ch -> key ch / 8, d0 = 8 * (ch % 8).
-    // V: 256 pair-chunks; thread -> keys 2p, 2p+1 (p = tid % 32), d0 = 8 * (tid / 32).
-    u32x4 kraw[2], k2raw[DIFF ? 2 : 1], vraw[2];
-    f32x4 craw[2], sraw[2];
+    // V: thread -> keys 2p, 2p+1 (p = tid % 32) and VD values of d from VD * (tid / 32).
     const int vp = tid & 31;
-    const int vd0 = (tid >> 5) * 8;
+    const int vd0 = (tid >> 5) * VD;
+    u32x4 rawk[NBR][KC], rawc[KC], raws[KC];
+    vraw_t rawv[2];
 
-    auto issue_loads = [&](int t) {
-        const int k0 = t * BN;
+    auto load_raw = [&](int t) __attribute__((always_inline)) {
+        const uint32_t k0 = (uint32_t)(t * BN);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < KC; ++i) {
             const int ch = tid + NT * i;
-            const int kj = k0 + (ch >> 3);
-            const int d0 = (ch & 7) * 8;
-            if (kj < L) {
-                kraw[i] = ld16(Kh + (size_t)kj * HD + d0);
-                if constexpr (DIFF) k2raw[i] = ld16(K2h + (size_t)kj * HD + d0);
-                craw[i] = ld16f(P.cos + (size_t)kj * NPAIR + d0 / 2);
-                sraw[i] = ld16f(P.sin + (size_t)kj * NPAIR + d0 / 2);
-            } else {
-                kraw[i] = u32x4{0, 0, 0, 0};
-                if constexpr (DIFF) k2raw[i] = u32x4{0, 0, 0, 0};
-                craw[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-                sraw[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
+            const uint32_t off = (k0 + (uint32_t)(ch >> 3)) * ROWB + (uint32_t)(ch & 7) * 16;
+#pragma unroll
+            for (int br = 0; br < NBR; ++br) rawk[br][i] = bload(rk[br], off);
+            rawc[i] = bload(rc, off);
+            raws[i] = bload(rs, off);
         }
-        const int ka = k0 + 2 * vp;
-        vraw[0] = (ka < L) ? ld16(Vh + (size_t)ka * HD + vd0) : u32x4{0, 0, 0, 0};
-        vraw[1] = (ka + 1 < L) ? ld16(Vh + (size_t)(ka + 1) * HD + vd0) : u32x4{0, 0, 0, 0};
+        const uint32_t offv = (k0 + 2u * vp) * ROWB + (uint32_t)vd0 * 2;
+        if constexpr (VD == 8) {
+            rawv[0] = bload(rv, offv);
+            rawv[1] = bload(rv, offv + ROWB);
+        } else {
+            rawv[0] = bload8(rv, offv);
+            rawv[1] = bload8(rv, offv + ROWB);
+        }
     };
 
-    auto stage = [&](int buf) {
+    auto stage = [&](int buf) __attribute__((always_inline)) {
         uint16_t *Ks = smem + buf * BUF_ELEMS;
-        uint16_t *Vt = Ks + NK * KS_ELEMS;
+        uint16_t *Vt = Ks + NBR * KS_ELEMS;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < KC; ++i) {
             const int ch = tid + NT * i;
-            const int key = ch >> 3;
-            const int d0 = (ch & 7) * 8;
-            *reinterpret_cast<u32x4 *>(Ks + key * KS_STRIDE + d0) = rope8<IO>(kraw[i], craw[i], sraw[i]);
-            if constexpr (DIFF)
-                *reinterpret_cast<u32x4 *>(Ks + KS_ELEMS + key * KS_STRIDE + d0) =
-                    rope8<IO>(k2raw[i], craw[i], sraw[i]);
+            const int at = (ch >> 3) * KS_STRIDE + (ch & 7) * 8;
+#pragma unroll
+            for (int br = 0; br < NBR; ++br)
+                *reinterpret_cast<u32x4 *>(Ks + br * KS_ELEMS + at) = rope8<IO>(rawk[br][i], rawc[i], raws[i]);
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t wa = vraw[0][j >> 1], wb = vraw[1][j >> 1];
-            const int sh = (j & 1) * 16;
+        for (int j = 0; j < VD; ++j) {
+            const uint32_t wa = rawv[0][j >> 1], wb = rawv[1][j >> 1];
             uint32_t w;
             if constexpr (IO == IO_BF16) {
-                const float fa = __uint_as_float(((wa >> sh) & 0xffffu) << 16);
-                const float fb = __uint_as_float(((wb >> sh) & 0xffffu) << 16);
+                const float fa = __uint_as_float((j & 1) ? (wa & 0xffff0000u) : (wa << 16));
+                const float fb = __uint_as_float((j & 1) ? (wb & 0xffff0000u) : (wb << 16));
                 w = pack2<IO_F16>(fa, fb);
             } else {
-                w = ((wa >> sh) & 0xffffu) | (((wb >> sh) & 0xffffu) << 16);
+                w = (j & 1) ? __builtin_amdgcn_perm(wb, wa, 0x07060302u) : __builtin_amdgcn_perm(wb, wa, 0x05040100u);
             }
             *reinterpret_cast<uint32_t *>(Vt + (vd0 + j) * VT_STRIDE + 2 * vp) = w;
         }
     };
 
-    // ---- running state -----------------------------------------------------------
-    RowState st[QB], st2[DIFF ? QB : 1];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        st[qb].o[0] = f32x16{};
-        st[qb].o[1] = f32x16{};
-        st[qb].m = -__builtin_inff();
-        st[qb].l = 0.0f;
-        if constexpr (DIFF) {
-            st2[qb].o[0] = f32x16{};
-            st2[qb].o[1] = f32x16{};
-            st2[qb].m = -__builtin_inff();
-            st2[qb].l = 0.0f;
-        }
-    }
-
-    const int qw_hi = qw + 32 * QB - 1;
-    const bool wave_live = qw < L;
-
-    issue_loads(t_begin);
-    for (int t = t_begin; t < t_end; ++t) {
-        const int buf = (t - t_begin) & 1;
-        stage(buf);
-        __syncthreads();
-        if (t + 1 < t_end) issue_loads(t + 1);
-
-        const int k0 = t * BN;
-        bool skip = !wave_live;
-        if (window >= 0) skip = skip || (k0 > qw_hi + window) || (k0 + BN - 1 < qw - window);
-        if (skip) continue;
-        const bool need_mask =
-            (k0 + BN > L) || (window >= 0 && (k0 < qw_hi - window || k0 + BN - 1 > qw + window));
-
+    // ---- MFMA stages -----------------------------------------------------------
+    auto qk = [&](int buf, f32x16 (&s)[NBR][QB][2]) __attribute__((always_inline)) {
         const uint16_t *Ks = smem + buf * BUF_ELEMS;
-        const uint16_t *Vt = Ks + NK * KS_ELEMS;
-
-        // S^T = K Q^T for every query block; each K operand is read once per wave.
-        f32x16 s[QB][2], s2[DIFF ? QB : 1][2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            u32x4 ka[4];
+        for (int br = 0; br < NBR; ++br)
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) ka[ks] = ld16(Ks + (kb * 32 + r) * KS_STRIDE + 16 * ks + 8 * g);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                f32x16 acc = {};
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) acc = mfma_qk<IO>(ka[ks], qreg[qb][ks], acc);
-                s[qb][kb] = acc;
-            }
-            if constexpr (DIFF) {
+            for (int kb = 0; kb < 2; ++kb) {
+                u32x4 ka[4];
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks)
-                    ka[ks] = ld16(Ks + KS_ELEMS + (kb * 32 + r) * KS_STRIDE + 16 * ks + 8 * g);
+                    ka[ks] = lds16(Ks + br * KS_ELEMS + (kb * 32 + r) * KS_STRIDE + 16 * ks + 8 * g);
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) {
                     f32x16 acc = {};
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) acc = mfma_qk<IO>(ka[ks], q2reg[qb][ks], acc);
-                    s2[qb][kb] = acc;
+                    for (int ks = 0; ks < 4; ++ks) acc = mfma_qk<IO>(ka[ks], qreg[br][qb][ks], acc);
+                    s[br][qb][kb] = acc;
                 }
             }
-        }
+    };
 
-        // online softmax -> P^T in fp16
-        u32x4 pp[QB][2][2], pp2[DIFF ? QB : 1][2][2];
+    Branch st[NBR][QB];
+#pragma unroll
+    for (int br = 0; br < NBR; ++br)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            const int qi = qw + qb * 32 + r;
-            if (need_mask) {
-                softmax_tile<true>(s[qb], st[qb], pp[qb], c, k0, qi, L, window, g);
-                if constexpr (DIFF) softmax_tile<true>(s2[qb], st2[qb], pp2[qb], c, k0, qi, L, window, g);
-            } else {
-                softmax_tile<false>(s[qb], st[qb], pp[qb], c, k0, qi, L, window, g);
-                if constexpr (DIFF) softmax_tile<false>(s2[qb], st2[qb], pp2[qb], c, k0, qi, L, window, g);
-            }
+            st[br][qb].o[0] = f32x16{};
+            st[br][qb].o[1] = f32x16{};
+#if SA3_SUM_MFMA
+            st[br][qb].l = f32x16{};
+#else
+            st[br][qb].l = 0.0f;
+#endif
+            st[br][qb].m = NEG_INF;
+            st[br][qb].a = 1.0f;
         }
 
-        // O^T += V^T P^T; each V^T operand is read once per wave.
+    // mask of tile t for each query block of this wave (lane-level lo/span)
+    auto tile_mask = [&](int t, int qb) __attribute__((always_inline)) {
+        const int k0 = t * BN;
+        const int qi = qw + qb * 32 + r;
+        int lo = 0, hi = L - 1;
+        if (window >= 0 && qi < L) {
+            lo = max(lo, qi - window);
+            hi = min(hi, qi + window);
+        }
+        TileMask mk;
+        lo -= k0 + 4 * g;
+        hi -= k0 + 4 * g;
+        if (hi < lo) {
+            mk.lo = 1 << 20;
+            mk.span = 0;
+        } else {
+            mk.lo = lo;
+            mk.span = (uint32_t)(hi - lo);
+        }
+        return mk;
+    };
+    // the wave-uniform decision whether tile t needs element masks
+    const int qhi_live = min(qw + 32 * QB - 1, L - 1);
+    auto tile_needs_mask = [&](int t) __attribute__((always_inline)) {
+        const int k0 = t * BN;
+        if (k0 + BN > L) return true;
+        if (window < 0 || qw > qhi_live) return false;
+        return k0 < qhi_live - window || k0 + BN - 1 > qw + window;
+    };
+
+    // ---- prologue ----------------------------------------------------------------
+    // The first block multiplies a zero P by the V tile of stage t_begin - 1: clear it.
+    {
+        uint32_t *vz = reinterpret_cast<uint32_t *>(smem + ((t_begin + NBUF - 1) % NBUF) * BUF_ELEMS +
+                                                    NBR * KS_ELEMS);
+        for (int i = tid; i < VT_ELEMS / 2; i += NT) vz[i] = 0u;
+    }
+    load_raw(t_begin);
+    stage(t_begin % NBUF);
+    load_raw(t_begin + 1);
+    stage((t_begin + 1) % NBUF);
+    load_raw(t_begin + 2);
+    __syncthreads();
+
+    // Score registers: with SA3_PIPE_S the block of tile t reads sbuf[P] and writes the
+    // scores of tile t+1 into sbuf[P^1]; otherwise one set is consumed, then rewritten.
+    // P ping-pongs: the block of tile t writes pbuf[P] (and its row sums rsum[P]) and
+    // multiplies pbuf[P^1], the P of tile t-1. P is the parity of t - t_begin, known at
+    // compile time in the unrolled loop.
+    constexpr int NS = SA3_PIPE_S ? 2 : 1;
+    f32x16 sbuf[NS][NBR][QB][2];
+    u32x4 pbuf[2][NBR][QB][2][2];
+    float rsum[2][NBR][QB];
+#pragma unroll
+    for (int br = 0; br < NBR; ++br)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            rsum[1][br][qb] = 0.0f;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) pbuf[1][br][qb][kb][tt] = u32x4{0, 0, 0, 0};
+        }
+    qk(t_begin % NBUF, sbuf[0]);
+    // A-operand rows of the row-sum block: row 0 (lanes 0 and 32) all ones in fp16.
+    const u32x4 ones = (r == 0) ? u32x4{0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u} : u32x4{0, 0, 0, 0};
+    (void)ones;
+
+    // Bring O and l to the base of tile t-1 (whose P is pbuf[PP]) before its P.V
+    // product: O *= alpha only when some row's base moved; l = l * alpha + its row sum.
+    auto carry = [&](auto pp_tag) __attribute__((always_inline)) {
+        constexpr int PP = decltype(pp_tag)::value;
+        bool moved = false;
+#pragma unroll
+        for (int br = 0; br < NBR; ++br)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) moved = moved || (st[br][qb].a != 1.0f);
+        if (__builtin_amdgcn_ballot_w64(moved)) {
+#pragma unroll
+            for (int br = 0; br < NBR; ++br)
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    Branch &b = st[br][qb];
+#pragma unroll
+                    for (int db = 0; db < 2; ++db)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) b.o[db][i] *= b.a;
+#if SA3_SUM_MFMA
+                    b.l[0] *= b.a;
+#endif
+                }
+        }
+#pragma unroll
+        for (int br = 0; br < NBR; ++br)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                Branch &b = st[br][qb];
+#if !SA3_SUM_MFMA
+                b.l = __builtin_fmaf(b.l, b.a, rsum[PP][br][qb]);
+#endif
+                b.a = 1.0f;
+            }
+    };
+
+    // O^T += V^T P^T (and l += 1^T P^T on the MFMA) for the given V^T operands and P
+    auto pv_sum = [&](const u32x4 (&va)[2][2][2], const u32x4 (&p)[NBR][QB][2][2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int br = 0; br < NBR; ++br)
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) {
+                        Branch &b = st[br][qb];
+                        b.o[0] = mfma_pv(va[0][kb][tt], p[br][qb][kb][tt], b.o[0]);
+                        b.o[1] = mfma_pv(va[1][kb][tt], p[br][qb][kb][tt], b.o[1]);
+#if SA3_SUM_MFMA
+                        b.l = mfma_pv(ones, p[br][qb][kb][tt], b.l);
+#endif
+                    }
+    };
+    auto load_v_operands = [&](int buf, u32x4 (&va)[2][2][2]) __attribute__((always_inline)) {
+        const uint16_t *Vt = smem + buf * BUF_ELEMS + NBR * KS_ELEMS;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -435,21 +577,147 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(Params P) {
                     const uint16_t *vrow = Vt + (db * 32 + r) * VT_STRIDE + kb * 32 + 16 * tt + 4 * g;
                     const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow);
                     const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + 8);
-                    const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) {
-                        st[qb].o[db] = mfma_pv(va, pp[qb][kb][tt], st[qb].o[db]);
-                        if constexpr (DIFF) st2[qb].o[db] = mfma_pv(va, pp2[qb][kb][tt], st2[qb].o[db]);
-                    }
+                    va[db][kb][tt] = u32x4{lo[0], lo[1], hi[0], hi[1]};
                 }
+    };
+
+    // One tile step: carry; softmax(t) alongside P.V(t-1) and QK^T(t+1); stage(t+2);
+    // the loads of tile t+3.
+    auto block = [&](int t, auto mask_tag, auto par_tag) __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        constexpr int PC = decltype(par_tag)::value;
+        constexpr int PN = PC ^ 1;
+        constexpr int SI = SA3_PIPE_S ? PC : 0;
+        constexpr int SO = SA3_PIPE_S ? PN : 0;
+        carry(std::integral_constant<int, PN>{});
+        TileMask mk[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) mk[qb] = MASK ? tile_mask(t, qb) : TileMask{0, 0};
+        // MFMA operands read from LDS first so their latency overlaps the softmax
+        u32x4 va[2][2][2];
+        load_v_operands((t + NBUF - 1) % NBUF, va);
+#if SA3_PIPE_S
+        u32x4 ka[NBR][2][4];
+        {
+            const uint16_t *Ks = smem + ((t + 1) % NBUF) * BUF_ELEMS;
+#pragma unroll
+            for (int br = 0; br < NBR; ++br)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks)
+                        ka[br][kb][ks] = lds16(Ks + br * KS_ELEMS + (kb * 32 + r) * KS_STRIDE + 16 * ks + 8 * g);
+        }
+#endif
+        // softmax of tile t: the tile maximum decides whether the base moves (lazily:
+        // only past TAU), then P = 2^(s*c - m) in fp16
+#pragma unroll
+        for (int br = 0; br < NBR; ++br)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                Branch &b = st[br][qb];
+                const float mt = tile_max<MASK>(sbuf[SI][br][qb], c, mk[qb]);
+                const float mn = (mt > b.m + TAU) ? mt : b.m;
+                b.a = (mn == b.m) ? 1.0f : ((b.m == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(b.m - mn));
+                b.m = mn;
+                softmax_p<MASK>(sbuf[SI][br][qb], c, (mn == NEG_INF) ? 0.0f : -mn, mk[qb], pbuf[PC][br][qb],
+                                rsum[PC][br][qb]);
+            }
+        pv_sum(va, pbuf[PN]);
+#if SA3_PIPE_S
+#pragma unroll
+        for (int br = 0; br < NBR; ++br)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    f32x16 acc = {};
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) acc = mfma_qk<IO>(ka[br][kb][ks], qreg[br][qb][ks], acc);
+                    sbuf[SO][br][qb][kb] = acc;
+                }
+#else
+        qk((t + 1) % NBUF, sbuf[SO]);
+#endif
+        stage((t + 2) % NBUF);
+        load_raw(t + 3);
+        // Group order for the scheduler: the MFMA operand reads first, then the MFMAs
+        // spread evenly through the softmax and staging VALU work.
+        constexpr int NMFMA = 16 * NBR * QB;
+        if constexpr (SA3_SCHED == 1) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 8 * NBR, 0);
+#pragma unroll
+            for (int i = 0; i < NMFMA; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+            }
+        } else if constexpr (SA3_SCHED == 2) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 16 + 8 * NBR, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+#pragma unroll
+            for (int i = 0; i < NMFMA; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+            }
+        } else if constexpr (SA3_SCHED == 3) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+#pragma unroll
+            for (int i = 0; i < 8 * NBR * QB; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 8 * NBR, 0);
+#pragma unroll
+            for (int i = 0; i < 8 * NBR * QB; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+            }
+        }
+        __syncthreads();
+    };
+
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    auto step = [&](int t, auto par_tag) __attribute__((always_inline)) {
+        if (tile_needs_mask(t))
+            block(t, std::true_type{}, par_tag);
+        else
+            block(t, std::false_type{}, par_tag);
+    };
+    int t = t_begin;
+    for (; t + 1 < t_end; t += 2) {
+        step(t, P0{});
+        step(t + 1, P1{});
+    }
+    if (t < t_end) step(t, P0{});
+    // the last tile's P sits in pbuf[parity of t_end - 1 - t_begin]
+    {
+        u32x4 va[2][2][2];
+        load_v_operands((t_end + NBUF - 1) % NBUF, va);
+        if ((t_end - t_begin) & 1) {
+            carry(P0{});
+            pv_sum(va, pbuf[0]);
+        } else {
+            carry(P1{});
+            pv_sum(va, pbuf[1]);
+        }
     }
 
-    // ---- epilogue: normalise, subtract, cast, store rows < L ---------------------
+    // ---- epilogue: normalise, subtract, cast, store rows < L -------------------------
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        const float inv = 1.0f / pair_sum(st[qb].l);
+#if SA3_SUM_MFMA
+        // row sums sit in element 0 of lanes 0..31; lanes 32..63 hold zeros there
+        const float inv = 1.0f / pair_sum(st[0][qb].l[0]);
         float inv2 = 0.0f;
-        if constexpr (DIFF) inv2 = 1.0f / pair_sum(st2[qb].l);
+        if constexpr (DIFF) inv2 = 1.0f / pair_sum(st[NBR - 1][qb].l[0]);
+#else
+        const float inv = 1.0f / pair_sum(st[0][qb].l);
+        float inv2 = 0.0f;
+        if constexpr (DIFF) inv2 = 1.0f / pair_sum(st[NBR - 1][qb].l);
+#endif
         const int qi = qw + qb * 32 + r;
         if (qi >= L) continue;
         const size_t row = head + (size_t)qi * HD;
@@ -460,8 +728,8 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(Params P) {
                 float o[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    o[j] = st[qb].o[db][grp * 4 + j] * inv;
-                    if constexpr (DIFF) o[j] = o[j] - P.lam * (st2[qb].o[db][grp * 4 + j] * inv2);
+                    o[j] = st[0][qb].o[db][grp * 4 + j] * inv;
+                    if constexpr (DIFF) o[j] = o[j] - P.lam * (st[NBR - 1][qb].o[db][grp * 4 + j] * inv2);
                 }
                 const int d = db * 32 + grp * 8 + g * 4;
                 if (P.out_dtype == OUT_F32) {
@@ -477,7 +745,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(Params P) {
     }
 }
 
-template <int IO, bool DIFF, int QB>
+template <int IO, bool DIFF, int NW, int QB>
 hipError_t launch(const LaunchArgs &a, int n_qtiles) {
     Params P;
     P.q = static_cast<const uint16_t *>(a.q);
@@ -495,17 +763,18 @@ hipError_t launch(const LaunchArgs &a, int n_qtiles) {
     P.lam = a.lam;
     P.c = a.scale_log2;
     const unsigned grid = (unsigned)n_qtiles * (unsigned)a.B * (unsigned)a.H;
-    hipLaunchKernelGGL((attn_fwd_kernel<IO, DIFF, QB>), dim3(grid), dim3(NT), 0,
+    hipLaunchKernelGGL((attn_fwd_kernel<IO, DIFF, NW, QB>), dim3(grid), dim3(NW * 64), 0,
                        static_cast<hipStream_t>(a.stream), P);
     return hipGetLastError();
 }
 
-// Query blocks of 32 rows per wave for an instance.
-int pick_qb(const LaunchArgs &a) { return a.diff ? 1 : 2; }
+// Instances: plain = 8 waves x 32 query rows (two waves per SIMD); differential =
+// 4 waves x 32 rows (one wave per SIMD: two branches of state per wave).
+constexpr int NW_PLAIN = SA3_NW_PLAIN, NW_DIFF = 4;
 
 }  // namespace
 
-int tile_rows(const LaunchArgs &a) { return 4 * 32 * pick_qb(a); }
+int tile_rows(const LaunchArgs &a) { return 32 * (a.diff ? NW_DIFF : NW_PLAIN); }
 
 int launch_forward(const LaunchArgs &a) {
     const int bm = tile_rows(a);
@@ -513,9 +782,9 @@ int launch_forward(const LaunchArgs &a) {
     const bool bf = a.dtype == 1;
     hipError_t e;
     if (a.diff) {
-        e = bf ? launch<IO_BF16, true, 1>(a, n_qtiles) : launch<IO_F16, true, 1>(a, n_qtiles);
+        e = bf ? launch<IO_BF16, true, NW_DIFF, 1>(a, n_qtiles) : launch<IO_F16, true, NW_DIFF, 1>(a, n_qtiles);
     } else {
-        e = bf ? launch<IO_BF16, false, 2>(a, n_qtiles) : launch<IO_F16, false, 2>(a, n_qtiles);
+        e = bf ? launch<IO_BF16, false, NW_PLAIN, 1>(a, n_qtiles) : launch<IO_F16, false, NW_PLAIN, 1>(a, n_qtiles);
     }
     return (int)e;
 }
