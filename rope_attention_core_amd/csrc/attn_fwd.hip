@@ -19,8 +19,10 @@
 //    lane ^ 32 (v_permlane32_swap).
 //  * O^T = V^T P^T with v_mfma_f32_32x32x16_f16: B = P^T comes straight from the
 //    softmax registers (the key order inside an MFMA step is permuted to match the
-//    accumulator layout and V^T is read with the same permutation); A = V^T from a
-//    transposed V tile in LDS. For bf16 inputs V is converted to fp16 as it is staged,
+//    accumulator layout); A = V^T from a transposed V tile in LDS whose key positions
+//    carry the same permutation, so each lane's operand is one 16-byte LDS read (the
+//    8-byte reads run at half the LDS bandwidth). For bf16 inputs V is converted to
+//    fp16 as it is staged,
 //    so P (rounded to fp16, 11 significant bits) and V meet in fp16.
 //  * K is rotated (FP32, fixed operation order, no contraction) and rounded to the IO
 //    dtype while it is staged into LDS; Q once into registers.
@@ -74,7 +76,7 @@ constexpr int ROWB = HD * 2;      // bytes per q/k/v row, and per cos/sin row (3
 constexpr int BN = 64;            // keys per tile
 constexpr int NBUF = 4;           // LDS stages
 constexpr int KS_STRIDE = 72;     // LDS row stride of the K tile in 16-bit elements
-constexpr int VT_STRIDE = 68;     // LDS row stride of the V^T tile in 16-bit elements
+constexpr int VT_STRIDE = 72;     // LDS row stride of the V^T tile in 16-bit elements
 constexpr uint32_t RSRC_WORD3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9)
 #ifndef SA3_PIPE_S
 #define SA3_PIPE_S 0   // QK^T of tile t+1 into a second score set while tile t's softmax runs
@@ -381,6 +383,9 @@ __global__ __launch_bounds__(NW * 64, DIFF ? 1 : 2) void attn_fwd_kernel(Params 
         }
     };
 
+    // V^T key positions: bits 2 and 3 of the key index swapped, so that the 8 keys one
+    // lane multiplies in a P.V step (see load_v_operands) are contiguous.
+    const int vpos = (2 * vp & ~12) | ((2 * vp & 4) << 1) | ((2 * vp & 8) >> 1);
     auto stage = [&](int buf) __attribute__((always_inline)) {
         uint16_t *Ks = smem + buf * BUF_ELEMS;
         uint16_t *Vt = Ks + NBR * KS_ELEMS;
@@ -403,7 +408,7 @@ __global__ __launch_bounds__(NW * 64, DIFF ? 1 : 2) void attn_fwd_kernel(Params 
             } else {
                 w = (j & 1) ? __builtin_amdgcn_perm(wb, wa, 0x07060302u) : __builtin_amdgcn_perm(wb, wa, 0x05040100u);
             }
-            *reinterpret_cast<uint32_t *>(Vt + (vd0 + j) * VT_STRIDE + 2 * vp) = w;
+            *reinterpret_cast<uint32_t *>(Vt + (vd0 + j) * VT_STRIDE + vpos) = w;
         }
     };
 
@@ -573,12 +578,8 @@ __global__ __launch_bounds__(NW * 64, DIFF ? 1 : 2) void attn_fwd_kernel(Params 
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int tt = 0; tt < 2; ++tt) {
-                    const uint16_t *vrow = Vt + (db * 32 + r) * VT_STRIDE + kb * 32 + 16 * tt + 4 * g;
-                    const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow);
-                    const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + 8);
-                    va[db][kb][tt] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-                }
+                for (int tt = 0; tt < 2; ++tt)
+                    va[db][kb][tt] = lds16(Vt + (db * 32 + r) * VT_STRIDE + kb * 32 + 16 * tt + 8 * g);
     };
 
     // One tile step: carry; softmax(t) alongside P.V(t-1) and QK^T(t+1); stage(t+2);
