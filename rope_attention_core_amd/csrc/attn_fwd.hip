@@ -34,9 +34,9 @@
 //  * Online softmax in base 2 (scale * log2 e folded into one FMA) with a lazy
 //    rescale: each row keeps an exponent base m; a tile moves it only when the tile's
 //    maximum exceeds m by more than TAU (and on the row's first valid keys, where m is
-//    set to the exact maximum). So P = 2^(s*c - m) <= 2^TAU fits fp16, and O and the
-//    running sum are rescaled (O *= 2^(m_old - m_new), a wave-uniform branch) only
-//    on those rare tiles. Any common base cancels in O / l, so the result is the same
+//    set to the exact maximum). So P = 2^(s*c - m) <= 2^TAU fits fp16; O and the
+//    running sum carry the factor 2^(m_old - m_new), which is exactly 1 except on
+//    those rare tiles. Any common base cancels in O / l, so the result is the same
 //    softmax.
 //  * Out-of-range rows read as zeros through buffer loads (the hardware returns 0
 //    past num_records), so tails need no branches; scores of keys >= L and outside
@@ -85,10 +85,16 @@ constexpr uint32_t RSRC_WORD3 = 0x00020000u;  // raw buffer, 32-bit data format 
 #define SA3_SUM_MFMA 0 // row sums on the MFMA (all-ones row of V^T) instead of FP32 adds
 #endif
 #ifndef SA3_SUM_DOT2
-#define SA3_SUM_DOT2 0 // FP32 row sums of the rounded P with v_dot2_f32_f16 instead of adds
+#define SA3_SUM_DOT2 1 // FP32 row sums of the rounded P with v_dot2_f32_f16 instead of adds
 #endif
 #ifndef SA3_SCHED
 #define SA3_SCHED 0    // instruction-group ordering hints for the tile block (0 = none)
+#endif
+#ifndef SA3_ALWAYS_RESCALE
+#define SA3_ALWAYS_RESCALE 1  // multiply O by the base factor on every tile (no branch)
+#endif
+#ifndef SA3_MAX3_ASM
+#define SA3_MAX3_ASM 0        // tile maximum as 16 v_max3_f32 without NaN canonicalisation
 #endif
 #ifndef SA3_TAU
 #define SA3_TAU 8.0f
@@ -226,9 +232,13 @@ __device__ __forceinline__ void softmax_p(const f32x16 (&s)[2], float c, float n
             for (int j = 0; j < 4; ++j) {
                 const f16x2 h = {(_Float16)e[8 * tt + 2 * j], (_Float16)e[8 * tt + 2 * j + 1]};
                 w[j] = __builtin_bit_cast(uint32_t, h);
+#if SA3_SUM_DOT2
                 // row sum of the rounded P (what the MFMA multiplies), four chains
                 acc[2 * kb + tt] = __builtin_amdgcn_fdot2(h, f16x2{(_Float16)1.0f, (_Float16)1.0f},
                                                           acc[2 * kb + tt], false);
+#else
+                acc[2 * kb + tt] += e[8 * tt + 2 * j] + e[8 * tt + 2 * j + 1];
+#endif
             }
             p[kb][tt] = w;
         }
@@ -265,7 +275,18 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[2], float c, TileMas
             }
             v[kb * 16 + i] = x;
         }
+#if SA3_MAX3_ASM
+    // MFMA results and -inf are canonical floats, so the quieting that fmaxf implies is not
+    // needed: 32 -> 1 with 3-input maxima (v[0] seeds the first, the rest in threes).
+    float a = v[0];
+#pragma unroll
+    for (int i = 1; i + 1 < 32; i += 2)
+        asm("v_max3_f32 %0, %1, %2, %3" : "=v"(a) : "v"(a), "v"(v[i]), "v"(v[i + 1]));
+    a = fmaxf(a, v[31]);
+    const float mx = pair_max(a);
+#else
     const float mx = pair_max(max32(v));
+#endif
     return (mx == NEG_INF) ? NEG_INF : mx * c;
 }
 
@@ -518,7 +539,10 @@ __global__ __launch_bounds__(NW * 64, DIFF ? 1 : 2) void attn_fwd_kernel(Params 
     (void)ones;
 
     // Bring O and l to the base of tile t-1 (whose P is pbuf[PP]) before its P.V
-    // product: O *= alpha only when some row's base moved; l = l * alpha + its row sum.
+    // product: O *= alpha, l = l * alpha + its row sum. alpha is exactly 1 unless the
+    // row's base moved, so the product is exact; it is done on every tile because a
+    // wave-uniform branch around it made the register allocator copy all 32 accumulator
+    // registers on every tile (and spill in the two-branch kernel).
     auto carry = [&](auto pp_tag) __attribute__((always_inline)) {
         constexpr int PP = decltype(pp_tag)::value;
         bool moved = false;
@@ -526,7 +550,7 @@ __global__ __launch_bounds__(NW * 64, DIFF ? 1 : 2) void attn_fwd_kernel(Params 
         for (int br = 0; br < NBR; ++br)
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) moved = moved || (st[br][qb].a != 1.0f);
-        if (__builtin_amdgcn_ballot_w64(moved)) {
+        if (SA3_ALWAYS_RESCALE || __builtin_amdgcn_ballot_w64(moved)) {
 #pragma unroll
             for (int br = 0; br < NBR; ++br)
 #pragma unroll
