@@ -97,25 +97,30 @@ class Bench:
                          scale=c.scale, out=self.out, differential=c.diff)
 
     def run(self, steps, warmup):
+        """Time `steps` back-to-back calls between two HIP events on the launch stream,
+        bracketed by device synchronisation (the headline ms/call), then the same number
+        of calls again, each between its own pair of events, for the spread."""
         torch = self.torch
         stream = torch.cuda.current_stream()
         for _ in range(warmup):
             self.call()
         torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
         wall0 = time.perf_counter()
         t0.record(stream)
+        for _ in range(steps):
+            self.call()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        total = t0.elapsed_time(t1)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         for a, b in ev:
             a.record(stream)
             self.call()
             b.record(stream)
-        t1.record(stream)
         torch.cuda.synchronize()
-        wall = time.perf_counter() - wall0
         per = sorted(a.elapsed_time(b) for a, b in ev)
-        total = t0.elapsed_time(t1)
         return {"ms_total": total, "ms_mean": total / steps, "ms_median": per[len(per) // 2],
                 "ms_min": per[0], "ms_max": per[-1], "wall_s": wall}
 
