@@ -11,10 +11,15 @@ the metric (TFLOP/s of algorithmic work, 4*D FLOPs per query-key pair), the roof
 the kernel against the MI355X dense bf16 MFMA peak, the CPU oracle timed on the host
 cores as a baseline, and ms/call + TFLOP/s of every other synthetic configuration.
 
-Timing: W untimed warmups, then K calls bracketed by synchronisation, timed with HIP
-events recorded on the stream the library launches on (torch's current stream, which
-the binding passes to the C-ABI). Each call also gets its own event pair so the median
-of the per-call durations is reported next to the mean.
+Timing: W untimed warmups (and at least 0.3 s of calls, so the clocks settle), then K
+back-to-back calls bracketed by synchronisation and timed with one pair of HIP events
+recorded on the stream the library launches on (torch's current stream, which the
+binding passes to the C-ABI): ms_per_step is their mean. A second pass gives each call
+its own event pair; its median, min and max are reported as the spread.
+
+Short latents: per-call time inside one captured graph of 96 and of 40 calls (the
+number of fused attention calls in a medium / small DiT forward) at L = 1, 16, 64, 256,
+next to the same figure for a trivial one-element kernel (the launch floor).
 """
 
 import argparse
@@ -30,8 +35,11 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6    # MI355X dense FP16/BF16 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+WARM_S = 0.3                 # minimum warmup time per timed configuration
 HEAD_CONFIG = "dit_long"
-OTHER_CONFIGS = ["tiny", "dit_short", "dit_2min", "dit_2min_prime", "samel_swa"]
+OTHER_CONFIGS = ["tiny", "dit_short", "dit_2min", "dit_2min_prime", "samel_swa", "samel_w17", "dit_medium_diff"]
+GRAPH_LENGTHS = [1, 16, 64, 256]   # short-latent sequences captured as one graph of N calls
+GRAPH_CALLS = [96, 40]             # fused attention calls per forward: medium and small DiT
 KERNEL_SOURCE = os.path.join(ROOT, "rope_attention_core_amd", "csrc", "attn_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_dit_long.json")
 
@@ -102,9 +110,14 @@ class Bench:
         of calls again, each between its own pair of events, for the spread."""
         torch = self.torch
         stream = torch.cuda.current_stream()
-        for _ in range(warmup):
-            self.call()
-        torch.cuda.synchronize()
+        # W warmup calls, and calls for at least WARM_S seconds, so the clocks have
+        # settled under this load before the timed region starts
+        n, t_end = 0, time.perf_counter() + WARM_S
+        while n < warmup or time.perf_counter() < t_end:
+            for _ in range(max(1, warmup)):
+                self.call()
+            torch.cuda.synchronize()
+            n += max(1, warmup)
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         wall0 = time.perf_counter()
         t0.record(stream)
@@ -123,6 +136,51 @@ class Bench:
         per = sorted(a.elapsed_time(b) for a, b in ev)
         return {"ms_total": total, "ms_mean": total / steps, "ms_median": per[len(per) // 2],
                 "ms_min": per[0], "ms_max": per[-1], "wall_s": wall}
+
+
+def graph_per_call_us(torch, fn, n_calls, replays=20):
+    """Capture n_calls of fn() into one graph; time replays back to back; us per call."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n_calls):
+            fn()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(replays):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) * 1e3 / (replays * n_calls)
+
+
+def short_graphs(torch, sa3, synth):
+    """Short-latent regime: per-call time of the fused core in a loop of 100 eager calls
+    and inside one captured graph of 96 / 40 calls, next to the per-launch floor of a
+    trivial kernel (a one-element add) captured the same way."""
+    x = torch.zeros(1, device="cuda")
+    res = {"launch_floor_graph_us": round(graph_per_call_us(torch, lambda: x.add_(1.0), 96), 3)}
+    for L in GRAPH_LENGTHS:
+        cfg = synth.config("dit_short", L=L)
+        b = Bench(torch, sa3, synth, cfg)
+        r = b.run(100, 5)
+        ent = {"shape": f"B{cfg.B} H{cfg.H} L{L} D{cfg.D} {cfg.io}",
+               "eager_loop_us_per_call": round(r["ms_mean"] * 1e3, 3)}
+        for n in GRAPH_CALLS:
+            ent[f"graph{n}_us_per_call"] = round(graph_per_call_us(torch, b.call, n), 3)
+        ent["gbs_compulsory_graph96"] = round(compulsory_bytes(cfg) / (ent["graph96_us_per_call"] * 1e-6) / 1e9, 1)
+        res[f"L{L}"] = ent
+        del b
+    return res
 
 
 def cpu_baseline(cfg, inputs, budget_s=12.0):
@@ -165,8 +223,8 @@ def cpu_baseline(cfg, inputs, budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-config lines")
     ap.add_argument("--copy-mb", type=int, default=0,
@@ -218,6 +276,7 @@ def main():
             }
             del b
         torch.cuda.empty_cache()
+    graphs = None if args.no_configs else short_graphs(torch, sa3, synth)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -257,6 +316,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "per_config": per_config,
+        "short_graphs": graphs,
     }
     print(json.dumps(line), flush=True)
 

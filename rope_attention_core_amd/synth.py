@@ -10,7 +10,11 @@ of that data exists here, so seeded normal draws with the pages' shapes stand in
   README, section "Benchmarks"), batch 1 per pass with CFG as a cond + uncond pair
   (sa3_trt README, section "DiT precision").
 * SAME-L shape: differential attention under a sliding window (TensorRT engines
-  README, sections "The SAME-L attention kernel" and "How the kernels differ").
+  README, sections "The SAME-L attention kernel" and "How the kernels differ"), with
+  a window of 513 keys and with the kernel's own +-17 keys ("Building your own").
+* Medium-DiT shape: the differential core at the long latent (the FP16-fix
+  discussion, section "Compatibility": the medium DiT is the differential one). The
+  pages give no head count; 24 heads as in the long-latent DiT shape.
 
 Recipe: ``numpy.random.default_rng(seed)`` draws fp64 standard normals in the order
 q, k, v (q1, k1, q2, k2, v when differential), each scaled by ``std``; the spike
@@ -71,6 +75,12 @@ CONFIGS = {
     # SAME-L-style differential sliding-window attention, window 513 keys (w = 256)
     "samel_swa": Config("samel_swa", 1, 16, 8192, 64, "bf16", seed=6, window=256,
                         lam=0.8, diff=True, out="f32"),
+    # the same with the SAME-L kernel's own window of +-17 keys (35 keys)
+    "samel_w17": Config("samel_w17", 1, 16, 8192, 64, "bf16", seed=8, window=17,
+                        lam=0.8, diff=True, out="f32"),
+    # medium-DiT-style differential full attention at the long latent, CFG pair
+    "dit_medium_diff": Config("dit_medium_diff", 2, 24, 4096, 64, "bf16", seed=7, lam=0.8,
+                              diff=True, out="f32"),
 }
 
 

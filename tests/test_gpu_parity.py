@@ -64,6 +64,44 @@ def test_samel_swa_reduced_full():
     G.assert_parity(G.run_gpu(cfg, inp), G.run_oracle(cfg, inp), what="samel_swa H2 L3000")
 
 
+def test_samel_w17_full_size_sampled():
+    """B=1, H=16, L=8192 bf16 differential, w=17 (35 keys), lambda=0.8, fp32 out."""
+    cfg = synth.config("samel_w17")
+    inp = synth.make_inputs(cfg)
+    got = G.run_gpu(cfg, inp)
+    assert np.all(np.isfinite(got))
+    rng = np.random.default_rng(102)
+    for h in (0, 9, 15):
+        rows = np.unique(np.concatenate([np.arange(0, 100), np.arange(8092, 8192), rng.integers(0, 8192, 400)]))
+        want = G.run_oracle_rows(cfg, inp, 0, h, rows)
+        G.assert_parity(got[0, h, rows], want, what=f"samel_w17 h{h}")
+
+
+def test_samel_w17_reduced_full():
+    cfg = synth.config("samel_w17", H=2, L=2500)
+    inp = synth.make_inputs(cfg)
+    G.assert_parity(G.run_gpu(cfg, inp), G.run_oracle(cfg, inp), what="samel_w17 H2 L2500")
+
+
+def test_dit_medium_diff_full_size_sampled():
+    """B=2, H=24, L=4096 bf16 differential full attention, lambda=0.8, fp32 out."""
+    cfg = synth.config("dit_medium_diff")
+    inp = synth.make_inputs(cfg)
+    got = G.run_gpu(cfg, inp)
+    assert np.all(np.isfinite(got))
+    rng = np.random.default_rng(103)
+    for b, h in ((0, 0), (1, 23), (1, 5)):
+        rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(4088, 4096), rng.integers(0, 4096, 120)]))
+        want = G.run_oracle_rows(cfg, inp, b, h, rows)
+        G.assert_parity(got[b, h, rows], want, what=f"dit_medium_diff b{b} h{h}")
+
+
+def test_dit_medium_diff_one_head_full():
+    cfg = synth.config("dit_medium_diff", B=1, H=1, L=2048)
+    inp = synth.make_inputs(cfg)
+    G.assert_parity(G.run_gpu(cfg, inp), G.run_oracle(cfg, inp), what="dit_medium_diff H1 L2048")
+
+
 TAILS = [1, 2, 3, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 511, 513, 1291, 1292]
 
 
