@@ -9,8 +9,10 @@
 // "How the kernels differ" and "Building your own": differential sliding-window
 // attention, window of +-WINDOW keys, FP32 subtraction).
 //
-// Work decomposition: one workgroup = NW waves = one tile of BM query rows of one
-// (b, h) slab; one wave = QB blocks of 32 query rows; keys in tiles of 64.
+// Work decomposition: one workgroup = 8 waves = one tile of query rows of one (b, h)
+// slab (256 rows; 128 in the differential variant, where a pair of waves shares 32
+// rows, one wave per softmax branch); one wave = 32 query rows of one branch; keys in
+// tiles of 64.
 //
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_{f16,bf16}:
 //    A = K tile rows (keys) from LDS, B = the wave's rotated Q, held in registers for
@@ -78,31 +80,7 @@ constexpr int NBUF = 4;           // LDS stages
 constexpr int KS_STRIDE = 72;     // LDS row stride of the K tile in 16-bit elements
 constexpr int VT_STRIDE = 72;     // LDS row stride of the V^T tile in 16-bit elements
 constexpr uint32_t RSRC_WORD3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9)
-#ifndef SA3_PIPE_S
-#define SA3_PIPE_S 0   // QK^T of tile t+1 into a second score set while tile t's softmax runs
-#endif
-#ifndef SA3_SUM_MFMA
-#define SA3_SUM_MFMA 0 // row sums on the MFMA (all-ones row of V^T) instead of FP32 adds
-#endif
-#ifndef SA3_SUM_DOT2
-#define SA3_SUM_DOT2 1 // FP32 row sums of the rounded P with v_dot2_f32_f16 instead of adds
-#endif
-#ifndef SA3_SCHED
-#define SA3_SCHED 0    // instruction-group ordering hints for the tile block (0 = none)
-#endif
-#ifndef SA3_ALWAYS_RESCALE
-#define SA3_ALWAYS_RESCALE 1  // multiply O by the base factor on every tile (no branch)
-#endif
-#ifndef SA3_MAX3_ASM
-#define SA3_MAX3_ASM 0        // tile maximum as 16 v_max3_f32 without NaN canonicalisation
-#endif
-#ifndef SA3_TAU
-#define SA3_TAU 8.0f
-#endif
-#ifndef SA3_NW_PLAIN
-#define SA3_NW_PLAIN 8
-#endif
-constexpr float TAU = SA3_TAU;                   // lazy rescale: the base moves only when a row's max passes it by more
+constexpr float TAU = 8.0f;       // lazy rescale: a row's base moves only when its max passes it by more
 
 struct Params {
     const uint16_t *q, *k, *v;
@@ -232,13 +210,9 @@ __device__ __forceinline__ void softmax_p(const f32x16 (&s)[2], float c, float n
             for (int j = 0; j < 4; ++j) {
                 const f16x2 h = {(_Float16)e[8 * tt + 2 * j], (_Float16)e[8 * tt + 2 * j + 1]};
                 w[j] = __builtin_bit_cast(uint32_t, h);
-#if SA3_SUM_DOT2
                 // row sum of the rounded P (what the MFMA multiplies), four chains
                 acc[2 * kb + tt] = __builtin_amdgcn_fdot2(h, f16x2{(_Float16)1.0f, (_Float16)1.0f},
                                                           acc[2 * kb + tt], false);
-#else
-                acc[2 * kb + tt] += e[8 * tt + 2 * j] + e[8 * tt + 2 * j + 1];
-#endif
             }
             p[kb][tt] = w;
         }
@@ -275,52 +249,44 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[2], float c, TileMas
             }
             v[kb * 16 + i] = x;
         }
-#if SA3_MAX3_ASM
-    // MFMA results and -inf are canonical floats, so the quieting that fmaxf implies is not
-    // needed: 32 -> 1 with 3-input maxima (v[0] seeds the first, the rest in threes).
-    float a = v[0];
-#pragma unroll
-    for (int i = 1; i + 1 < 32; i += 2)
-        asm("v_max3_f32 %0, %1, %2, %3" : "=v"(a) : "v"(a), "v"(v[i]), "v"(v[i + 1]));
-    a = fmaxf(a, v[31]);
-    const float mx = pair_max(a);
-#else
     const float mx = pair_max(max32(v));
-#endif
     return (mx == NEG_INF) ? NEG_INF : mx * c;
 }
 
+
 struct Branch {
     f32x16 o[2];     // O^T accumulators for d in [0, 32) and [32, 64)
-#if SA3_SUM_MFMA
-    f32x16 l;        // row sums of P: element 0 of lanes 0..31 (an all-ones row of V^T)
-#else
     float l;         // this lane's partial FP32 sum of P (its 16 keys of each 32)
-#endif
     float m;         // exponent base in log2 units (-inf: no valid key yet)
     float a;         // factor taking O and l from the previous base to m
 };
 
-// Two waves per SIMD for the plain instances (registers <= 256 per wave): with 8-wave
-// workgroups they come from one workgroup, with 4-wave workgroups from two.
-template <int IO, bool DIFF, int NW, int QB>
-__global__ __launch_bounds__(NW * 64, DIFF ? 1 : 2) void attn_fwd_kernel(Params P) {
+// One workgroup = 8 waves (two per SIMD, registers <= 256 per wave). Plain: each wave
+// owns 32 query rows, BM = 256. Differential: waves w and w + 4 own the same 32 rows,
+// wave w the first softmax branch (Q1, K1) and wave w + 4 the second (Q2, K2); both
+// multiply the same staged V tile, BM = 128, and the second branch hands O2 / l2 to the
+// first through LDS at the end.
+template <int IO, bool DIFF>
+__global__ __launch_bounds__(512, 2) void attn_fwd_kernel(Params P) {
+    constexpr int NW = 8;
     constexpr int NT = NW * 64;
-    constexpr int NBR = DIFF ? 2 : 1;
-    constexpr int BM = NW * 32 * QB;
-    constexpr int KC = 512 / NT;             // K chunks of 8 elements per thread per branch
+    constexpr int NBS = DIFF ? 2 : 1;        // K tiles staged per key tile (one per branch)
+    constexpr int WPB = NW / NBS;            // waves (32-row query blocks) per branch
+    constexpr int BM = WPB * 32;
     constexpr int VD = 4096 / (2 * NT);      // d values per thread in the V^T staging (2 keys each)
-    static_assert(KC >= 1 && (VD == 8 || VD == 4), "unsupported workgroup size");
-    using vraw_t = std::conditional_t<VD == 8, u32x4, u32x2>;
+    static_assert(VD == 4, "staging layout assumes 512 threads");
     constexpr int KS_ELEMS = BN * KS_STRIDE;
     constexpr int VT_ELEMS = HD * VT_STRIDE;
-    constexpr int BUF_ELEMS = NBR * KS_ELEMS + VT_ELEMS;
+    constexpr int BUF_ELEMS = NBS * KS_ELEMS + VT_ELEMS;
+    static_assert(!DIFF || NBUF * BUF_ELEMS * 2 >= WPB * 32 * 64 * 4, "LDS too small for the O2 exchange");
     __shared__ __attribute__((aligned(16))) uint16_t smem[NBUF * BUF_ELEMS];
 
     const float NEG_INF = -__builtin_inff();
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const int wbr = DIFF ? wave / WPB : 0;   // this wave's softmax branch
+    const int wq = DIFF ? wave % WPB : wave; // this wave's query block
     const int r = lane & 31;
     const int g = lane >> 5;
     const int L = P.L;
@@ -337,31 +303,26 @@ __global__ __launch_bounds__(NW * 64, DIFF ? 1 : 2) void attn_fwd_kernel(Params 
 
     const size_t head = (size_t)bh * (size_t)L * HD;
     const uint32_t nrec = (uint32_t)L * ROWB;
-    rsrc_t rq[NBR], rk[NBR];
+    rsrc_t rk[NBS];
 #pragma unroll
-    for (int br = 0; br < NBR; ++br) {
-        rq[br] = make_rsrc(P.q + br * P.branch_stride + head, nrec);
-        rk[br] = make_rsrc(P.k + br * P.branch_stride + head, nrec);
-    }
+    for (int br = 0; br < NBS; ++br) rk[br] = make_rsrc(P.k + br * P.branch_stride + head, nrec);
+    const rsrc_t rq = make_rsrc(P.q + wbr * P.branch_stride + head, nrec);
     const rsrc_t rv = make_rsrc(P.v + head, nrec);
     const rsrc_t rc = make_rsrc(P.cos, nrec);
     const rsrc_t rs = make_rsrc(P.sin, nrec);
 
     const int q0 = qt * BM;
-    const int qw = q0 + wave * 32 * QB;
+    const int qw = q0 + wq * 32;
 
     // ---- Q: rotate once into registers (MFMA B-operand layout) -------------------
-    u32x4 qreg[NBR][QB][4];
+    u32x4 qreg[4];
     const uint32_t qsign = P.neg_scale ? 0x80008000u : 0u;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const uint32_t row = (uint32_t)(qw + qb * 32 + r) * ROWB;
+    {
+        const uint32_t row = (uint32_t)(qw + r) * ROWB;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const uint32_t off = row + (uint32_t)(16 * ks + 8 * g) * 2;
-            const u32x4 cc = bload(rc, off), ss = bload(rs, off);
-#pragma unroll
-            for (int br = 0; br < NBR; ++br) qreg[br][qb][ks] = rope8<IO>(bload(rq[br], off), cc, ss) ^ qsign;
+            qreg[ks] = rope8<IO>(bload(rq, off), bload(rc, off), bload(rs, off)) ^ qsign;
         }
     }
 
@@ -376,48 +337,35 @@ __global__ __launch_bounds__(NW * 64, DIFF ? 1 : 2) void attn_fwd_kernel(Params 
     const int t_end = (k_hi + BN - 1) / BN;
 
     // ---- staging: global -> registers -> (rotate / transpose) -> LDS -------------
-    // K: 512 chunks of 8 elements; chunk ch -> key ch / 8, d0 = 8 * (ch % 8).
-    // V: thread -> keys 2p, 2p+1 (p = tid % 32) and VD values of d from VD * (tid / 32).
+    // K (each branch): 512 chunks of 8 elements; thread tid -> key tid / 8, d0 = 8 * (tid % 8).
+    // V: thread -> keys 2p, 2p+1 (p = tid % 32) and 4 values of d from 4 * (tid / 32).
     const int vp = tid & 31;
     const int vd0 = (tid >> 5) * VD;
-    u32x4 rawk[NBR][KC], rawc[KC], raws[KC];
-    vraw_t rawv[2];
+    u32x4 rawk[NBS], rawc, raws;
+    u32x2 rawv[2];
 
     auto load_raw = [&](int t) __attribute__((always_inline)) {
         const uint32_t k0 = (uint32_t)(t * BN);
+        const uint32_t off = (k0 + (uint32_t)(tid >> 3)) * ROWB + (uint32_t)(tid & 7) * 16;
 #pragma unroll
-        for (int i = 0; i < KC; ++i) {
-            const int ch = tid + NT * i;
-            const uint32_t off = (k0 + (uint32_t)(ch >> 3)) * ROWB + (uint32_t)(ch & 7) * 16;
-#pragma unroll
-            for (int br = 0; br < NBR; ++br) rawk[br][i] = bload(rk[br], off);
-            rawc[i] = bload(rc, off);
-            raws[i] = bload(rs, off);
-        }
+        for (int br = 0; br < NBS; ++br) rawk[br] = bload(rk[br], off);
+        rawc = bload(rc, off);
+        raws = bload(rs, off);
         const uint32_t offv = (k0 + 2u * vp) * ROWB + (uint32_t)vd0 * 2;
-        if constexpr (VD == 8) {
-            rawv[0] = bload(rv, offv);
-            rawv[1] = bload(rv, offv + ROWB);
-        } else {
-            rawv[0] = bload8(rv, offv);
-            rawv[1] = bload8(rv, offv + ROWB);
-        }
+        rawv[0] = bload8(rv, offv);
+        rawv[1] = bload8(rv, offv + ROWB);
     };
 
     // V^T key positions: bits 2 and 3 of the key index swapped, so that the 8 keys one
     // lane multiplies in a P.V step (see load_v_operands) are contiguous.
     const int vpos = (2 * vp & ~12) | ((2 * vp & 4) << 1) | ((2 * vp & 8) >> 1);
+    const int kat = (tid >> 3) * KS_STRIDE + (tid & 7) * 8;
     auto stage = [&](int buf) __attribute__((always_inline)) {
         uint16_t *Ks = smem + buf * BUF_ELEMS;
-        uint16_t *Vt = Ks + NBR * KS_ELEMS;
+        uint16_t *Vt = Ks + NBS * KS_ELEMS;
 #pragma unroll
-        for (int i = 0; i < KC; ++i) {
-            const int ch = tid + NT * i;
-            const int at = (ch >> 3) * KS_STRIDE + (ch & 7) * 8;
-#pragma unroll
-            for (int br = 0; br < NBR; ++br)
-                *reinterpret_cast<u32x4 *>(Ks + br * KS_ELEMS + at) = rope8<IO>(rawk[br][i], rawc[i], raws[i]);
-        }
+        for (int br = 0; br < NBS; ++br)
+            *reinterpret_cast<u32x4 *>(Ks + br * KS_ELEMS + kat) = rope8<IO>(rawk[br], rawc, raws);
 #pragma unroll
         for (int j = 0; j < VD; ++j) {
             const uint32_t wa = rawv[0][j >> 1], wb = rawv[1][j >> 1];
@@ -434,46 +382,32 @@ __global__ __launch_bounds__(NW * 64, DIFF ? 1 : 2) void attn_fwd_kernel(Params 
     };
 
     // ---- MFMA stages -----------------------------------------------------------
-    auto qk = [&](int buf, f32x16 (&s)[NBR][QB][2]) __attribute__((always_inline)) {
-        const uint16_t *Ks = smem + buf * BUF_ELEMS;
+    // S^T = K Q^T for this wave's branch: [kb] = keys 32 kb .. 32 kb + 31 of the tile
+    auto qk = [&](int buf, f32x16 (&s)[2]) __attribute__((always_inline)) {
+        const uint16_t *Ks = smem + buf * BUF_ELEMS + wbr * KS_ELEMS;
 #pragma unroll
-        for (int br = 0; br < NBR; ++br)
+        for (int kb = 0; kb < 2; ++kb) {
+            u32x4 ka[4];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                u32x4 ka[4];
+            for (int ks = 0; ks < 4; ++ks) ka[ks] = lds16(Ks + (kb * 32 + r) * KS_STRIDE + 16 * ks + 8 * g);
+            f32x16 acc = {};
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    ka[ks] = lds16(Ks + br * KS_ELEMS + (kb * 32 + r) * KS_STRIDE + 16 * ks + 8 * g);
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    f32x16 acc = {};
-#pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) acc = mfma_qk<IO>(ka[ks], qreg[br][qb][ks], acc);
-                    s[br][qb][kb] = acc;
-                }
-            }
+            for (int ks = 0; ks < 4; ++ks) acc = mfma_qk<IO>(ka[ks], qreg[ks], acc);
+            s[kb] = acc;
+        }
     };
 
-    Branch st[NBR][QB];
-#pragma unroll
-    for (int br = 0; br < NBR; ++br)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            st[br][qb].o[0] = f32x16{};
-            st[br][qb].o[1] = f32x16{};
-#if SA3_SUM_MFMA
-            st[br][qb].l = f32x16{};
-#else
-            st[br][qb].l = 0.0f;
-#endif
-            st[br][qb].m = NEG_INF;
-            st[br][qb].a = 1.0f;
-        }
+    Branch st;
+    st.o[0] = f32x16{};
+    st.o[1] = f32x16{};
+    st.l = 0.0f;
+    st.m = NEG_INF;
+    st.a = 1.0f;
 
-    // mask of tile t for each query block of this wave (lane-level lo/span)
-    auto tile_mask = [&](int t, int qb) __attribute__((always_inline)) {
+    // mask of tile t for this wave's rows (lane-level lo/span)
+    auto tile_mask = [&](int t) __attribute__((always_inline)) {
         const int k0 = t * BN;
-        const int qi = qw + qb * 32 + r;
+        const int qi = qw + r;
         int lo = 0, hi = L - 1;
         if (window >= 0 && qi < L) {
             lo = max(lo, qi - window);
@@ -492,7 +426,7 @@ __global__ __launch_bounds__(NW * 64, DIFF ? 1 : 2) void attn_fwd_kernel(Params 
         return mk;
     };
     // the wave-uniform decision whether tile t needs element masks
-    const int qhi_live = min(qw + 32 * QB - 1, L - 1);
+    const int qhi_live = min(qw + 31, L - 1);
     auto tile_needs_mask = [&](int t) __attribute__((always_inline)) {
         const int k0 = t * BN;
         if (k0 + BN > L) return true;
@@ -504,7 +438,7 @@ __global__ __launch_bounds__(NW * 64, DIFF ? 1 : 2) void attn_fwd_kernel(Params 
     // The first block multiplies a zero P by the V tile of stage t_begin - 1: clear it.
     {
         uint32_t *vz = reinterpret_cast<uint32_t *>(smem + ((t_begin + NBUF - 1) % NBUF) * BUF_ELEMS +
-                                                    NBR * KS_ELEMS);
+                                                    NBS * KS_ELEMS);
         for (int i = tid; i < VT_ELEMS / 2; i += NT) vz[i] = 0u;
     }
     load_raw(t_begin);
@@ -514,89 +448,47 @@ __global__ __launch_bounds__(NW * 64, DIFF ? 1 : 2) void attn_fwd_kernel(Params 
     load_raw(t_begin + 2);
     __syncthreads();
 
-    // Score registers: with SA3_PIPE_S the block of tile t reads sbuf[P] and writes the
-    // scores of tile t+1 into sbuf[P^1]; otherwise one set is consumed, then rewritten.
+    // Scores: one set, consumed by the softmax of tile t, then rewritten with tile t+1.
     // P ping-pongs: the block of tile t writes pbuf[P] (and its row sums rsum[P]) and
     // multiplies pbuf[P^1], the P of tile t-1. P is the parity of t - t_begin, known at
     // compile time in the unrolled loop.
-    constexpr int NS = SA3_PIPE_S ? 2 : 1;
-    f32x16 sbuf[NS][NBR][QB][2];
-    u32x4 pbuf[2][NBR][QB][2][2];
-    float rsum[2][NBR][QB];
+    f32x16 sbuf[2];
+    u32x4 pbuf[2][2][2];
+    float rsum[2];
+    rsum[1] = 0.0f;
 #pragma unroll
-    for (int br = 0; br < NBR; ++br)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            rsum[1][br][qb] = 0.0f;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt) pbuf[1][br][qb][kb][tt] = u32x4{0, 0, 0, 0};
-        }
-    qk(t_begin % NBUF, sbuf[0]);
-    // A-operand rows of the row-sum block: row 0 (lanes 0 and 32) all ones in fp16.
-    const u32x4 ones = (r == 0) ? u32x4{0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u} : u32x4{0, 0, 0, 0};
-    (void)ones;
+        for (int tt = 0; tt < 2; ++tt) pbuf[1][kb][tt] = u32x4{0, 0, 0, 0};
+    qk(t_begin % NBUF, sbuf);
 
     // Bring O and l to the base of tile t-1 (whose P is pbuf[PP]) before its P.V
     // product: O *= alpha, l = l * alpha + its row sum. alpha is exactly 1 unless the
     // row's base moved, so the product is exact; it is done on every tile because a
     // wave-uniform branch around it made the register allocator copy all 32 accumulator
-    // registers on every tile (and spill in the two-branch kernel).
+    // registers on every tile.
     auto carry = [&](auto pp_tag) __attribute__((always_inline)) {
         constexpr int PP = decltype(pp_tag)::value;
-        bool moved = false;
 #pragma unroll
-        for (int br = 0; br < NBR; ++br)
+        for (int db = 0; db < 2; ++db)
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) moved = moved || (st[br][qb].a != 1.0f);
-        if (SA3_ALWAYS_RESCALE || __builtin_amdgcn_ballot_w64(moved)) {
-#pragma unroll
-            for (int br = 0; br < NBR; ++br)
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    Branch &b = st[br][qb];
-#pragma unroll
-                    for (int db = 0; db < 2; ++db)
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) b.o[db][i] *= b.a;
-#if SA3_SUM_MFMA
-                    b.l[0] *= b.a;
-#endif
-                }
-        }
-#pragma unroll
-        for (int br = 0; br < NBR; ++br)
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                Branch &b = st[br][qb];
-#if !SA3_SUM_MFMA
-                b.l = __builtin_fmaf(b.l, b.a, rsum[PP][br][qb]);
-#endif
-                b.a = 1.0f;
-            }
+            for (int i = 0; i < 16; ++i) st.o[db][i] *= st.a;
+        st.l = __builtin_fmaf(st.l, st.a, rsum[PP]);
+        st.a = 1.0f;
     };
 
-    // O^T += V^T P^T (and l += 1^T P^T on the MFMA) for the given V^T operands and P
-    auto pv_sum = [&](const u32x4 (&va)[2][2][2], const u32x4 (&p)[NBR][QB][2][2]) __attribute__((always_inline)) {
+    // O^T += V^T P^T for the given V^T operands and P
+    auto pv_sum = [&](const u32x4 (&va)[2][2][2], const u32x4 (&p)[2][2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int br = 0; br < NBR; ++br)
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) {
-                        Branch &b = st[br][qb];
-                        b.o[0] = mfma_pv(va[0][kb][tt], p[br][qb][kb][tt], b.o[0]);
-                        b.o[1] = mfma_pv(va[1][kb][tt], p[br][qb][kb][tt], b.o[1]);
-#if SA3_SUM_MFMA
-                        b.l = mfma_pv(ones, p[br][qb][kb][tt], b.l);
-#endif
-                    }
+            for (int tt = 0; tt < 2; ++tt) {
+                st.o[0] = mfma_pv(va[0][kb][tt], p[kb][tt], st.o[0]);
+                st.o[1] = mfma_pv(va[1][kb][tt], p[kb][tt], st.o[1]);
+            }
     };
     auto load_v_operands = [&](int buf, u32x4 (&va)[2][2][2]) __attribute__((always_inline)) {
-        const uint16_t *Vt = smem + buf * BUF_ELEMS + NBR * KS_ELEMS;
+        const uint16_t *Vt = smem + buf * BUF_ELEMS + NBS * KS_ELEMS;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -612,94 +504,24 @@ __global__ __launch_bounds__(NW * 64, DIFF ? 1 : 2) void attn_fwd_kernel(Params 
         constexpr bool MASK = decltype(mask_tag)::value;
         constexpr int PC = decltype(par_tag)::value;
         constexpr int PN = PC ^ 1;
-        constexpr int SI = SA3_PIPE_S ? PC : 0;
-        constexpr int SO = SA3_PIPE_S ? PN : 0;
         carry(std::integral_constant<int, PN>{});
-        TileMask mk[QB];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) mk[qb] = MASK ? tile_mask(t, qb) : TileMask{0, 0};
+        const TileMask mk = MASK ? tile_mask(t) : TileMask{0, 0};
         // MFMA operands read from LDS first so their latency overlaps the softmax
         u32x4 va[2][2][2];
         load_v_operands((t + NBUF - 1) % NBUF, va);
-#if SA3_PIPE_S
-        u32x4 ka[NBR][2][4];
-        {
-            const uint16_t *Ks = smem + ((t + 1) % NBUF) * BUF_ELEMS;
-#pragma unroll
-            for (int br = 0; br < NBR; ++br)
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int ks = 0; ks < 4; ++ks)
-                        ka[br][kb][ks] = lds16(Ks + br * KS_ELEMS + (kb * 32 + r) * KS_STRIDE + 16 * ks + 8 * g);
-        }
-#endif
         // softmax of tile t: the tile maximum decides whether the base moves (lazily:
         // only past TAU), then P = 2^(s*c - m) in fp16
-#pragma unroll
-        for (int br = 0; br < NBR; ++br)
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                Branch &b = st[br][qb];
-                const float mt = tile_max<MASK>(sbuf[SI][br][qb], c, mk[qb]);
-                const float mn = (mt > b.m + TAU) ? mt : b.m;
-                b.a = (mn == b.m) ? 1.0f : ((b.m == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(b.m - mn));
-                b.m = mn;
-                softmax_p<MASK>(sbuf[SI][br][qb], c, (mn == NEG_INF) ? 0.0f : -mn, mk[qb], pbuf[PC][br][qb],
-                                rsum[PC][br][qb]);
-            }
+        {
+            const float mt = tile_max<MASK>(sbuf, c, mk);
+            const float mn = (mt > st.m + TAU) ? mt : st.m;
+            st.a = (mn == st.m) ? 1.0f : ((st.m == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(st.m - mn));
+            st.m = mn;
+            softmax_p<MASK>(sbuf, c, (mn == NEG_INF) ? 0.0f : -mn, mk, pbuf[PC], rsum[PC]);
+        }
         pv_sum(va, pbuf[PN]);
-#if SA3_PIPE_S
-#pragma unroll
-        for (int br = 0; br < NBR; ++br)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    f32x16 acc = {};
-#pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) acc = mfma_qk<IO>(ka[br][kb][ks], qreg[br][qb][ks], acc);
-                    sbuf[SO][br][qb][kb] = acc;
-                }
-#else
-        qk((t + 1) % NBUF, sbuf[SO]);
-#endif
+        qk((t + 1) % NBUF, sbuf);
         stage((t + 2) % NBUF);
         load_raw(t + 3);
-        // Group order for the scheduler: the MFMA operand reads first, then the MFMAs
-        // spread evenly through the softmax and staging VALU work.
-        constexpr int NMFMA = 16 * NBR * QB;
-        if constexpr (SA3_SCHED == 1) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 8 * NBR, 0);
-#pragma unroll
-            for (int i = 0; i < NMFMA; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-            }
-        } else if constexpr (SA3_SCHED == 2) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 16 + 8 * NBR, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
-#pragma unroll
-            for (int i = 0; i < NMFMA; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
-            }
-        } else if constexpr (SA3_SCHED == 3) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-#pragma unroll
-            for (int i = 0; i < 8 * NBR * QB; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x100, 8 * NBR, 0);
-#pragma unroll
-            for (int i = 0; i < 8 * NBR * QB; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
-            }
-        }
         __syncthreads();
     };
 
@@ -731,46 +553,51 @@ __global__ __launch_bounds__(NW * 64, DIFF ? 1 : 2) void attn_fwd_kernel(Params 
     }
 
     // ---- epilogue: normalise, subtract, cast, store rows < L -------------------------
+    const float inv = 1.0f / pair_sum(st.l);
+    const int qi = qw + r;
+    if constexpr (DIFF) {
+        // The second branch hands x2 = O2 / l2 to the first through LDS (the stages
+        // are free once every wave has left the loop): element e of lane l of query
+        // block wq at word (wq * 32 + e) * 64 + l, so a wave's 64 lanes write 64
+        // consecutive words per element.
+        float *xb = reinterpret_cast<float *>(smem);
+        __syncthreads();
+        if (wbr == 1) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-#if SA3_SUM_MFMA
-        // row sums sit in element 0 of lanes 0..31; lanes 32..63 hold zeros there
-        const float inv = 1.0f / pair_sum(st[0][qb].l[0]);
-        float inv2 = 0.0f;
-        if constexpr (DIFF) inv2 = 1.0f / pair_sum(st[NBR - 1][qb].l[0]);
-#else
-        const float inv = 1.0f / pair_sum(st[0][qb].l);
-        float inv2 = 0.0f;
-        if constexpr (DIFF) inv2 = 1.0f / pair_sum(st[NBR - 1][qb].l);
-#endif
-        const int qi = qw + qb * 32 + r;
-        if (qi >= L) continue;
-        const size_t row = head + (size_t)qi * HD;
+            for (int db = 0; db < 2; ++db)
 #pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-            for (int grp = 0; grp < 4; ++grp) {
-                float o[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    o[j] = st[0][qb].o[db][grp * 4 + j] * inv;
-                    if constexpr (DIFF) o[j] = o[j] - P.lam * (st[NBR - 1][qb].o[db][grp * 4 + j] * inv2);
-                }
-                const int d = db * 32 + grp * 8 + g * 4;
-                if (P.out_dtype == OUT_F32) {
-                    *reinterpret_cast<f32x4 *>(static_cast<float *>(P.out) + row + d) = f32x4{o[0], o[1], o[2], o[3]};
-                } else if (P.out_dtype == OUT_BF16) {
-                    *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(P.out) + row + d) =
-                        u32x2{pack2<IO_BF16>(o[0], o[1]), pack2<IO_BF16>(o[2], o[3])};
-                } else {
-                    *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(P.out) + row + d) =
-                        u32x2{pack2<IO_F16>(o[0], o[1]), pack2<IO_F16>(o[2], o[3])};
-                }
-            }
+                for (int i = 0; i < 16; ++i) xb[(wq * 32 + db * 16 + i) * 64 + lane] = st.o[db][i] * inv;
+        }
+        __syncthreads();
+        if (wbr == 1) return;
     }
+    if (qi >= L) return;
+    const size_t row = head + (size_t)qi * HD;
+    const float *xb = reinterpret_cast<const float *>(smem);
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) {
+            float o[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                o[j] = st.o[db][grp * 4 + j] * inv;
+                if constexpr (DIFF) o[j] = o[j] - P.lam * xb[(wq * 32 + db * 16 + grp * 4 + j) * 64 + lane];
+            }
+            const int d = db * 32 + grp * 8 + g * 4;
+            if (P.out_dtype == OUT_F32) {
+                *reinterpret_cast<f32x4 *>(static_cast<float *>(P.out) + row + d) = f32x4{o[0], o[1], o[2], o[3]};
+            } else if (P.out_dtype == OUT_BF16) {
+                *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(P.out) + row + d) =
+                    u32x2{pack2<IO_BF16>(o[0], o[1]), pack2<IO_BF16>(o[2], o[3])};
+            } else {
+                *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(P.out) + row + d) =
+                    u32x2{pack2<IO_F16>(o[0], o[1]), pack2<IO_F16>(o[2], o[3])};
+            }
+        }
 }
 
-template <int IO, bool DIFF, int NW, int QB>
+template <int IO, bool DIFF>
 hipError_t launch(const LaunchArgs &a, int n_qtiles) {
     Params P;
     P.q = static_cast<const uint16_t *>(a.q);
@@ -788,29 +615,24 @@ hipError_t launch(const LaunchArgs &a, int n_qtiles) {
     P.lam = a.lam;
     P.c = a.scale_log2;
     const unsigned grid = (unsigned)n_qtiles * (unsigned)a.B * (unsigned)a.H;
-    hipLaunchKernelGGL((attn_fwd_kernel<IO, DIFF, NW, QB>), dim3(grid), dim3(NW * 64), 0,
-                       static_cast<hipStream_t>(a.stream), P);
+    hipLaunchKernelGGL((attn_fwd_kernel<IO, DIFF>), dim3(grid), dim3(512), 0, static_cast<hipStream_t>(a.stream), P);
     return hipGetLastError();
 }
 
-// Instances: plain = 8 waves x 32 query rows (two waves per SIMD); differential =
-// 4 waves x 32 rows (one wave per SIMD: two branches of state per wave).
-constexpr int NW_PLAIN = SA3_NW_PLAIN, NW_DIFF = 4;
-
 }  // namespace
 
-int tile_rows(const LaunchArgs &a) { return 32 * (a.diff ? NW_DIFF : NW_PLAIN); }
+// Query rows per workgroup: 256 (8 waves x 32) plain, 128 (4 pairs of waves) differential.
+int tile_rows(const LaunchArgs &a) { return a.diff ? 128 : 256; }
 
 int launch_forward(const LaunchArgs &a) {
     const int bm = tile_rows(a);
     const int n_qtiles = (a.L + bm - 1) / bm;
     const bool bf = a.dtype == 1;
     hipError_t e;
-    if (a.diff) {
-        e = bf ? launch<IO_BF16, true, NW_DIFF, 1>(a, n_qtiles) : launch<IO_F16, true, NW_DIFF, 1>(a, n_qtiles);
-    } else {
-        e = bf ? launch<IO_BF16, false, NW_PLAIN, 1>(a, n_qtiles) : launch<IO_F16, false, NW_PLAIN, 1>(a, n_qtiles);
-    }
+    if (a.diff)
+        e = bf ? launch<IO_BF16, true>(a, n_qtiles) : launch<IO_F16, true>(a, n_qtiles);
+    else
+        e = bf ? launch<IO_BF16, false>(a, n_qtiles) : launch<IO_F16, false>(a, n_qtiles);
     return (int)e;
 }
 
