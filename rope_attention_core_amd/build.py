@@ -3,7 +3,8 @@
     python -m rope_attention_core_amd.build [--asm DIR]
 
 The library is one shared object: the C-ABI layer (csrc/api.cpp), the host RoPE
-table (csrc/rope_table.cpp) and the kernels (csrc/attn_fwd.hip). It is written next
+table (csrc/rope_table.cpp) and the kernels (csrc/attn_fwd.hip for full attention and
+wide windows, csrc/attn_narrow.hip for windows of half-width <= 32). It is written next
 to this file so that it travels with the source tree.
 """
 
@@ -20,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsa3attn.so")
 
 ARCH = "gfx950"
-SOURCES = ["attn_fwd.hip", "api.cpp", "rope_table.cpp"]
+SOURCES = ["attn_fwd.hip", "attn_narrow.hip", "api.cpp", "rope_table.cpp"]
 # Packed FP32 instructions are kept out of the device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]

@@ -47,212 +47,10 @@
 //    robin over the 8 XCDs) are consecutive tiles of the same heads, keeping each
 //    head's K/V in one XCD's L2.
 
-#include <hip/hip_runtime.h>
-
-#include <cmath>
-#include <cstdint>
-#include <type_traits>
-
-#include "sa3attn_internal.hpp"
+#include "attn_common.hpp"
 
 namespace sa3 {
 namespace {
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-constexpr int IO_F16 = 0;
-constexpr int IO_BF16 = 1;
-constexpr int OUT_BF16 = 1;
-constexpr int OUT_F32 = 2;
-
-constexpr int HD = 64;            // head dim
-constexpr int ROWB = HD * 2;      // bytes per q/k/v row, and per cos/sin row (32 floats)
-constexpr int BN = 64;            // keys per tile
-constexpr int NBUF = 4;           // LDS stages
-constexpr int KS_STRIDE = 72;     // LDS row stride of the K tile in 16-bit elements
-constexpr int VT_STRIDE = 72;     // LDS row stride of the V^T tile in 16-bit elements
-constexpr uint32_t RSRC_WORD3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9)
-constexpr float TAU = 8.0f;       // lazy rescale: a row's base moves only when its max passes it by more
-
-struct Params {
-    const uint16_t *q, *k, *v;
-    const float *cos, *sin;
-    void *out;
-    long long branch_stride;      // elements from branch 1 to branch 2 of q / k
-    int L, window, n_qtiles, out_dtype, neg_scale;
-    float lam, c;                 // c = |scale| * log2(e)
-};
-
-// ---- element conversions -------------------------------------------------------
-
-template <int IO>
-__device__ __forceinline__ void unpack2(uint32_t u, float &a, float &b) {
-    if constexpr (IO == IO_BF16) {
-        a = __uint_as_float(u << 16);
-        b = __uint_as_float(u & 0xffff0000u);
-    } else {
-        f16x2 h = __builtin_bit_cast(f16x2, u);
-        a = (float)h[0];
-        b = (float)h[1];
-    }
-}
-
-// Round two floats to nearest-even in the given 16-bit type and pack them (a low).
-template <int IO>
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-    if constexpr (IO == IO_BF16) {
-        bf16x2 h = {(__bf16)a, (__bf16)b};
-        return __builtin_bit_cast(uint32_t, h);
-    } else {
-        f16x2 h = {(_Float16)a, (_Float16)b};
-        return __builtin_bit_cast(uint32_t, h);
-    }
-}
-
-// RoPE on 8 consecutive elements (4 adjacent pairs) with their cos/sin, in FP32 with
-// every product and sum rounded on its own, then rounded to the IO dtype.
-template <int IO>
-__device__ __forceinline__ u32x4 rope8(u32x4 x, u32x4 cw, u32x4 sw) {
-#pragma clang fp contract(off)
-    u32x4 r;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        float x0, x1;
-        unpack2<IO>(x[j], x0, x1);
-        const float c = __uint_as_float(cw[j]);
-        const float s = __uint_as_float(sw[j]);
-        const float a = x0 * c;
-        const float b = x1 * s;
-        const float e = x0 * s;
-        const float f = x1 * c;
-        r[j] = pack2<IO>(a - b, e + f);
-    }
-    return r;
-}
-
-template <int IO>
-__device__ __forceinline__ f32x16 mfma_qk(u32x4 a, u32x4 b, f32x16 acc) {
-    if constexpr (IO == IO_BF16)
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
-    else
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                      __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
-}
-
-__device__ __forceinline__ f32x16 mfma_pv(u32x4 a, u32x4 b, f32x16 acc) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
-}
-
-// max / sum over the two lanes (l, l ^ 32) that hold the same query.
-__device__ __forceinline__ float pair_max(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, (int)RSRC_WORD3);
-}
-// 16- and 8-byte loads; bytes at or past num_records read as zero.
-__device__ __forceinline__ u32x4 bload(rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-}
-__device__ __forceinline__ u32x2 bload8(rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
-}
-
-__device__ __forceinline__ u32x4 lds16(const uint16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
-
-// Validity of the keys of a masked tile for one lane: key offset o (0..63 inside the
-// tile, as laid out in the S^T accumulator) is valid iff lo <= o - 4g <= lo + span,
-// evaluated as one unsigned compare.
-struct TileMask {
-    int lo;           // first valid key offset relative to k0 + 4g
-    uint32_t span;    // number of further valid offsets
-};
-
-// softmax of one 32-query block of one branch over one 64-key tile against the
-// exponent base -nb: P^T packed as fp16 MFMA B operands [kb][tt].
-template <bool MASK>
-__device__ __forceinline__ void softmax_p(const f32x16 (&s)[2], float c, float nb, TileMask mk,
-                                          u32x4 (&p)[2][2], float &rowsum) {
-    const float NEG_INF = -__builtin_inff();
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        float e[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float t = __builtin_fmaf(s[kb][i], c, nb);
-            if constexpr (MASK) {
-                const int o = kb * 32 + (i >> 2) * 8 + (i & 3);
-                t = ((uint32_t)(o - mk.lo) <= mk.span) ? t : NEG_INF;
-            }
-            e[i] = __builtin_amdgcn_exp2f(t);
-        }
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            u32x4 w;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const f16x2 h = {(_Float16)e[8 * tt + 2 * j], (_Float16)e[8 * tt + 2 * j + 1]};
-                w[j] = __builtin_bit_cast(uint32_t, h);
-                // row sum of the rounded P (what the MFMA multiplies), four chains
-                acc[2 * kb + tt] = __builtin_amdgcn_fdot2(h, f16x2{(_Float16)1.0f, (_Float16)1.0f},
-                                                          acc[2 * kb + tt], false);
-            }
-            p[kb][tt] = w;
-        }
-    }
-    rowsum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-}
-
-// Maximum of 32 values as a tree of 3-input maxima (depth 4) rather than a chain.
-__device__ __forceinline__ float max32(const float (&v)[32]) {
-    float a[11];
-#pragma unroll
-    for (int i = 0; i < 10; ++i) a[i] = fmaxf(fmaxf(v[3 * i], v[3 * i + 1]), v[3 * i + 2]);
-    a[10] = fmaxf(v[30], v[31]);
-    const float b0 = fmaxf(fmaxf(a[0], a[1]), a[2]);
-    const float b1 = fmaxf(fmaxf(a[3], a[4]), a[5]);
-    const float b2 = fmaxf(fmaxf(a[6], a[7]), a[8]);
-    const float b3 = fmaxf(a[9], a[10]);
-    return fmaxf(fmaxf(b0, b1), fmaxf(b2, b3));
-}
-
-// exact maximum of c * s over the valid keys of this lane pair (log2 units)
-template <bool MASK>
-__device__ __forceinline__ float tile_max(const f32x16 (&s)[2], float c, TileMask mk) {
-    const float NEG_INF = -__builtin_inff();
-    float v[32];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float x = s[kb][i];
-            if constexpr (MASK) {
-                const int o = kb * 32 + (i >> 2) * 8 + (i & 3);
-                x = ((uint32_t)(o - mk.lo) <= mk.span) ? x : NEG_INF;
-            }
-            v[kb * 16 + i] = x;
-        }
-    const float mx = pair_max(max32(v));
-    return (mx == NEG_INF) ? NEG_INF : mx * c;
-}
-
 
 struct Branch {
     f32x16 o[2];     // O^T accumulators for d in [0, 32) and [32, 64)
@@ -621,10 +419,19 @@ hipError_t launch(const LaunchArgs &a, int n_qtiles) {
 
 }  // namespace
 
+// Windows of half-width <= NARROW_MAX_W go to the narrow-window kernel (attn_narrow.hip),
+// which stages a query block's whole key span at once.
+constexpr int NARROW_MAX_W = 32;
+bool use_narrow(const LaunchArgs &a) { return a.window >= 0 && a.window <= NARROW_MAX_W; }
+
 // Query rows per workgroup: 256 (8 waves x 32) plain, 128 (4 pairs of waves) differential.
-int tile_rows(const LaunchArgs &a) { return a.diff ? 128 : 256; }
+int tile_rows(const LaunchArgs &a) {
+    if (use_narrow(a)) return narrow_tile_rows(a);
+    return a.diff ? 128 : 256;
+}
 
 int launch_forward(const LaunchArgs &a) {
+    if (use_narrow(a)) return launch_narrow(a);
     const int bm = tile_rows(a);
     const int n_qtiles = (a.L + bm - 1) / bm;
     const bool bf = a.dtype == 1;

@@ -1,0 +1,311 @@
+// Fused RoPE attention forward for narrow sliding windows (half-width w <= 32) on
+// gfx950: the SAME-L decoder's own window is +-17 keys (TensorRT engines README,
+// section "Building your own"; "How the kernels differ" for the differential form).
+//
+// With so few keys per query the work is bound by HBM traffic and load latency, not
+// by the MFMA: the long-span kernel's four-stage software pipeline would mostly run
+// its prologue. Here one workgroup takes a short block of query rows and stages the
+// whole key span they can see, [q0 - w, q0 + BM - 1 + w], at once (BM + 64 keys),
+// then each wave computes its scores over that span, one exact softmax (the maximum
+// over the whole span is known, so there is no running rescale), and P.V, and stores.
+// Small workgroups and a small LDS footprint keep several of them resident per CU so
+// that their loads overlap.
+//
+//  * Plain: 4 waves x 32 query rows (BM = 128), span 192 keys.
+//  * Differential: waves w and w + 2 share 32 rows, one softmax branch each (BM = 64),
+//    span 128 keys; the second branch hands O2 / l2 to the first through LDS.
+//  * Arithmetic per element is the long-span kernel's: RoPE in FP32 with separate
+//    roundings then RNE to the IO dtype, S^T = K Q^T on MFMA (FP32 accumulation),
+//    P = 2^(s * c - m) rounded to fp16, FP32 row sums of the rounded P, O^T = V^T P^T
+//    on MFMA with V in fp16, out = O / l (minus lambda * O2 / l2 in FP32).
+//  * Keys before 0 or at / after L read as zeros through the buffer range check (a
+//    negative row gives an offset far above num_records) and are masked.
+
+#include "attn_common.hpp"
+
+namespace sa3 {
+namespace {
+
+// Span of keys staged per workgroup and the LDS strides (16-bit elements). The V^T
+// stride keeps the 16-byte operand reads of 16 consecutive rows on distinct banks.
+template <bool DIFF>
+struct NarrowShape {
+    static constexpr int NT = 256;                    // threads (4 waves)
+    static constexpr int NBS = DIFF ? 2 : 1;          // branches staged
+    static constexpr int WPB = DIFF ? 2 : 4;          // query blocks (waves) per branch
+    static constexpr int BM = WPB * 32;               // query rows per workgroup
+    static constexpr int NK = BM + 64;                // keys staged (covers BM + 2w, w <= 32)
+    static constexpr int NKB = NK / 32;               // 32-key blocks
+    static constexpr int KS = 72;                     // K row stride
+    static constexpr int VS = NK + 8;                 // V^T row stride
+    static constexpr int K_ELEMS = NK * KS;
+    static constexpr int V_ELEMS = HD * VS;
+    static constexpr int LDS_ELEMS = NBS * K_ELEMS + V_ELEMS;
+};
+
+template <int IO, bool DIFF>
+__global__ __launch_bounds__(256, 2) void attn_narrow_kernel(Params P) {
+    using S = NarrowShape<DIFF>;
+    constexpr int NT = S::NT, NBS = S::NBS, WPB = S::WPB, BM = S::BM, NK = S::NK, NKB = S::NKB;
+    constexpr int KC = NK * 8 / NT;          // K chunks (8 elements) per thread per branch
+    constexpr int VC = NK * 4 / NT;          // V items (2 keys x 8 d) per thread
+    static_assert(NK * 8 % NT == 0 && NK * 4 % NT == 0, "staging split");
+    static_assert(!DIFF || S::LDS_ELEMS * 2 >= WPB * 32 * 64 * 4, "LDS too small for the O2 exchange");
+    __shared__ __attribute__((aligned(16))) uint16_t smem[S::LDS_ELEMS];
+
+    const float NEG_INF = -__builtin_inff();
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wbr = DIFF ? wave / WPB : 0;
+    const int wq = DIFF ? wave % WPB : wave;
+    const int r = lane & 31;
+    const int g = lane >> 5;
+    const int L = P.L;
+    const int w = P.window;
+    const float c = P.c;
+
+    // XCD-aware remap of the workgroup id, as in the long-span kernel.
+    const int nblk = gridDim.x;
+    const int bid = blockIdx.x;
+    const int per = nblk >> 3, rem = nblk & 7, xcd = bid & 7, idx = bid >> 3;
+    const int lid = (xcd < rem) ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+    const int bh = lid / P.n_qtiles;
+    const int qt = lid - bh * P.n_qtiles;
+
+    const size_t head = (size_t)bh * (size_t)L * HD;
+    const uint32_t nrec = (uint32_t)L * ROWB;
+    rsrc_t rk[NBS];
+#pragma unroll
+    for (int br = 0; br < NBS; ++br) rk[br] = make_rsrc(P.k + br * P.branch_stride + head, nrec);
+    const rsrc_t rq = make_rsrc(P.q + wbr * P.branch_stride + head, nrec);
+    const rsrc_t rv = make_rsrc(P.v + head, nrec);
+    const rsrc_t rc = make_rsrc(P.cos, nrec);
+    const rsrc_t rs = make_rsrc(P.sin, nrec);
+
+    const int q0 = qt * BM;
+    const int qw = q0 + wq * 32;
+    const int ks0 = q0 - w;                  // first staged key (may be negative)
+
+    // ---- issue every load: Q rows of this wave, then the K / cos / sin / V span ------
+    u32x4 rq_raw[4], rqc[4], rqs[4];
+    {
+        const uint32_t row = (uint32_t)(qw + r) * ROWB;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const uint32_t off = row + (uint32_t)(16 * ks + 8 * g) * 2;
+            rq_raw[ks] = bload(rq, off);
+            rqc[ks] = bload(rc, off);
+            rqs[ks] = bload(rs, off);
+        }
+    }
+    u32x4 rawk[NBS][KC], rawc[KC], raws[KC];
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+        const int it = tid + NT * i;
+        const uint32_t off = (uint32_t)(ks0 + (it >> 3)) * ROWB + (uint32_t)(it & 7) * 16;
+#pragma unroll
+        for (int br = 0; br < NBS; ++br) rawk[br][i] = bload(rk[br], off);
+        rawc[i] = bload(rc, off);
+        raws[i] = bload(rs, off);
+    }
+    // V item: keys 2p, 2p + 1 of the span and 8 values of d from 8 * ch
+    u32x4 rawv[VC][2];
+#pragma unroll
+    for (int i = 0; i < VC; ++i) {
+        const int it = tid + NT * i;
+        const int p = it % (NK / 2), ch = it / (NK / 2);
+        const uint32_t off = (uint32_t)(ks0 + 2 * p) * ROWB + (uint32_t)ch * 16;
+        rawv[i][0] = bload(rv, off);
+        rawv[i][1] = bload(rv, off + ROWB);
+    }
+
+    // ---- rotate Q into registers; rotate / transpose the span into LDS ---------------
+    u32x4 qreg[4];
+    const uint32_t qsign = P.neg_scale ? 0x80008000u : 0u;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qreg[ks] = rope8<IO>(rq_raw[ks], rqc[ks], rqs[ks]) ^ qsign;
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+        const int it = tid + NT * i;
+        const int at = (it >> 3) * S::KS + (it & 7) * 8;
+#pragma unroll
+        for (int br = 0; br < NBS; ++br)
+            *reinterpret_cast<u32x4 *>(smem + br * S::K_ELEMS + at) = rope8<IO>(rawk[br][i], rawc[i], raws[i]);
+    }
+    uint16_t *Vt = smem + NBS * S::K_ELEMS;
+#pragma unroll
+    for (int i = 0; i < VC; ++i) {
+        const int it = tid + NT * i;
+        const int p = it % (NK / 2), ch = it / (NK / 2);
+        // key positions inside each 16 carry bits 2 and 3 swapped (the P.V operand order)
+        const int k2 = 2 * p;
+        const int pos = (k2 & ~12) | ((k2 & 4) << 1) | ((k2 & 8) >> 1);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t wa = rawv[i][0][j >> 1], wb = rawv[i][1][j >> 1];
+            uint32_t wv;
+            if constexpr (IO == IO_BF16) {
+                const float fa = __uint_as_float((j & 1) ? (wa & 0xffff0000u) : (wa << 16));
+                const float fb = __uint_as_float((j & 1) ? (wb & 0xffff0000u) : (wb << 16));
+                wv = pack2<IO_F16>(fa, fb);
+            } else {
+                wv = (j & 1) ? __builtin_amdgcn_perm(wb, wa, 0x07060302u) : __builtin_amdgcn_perm(wb, wa, 0x05040100u);
+            }
+            *reinterpret_cast<uint32_t *>(Vt + (8 * ch + j) * S::VS + pos) = wv;
+        }
+    }
+    __syncthreads();
+
+    // ---- scores of this wave's 32 rows over the span: S^T blocks of 32 keys ----------
+    const uint16_t *Ks = smem + wbr * S::K_ELEMS;
+    f32x16 s[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+        u32x4 ka[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) ka[ks] = lds16(Ks + (kb * 32 + r) * S::KS + 16 * ks + 8 * g);
+        f32x16 acc = {};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) acc = mfma_qk<IO>(ka[ks], qreg[ks], acc);
+        s[kb] = acc;
+    }
+
+    // valid keys of this lane's query: [max(0, qi - w), min(L - 1, qi + w)], as offsets o
+    // inside the span relative to 4g (the accumulator layout), lo <= o <= lo + span
+    const int qi = qw + r;
+    int lo = max(0, qi - w) - (ks0 + 4 * g);
+    int hi = min(L - 1, qi + w) - (ks0 + 4 * g);
+    const bool any = hi >= lo;
+    const uint32_t span = any ? (uint32_t)(hi - lo) : 0u;
+    if (!any) lo = 1 << 20;
+    auto valid = [&](int kb, int i) __attribute__((always_inline)) {
+        const int o = kb * 32 + (i >> 2) * 8 + (i & 3);
+        return (uint32_t)(o - lo) <= span;
+    };
+
+    // exact maximum over the span (log2 units), then P = 2^(s c - m) in fp16
+    float mx = NEG_INF;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, valid(kb, i) ? s[kb][i] : NEG_INF);
+    mx = pair_max(mx);
+    const float nb = (mx == NEG_INF) ? 0.0f : -(mx * c);
+
+    u32x4 pk[NKB][2];
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+        float e[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float t = __builtin_fmaf(s[kb][i], c, nb);
+            e[i] = __builtin_amdgcn_exp2f(valid(kb, i) ? t : NEG_INF);
+        }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            u32x4 wv;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f16x2 h = {(_Float16)e[8 * tt + 2 * j], (_Float16)e[8 * tt + 2 * j + 1]};
+                wv[j] = __builtin_bit_cast(uint32_t, h);
+                acc[(kb & 1) * 2 + tt] = __builtin_amdgcn_fdot2(h, f16x2{(_Float16)1.0f, (_Float16)1.0f},
+                                                                acc[(kb & 1) * 2 + tt], false);
+            }
+            pk[kb][tt] = wv;
+        }
+    }
+    const float l = pair_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
+
+    // ---- O^T = V^T P^T over the span ----------------------------------------------
+    f32x16 o[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int db = 0; db < 2; ++db) {
+                const u32x4 va = lds16(Vt + (db * 32 + r) * S::VS + kb * 32 + 16 * tt + 8 * g);
+                o[db] = mfma_pv(va, pk[kb][tt], o[db]);
+            }
+
+    // ---- epilogue: normalise, subtract, cast, store rows < L -------------------------
+    const float inv = 1.0f / l;
+    if constexpr (DIFF) {
+        float *xb = reinterpret_cast<float *>(smem);
+        __syncthreads();   // every wave is done with the staged span
+        if (wbr == 1) {
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) xb[(wq * 32 + db * 16 + i) * 64 + lane] = o[db][i] * inv;
+        }
+        __syncthreads();
+        if (wbr == 1) return;
+    }
+    if (qi >= L) return;
+    const size_t row = head + (size_t)qi * HD;
+    const float *xb = reinterpret_cast<const float *>(smem);
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) {
+            float y[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                y[j] = o[db][grp * 4 + j] * inv;
+                if constexpr (DIFF) y[j] = y[j] - P.lam * xb[(wq * 32 + db * 16 + grp * 4 + j) * 64 + lane];
+            }
+            const int d = db * 32 + grp * 8 + g * 4;
+            if (P.out_dtype == OUT_F32) {
+                *reinterpret_cast<f32x4 *>(static_cast<float *>(P.out) + row + d) = f32x4{y[0], y[1], y[2], y[3]};
+            } else if (P.out_dtype == OUT_BF16) {
+                *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(P.out) + row + d) =
+                    u32x2{pack2<IO_BF16>(y[0], y[1]), pack2<IO_BF16>(y[2], y[3])};
+            } else {
+                *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(P.out) + row + d) =
+                    u32x2{pack2<IO_F16>(y[0], y[1]), pack2<IO_F16>(y[2], y[3])};
+            }
+        }
+}
+
+template <int IO, bool DIFF>
+hipError_t launch_n(const LaunchArgs &a) {
+    using S = NarrowShape<DIFF>;
+    Params P;
+    P.q = static_cast<const uint16_t *>(a.q);
+    P.k = static_cast<const uint16_t *>(a.k);
+    P.v = static_cast<const uint16_t *>(a.v);
+    P.cos = a.cos;
+    P.sin = a.sin;
+    P.out = a.out;
+    P.branch_stride = (long long)a.B * a.H * a.L * HD;
+    P.L = a.L;
+    P.window = a.window;
+    P.n_qtiles = (a.L + S::BM - 1) / S::BM;
+    P.out_dtype = a.out_dtype;
+    P.neg_scale = a.neg_scale;
+    P.lam = a.lam;
+    P.c = a.scale_log2;
+    const unsigned grid = (unsigned)P.n_qtiles * (unsigned)a.B * (unsigned)a.H;
+    hipLaunchKernelGGL((attn_narrow_kernel<IO, DIFF>), dim3(grid), dim3(S::NT), 0,
+                       static_cast<hipStream_t>(a.stream), P);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int narrow_tile_rows(const LaunchArgs &a) { return a.diff ? NarrowShape<true>::BM : NarrowShape<false>::BM; }
+
+int launch_narrow(const LaunchArgs &a) {
+    const bool bf = a.dtype == 1;
+    hipError_t e;
+    if (a.diff)
+        e = bf ? launch_n<IO_BF16, true>(a) : launch_n<IO_F16, true>(a);
+    else
+        e = bf ? launch_n<IO_BF16, false>(a) : launch_n<IO_F16, false>(a);
+    return (int)e;
+}
+
+}  // namespace sa3

@@ -1,5 +1,5 @@
 // Internal interface between the C-ABI layer (api.cpp) and the gfx950 kernels
-// (attn_fwd.hip). Not installed; not part of the public header.
+// (attn_fwd.hip, attn_narrow.hip). Not installed; not part of the public header.
 #pragma once
 
 #include <cstdint>
@@ -31,5 +31,9 @@ int launch_forward(const LaunchArgs &a);
 // Query rows handled by one workgroup of the instance launch_forward picks, so the
 // host can check the grid size before launching.
 int tile_rows(const LaunchArgs &a);
+
+// The narrow-window kernel (half-width <= 32): launcher and rows per workgroup.
+int launch_narrow(const LaunchArgs &a);
+int narrow_tile_rows(const LaunchArgs &a);
 
 }  // namespace sa3
