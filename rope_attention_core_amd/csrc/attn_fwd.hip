@@ -419,10 +419,9 @@ hipError_t launch(const LaunchArgs &a, int n_qtiles) {
 
 }  // namespace
 
-// Windows of half-width <= NARROW_MAX_W go to the narrow-window kernel (attn_narrow.hip),
-// which stages a query block's whole key span at once.
-constexpr int NARROW_MAX_W = 32;
-bool use_narrow(const LaunchArgs &a) { return a.window >= 0 && a.window <= NARROW_MAX_W; }
+// Sequences of at most 256 keys and windows of half-width <= 32 go to the single-span
+// kernel (attn_narrow.hip), which stages a query block's whole key span at once.
+bool use_narrow(const LaunchArgs &a) { return narrow_applies(a); }
 
 // Query rows per workgroup: 256 (8 waves x 32) plain, 128 (4 pairs of waves) differential.
 int tile_rows(const LaunchArgs &a) {

@@ -1,19 +1,21 @@
-// Fused RoPE attention forward for narrow sliding windows (half-width w <= 32) on
-// gfx950: the SAME-L decoder's own window is +-17 keys (TensorRT engines README,
-// section "Building your own"; "How the kernels differ" for the differential form).
+// Fused RoPE attention forward on gfx950 for key spans short enough to stage at once:
+// narrow sliding windows (half-width w <= 32; the SAME-L decoder's own window is +-17
+// keys, TensorRT engines README, section "Building your own"; "How the kernels differ"
+// for the differential form) and short sequences (L <= 256: the short latents of the
+// DiTs, sa3_trt README, section "DiT precision").
 //
 // With so few keys per query the work is bound by HBM traffic and load latency, not
 // by the MFMA: the long-span kernel's four-stage software pipeline would mostly run
 // its prologue. Here one workgroup takes a short block of query rows and stages the
-// whole key span they can see, [q0 - w, q0 + BM - 1 + w], at once (BM + 64 keys),
-// then each wave computes its scores over that span, one exact softmax (the maximum
-// over the whole span is known, so there is no running rescale), and P.V, and stores.
-// Small workgroups and a small LDS footprint keep several of them resident per CU so
-// that their loads overlap.
+// whole key span they can see at once ([q0 - w, q0 + BM - 1 + w], BM + 64 keys, for a
+// narrow window; all of [0, L) for a short sequence), then each wave computes its
+// scores over that span, one exact softmax (the maximum over the whole span is known,
+// so there is no running rescale), and P.V, and stores. Small workgroups and a small
+// LDS footprint keep several of them resident per CU so that their loads overlap.
 //
-//  * Plain: 4 waves x 32 query rows (BM = 128), span 192 keys.
+//  * Plain: 4 waves x 32 query rows (BM = 128); windowed span 192 keys.
 //  * Differential: waves w and w + 2 share 32 rows, one softmax branch each (BM = 64),
-//    span 128 keys; the second branch hands O2 / l2 to the first through LDS.
+//    windowed span 128 keys; the second branch hands O2 / l2 to the first through LDS.
 //  * Arithmetic per element is the long-span kernel's: RoPE in FP32 with separate
 //    roundings then RNE to the IO dtype, S^T = K Q^T on MFMA (FP32 accumulation),
 //    P = 2^(s * c - m) rounded to fp16, FP32 row sums of the rounded P, O^T = V^T P^T
@@ -26,15 +28,18 @@
 namespace sa3 {
 namespace {
 
-// Span of keys staged per workgroup and the LDS strides (16-bit elements). The V^T
-// stride keeps the 16-byte operand reads of 16 consecutive rows on distinct banks.
-template <bool DIFF>
+// Span of keys staged per workgroup and the LDS strides (16-bit elements). NKF = 0:
+// windowed mode, the span [q0 - w, q0 + BM - 1 + w] of a window of half-width w <= 32
+// (BM + 64 keys). NKF > 0: short-sequence mode, the whole sequence [0, L) with L <= NKF
+// and any window. The V^T stride keeps the 16-byte operand reads of 16 consecutive
+// rows on distinct banks.
+template <bool DIFF, int NKF>
 struct NarrowShape {
     static constexpr int NT = 256;                    // threads (4 waves)
     static constexpr int NBS = DIFF ? 2 : 1;          // branches staged
     static constexpr int WPB = DIFF ? 2 : 4;          // query blocks (waves) per branch
     static constexpr int BM = WPB * 32;               // query rows per workgroup
-    static constexpr int NK = BM + 64;                // keys staged (covers BM + 2w, w <= 32)
+    static constexpr int NK = NKF ? NKF : BM + 64;    // keys staged
     static constexpr int NKB = NK / 32;               // 32-key blocks
     static constexpr int KS = 72;                     // K row stride
     static constexpr int VS = NK + 8;                 // V^T row stride
@@ -43,9 +48,11 @@ struct NarrowShape {
     static constexpr int LDS_ELEMS = NBS * K_ELEMS + V_ELEMS;
 };
 
-template <int IO, bool DIFF>
-__global__ __launch_bounds__(256, 2) void attn_narrow_kernel(Params P) {
-    using S = NarrowShape<DIFF>;
+// Windowed mode keeps registers <= 168 so that three workgroups share a CU (their LDS
+// fits too); short-sequence mode may use up to 256.
+template <int IO, bool DIFF, int NKF>
+__global__ __launch_bounds__(256, NKF ? 2 : 3) void attn_narrow_kernel(Params P) {
+    using S = NarrowShape<DIFF, NKF>;
     constexpr int NT = S::NT, NBS = S::NBS, WPB = S::WPB, BM = S::BM, NK = S::NK, NKB = S::NKB;
     constexpr int KC = NK * 8 / NT;          // K chunks (8 elements) per thread per branch
     constexpr int VC = NK * 4 / NT;          // V items (2 keys x 8 d) per thread
@@ -85,7 +92,7 @@ __global__ __launch_bounds__(256, 2) void attn_narrow_kernel(Params P) {
 
     const int q0 = qt * BM;
     const int qw = q0 + wq * 32;
-    const int ks0 = q0 - w;                  // first staged key (may be negative)
+    const int ks0 = NKF ? 0 : q0 - w;        // first staged key (may be negative)
 
     // ---- issue every load: Q rows of this wave, then the K / cos / sin / V span ------
     u32x4 rq_raw[4], rqc[4], rqs[4];
@@ -193,7 +200,8 @@ __global__ __launch_bounds__(256, 2) void attn_narrow_kernel(Params P) {
     mx = pair_max(mx);
     const float nb = (mx == NEG_INF) ? 0.0f : -(mx * c);
 
-    u32x4 pk[NKB][2];
+    // P of each 32-key block, its FP32 row sums, and O^T += V^T P^T right away
+    f32x16 o[2] = {f32x16{}, f32x16{}};
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -205,30 +213,22 @@ __global__ __launch_bounds__(256, 2) void attn_narrow_kernel(Params P) {
         }
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            u32x4 wv;
+            u32x4 pk;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const f16x2 h = {(_Float16)e[8 * tt + 2 * j], (_Float16)e[8 * tt + 2 * j + 1]};
-                wv[j] = __builtin_bit_cast(uint32_t, h);
+                pk[j] = __builtin_bit_cast(uint32_t, h);
                 acc[(kb & 1) * 2 + tt] = __builtin_amdgcn_fdot2(h, f16x2{(_Float16)1.0f, (_Float16)1.0f},
                                                                 acc[(kb & 1) * 2 + tt], false);
             }
-            pk[kb][tt] = wv;
-        }
-    }
-    const float l = pair_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
-
-    // ---- O^T = V^T P^T over the span ----------------------------------------------
-    f32x16 o[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int db = 0; db < 2; ++db) {
                 const u32x4 va = lds16(Vt + (db * 32 + r) * S::VS + kb * 32 + 16 * tt + 8 * g);
-                o[db] = mfma_pv(va, pk[kb][tt], o[db]);
+                o[db] = mfma_pv(va, pk, o[db]);
             }
+        }
+    }
+    const float l = pair_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
 
     // ---- epilogue: normalise, subtract, cast, store rows < L -------------------------
     const float inv = 1.0f / l;
@@ -270,9 +270,9 @@ __global__ __launch_bounds__(256, 2) void attn_narrow_kernel(Params P) {
         }
 }
 
-template <int IO, bool DIFF>
+template <int IO, bool DIFF, int NKF>
 hipError_t launch_n(const LaunchArgs &a) {
-    using S = NarrowShape<DIFF>;
+    using S = NarrowShape<DIFF, NKF>;
     Params P;
     P.q = static_cast<const uint16_t *>(a.q);
     P.k = static_cast<const uint16_t *>(a.k);
@@ -282,30 +282,42 @@ hipError_t launch_n(const LaunchArgs &a) {
     P.out = a.out;
     P.branch_stride = (long long)a.B * a.H * a.L * HD;
     P.L = a.L;
-    P.window = a.window;
+    // short-sequence mode: every key of [0, L) is staged, so a window only masks
+    P.window = (NKF && a.window < 0) ? a.L : a.window;
     P.n_qtiles = (a.L + S::BM - 1) / S::BM;
     P.out_dtype = a.out_dtype;
     P.neg_scale = a.neg_scale;
     P.lam = a.lam;
     P.c = a.scale_log2;
     const unsigned grid = (unsigned)P.n_qtiles * (unsigned)a.B * (unsigned)a.H;
-    hipLaunchKernelGGL((attn_narrow_kernel<IO, DIFF>), dim3(grid), dim3(S::NT), 0,
+    hipLaunchKernelGGL((attn_narrow_kernel<IO, DIFF, NKF>), dim3(grid), dim3(S::NT), 0,
                        static_cast<hipStream_t>(a.stream), P);
     return hipGetLastError();
 }
 
+template <int NKF>
+hipError_t launch_nk(const LaunchArgs &a) {
+    const bool bf = a.dtype == 1;
+    if (a.diff) return bf ? launch_n<IO_BF16, true, NKF>(a) : launch_n<IO_F16, true, NKF>(a);
+    return bf ? launch_n<IO_BF16, false, NKF>(a) : launch_n<IO_F16, false, NKF>(a);
+}
+
+// Short-sequence mode for L <= 256 (span of 64, 128 or 256 keys), else windowed mode.
+int span_keys(const LaunchArgs &a) { return a.L <= 64 ? 64 : a.L <= 128 ? 128 : a.L <= 256 ? 256 : 0; }
+
 }  // namespace
 
-int narrow_tile_rows(const LaunchArgs &a) { return a.diff ? NarrowShape<true>::BM : NarrowShape<false>::BM; }
+bool narrow_applies(const LaunchArgs &a) { return span_keys(a) > 0 || (a.window >= 0 && a.window <= 32); }
+
+int narrow_tile_rows(const LaunchArgs &a) { return a.diff ? NarrowShape<true, 0>::BM : NarrowShape<false, 0>::BM; }
 
 int launch_narrow(const LaunchArgs &a) {
-    const bool bf = a.dtype == 1;
-    hipError_t e;
-    if (a.diff)
-        e = bf ? launch_n<IO_BF16, true>(a) : launch_n<IO_F16, true>(a);
-    else
-        e = bf ? launch_n<IO_BF16, false>(a) : launch_n<IO_F16, false>(a);
-    return (int)e;
+    switch (span_keys(a)) {
+        case 64: return (int)launch_nk<64>(a);
+        case 128: return (int)launch_nk<128>(a);
+        case 256: return (int)launch_nk<256>(a);
+        default: return (int)launch_nk<0>(a);
+    }
 }
 
 }  // namespace sa3

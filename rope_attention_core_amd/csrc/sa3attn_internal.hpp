@@ -32,7 +32,9 @@ int launch_forward(const LaunchArgs &a);
 // host can check the grid size before launching.
 int tile_rows(const LaunchArgs &a);
 
-// The narrow-window kernel (half-width <= 32): launcher and rows per workgroup.
+// The single-span kernel (sequences of <= 256 keys, or windows of half-width <= 32):
+// whether it takes this call, its launcher and its query rows per workgroup.
+bool narrow_applies(const LaunchArgs &a);
 int launch_narrow(const LaunchArgs &a);
 int narrow_tile_rows(const LaunchArgs &a);
 

@@ -119,7 +119,24 @@ def test_tail_lengths_bf16_windowed_diff(L):
     G.assert_parity(G.run_gpu(cfg, inp), G.run_oracle(cfg, inp), what=f"swa tail L{L}")
 
 
-@pytest.mark.parametrize("w", [0, 1, 15, 16, 17, 63, 64, 65, 255, 256, 257, 698, 699, 700, 5000, -1])
+@pytest.mark.parametrize("L", [1, 31, 64, 65, 100, 128, 129, 200, 256])
+@pytest.mark.parametrize("w", [-1, 40])
+def test_short_sequences_differential(L, w):
+    """Short sequences (the single-span kernel) in the two-branch form, full and windowed."""
+    cfg = synth.config("samel_swa", H=3, L=L, window=w, seed=7000 + L)
+    inp = synth.make_inputs(cfg)
+    G.assert_parity(G.run_gpu(cfg, inp), G.run_oracle(cfg, inp), what=f"short diff L{L} w{w}")
+
+
+@pytest.mark.parametrize("L", [40, 129, 200, 256])
+@pytest.mark.parametrize("w", [0, 5, 33, 100])
+def test_short_sequences_windowed(L, w):
+    cfg = synth.config("dit_short", H=2, L=L, window=w, seed=7500 + L + w)
+    inp = synth.make_inputs(cfg)
+    G.assert_parity(G.run_gpu(cfg, inp), G.run_oracle(cfg, inp), what=f"short w{w} L{L}", out=cfg.out_dtype)
+
+
+@pytest.mark.parametrize("w", [0, 1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 255, 256, 257, 698, 699, 700, 5000, -1])
 @pytest.mark.parametrize("io", ["f16", "bf16"])
 def test_window_sweep(w, io):
     cfg = synth.config("dit_2min", H=2, L=700, window=w, io=io, seed=3000 + max(w, 0),
