@@ -2,6 +2,7 @@
 """Benchmark of the fused RoPE attention core on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-configs]
+    python bench.py --only CONFIG      # one configuration, one short line (for profiling)
 
 One step = one call of the whole fused core (RoPE on Q/K, QK^T, FP32 online softmax,
 P.V) over one batch of synthetic input already resident in HBM. The headline workload
@@ -220,6 +221,20 @@ def cpu_baseline(cfg, inputs, budget_s=12.0):
     }
 
 
+def copy_reference(torch, mb):
+    """Three plain device copies of mb MiB: a known-size reference for the HBM counters."""
+    if mb <= 0:
+        return
+    n = mb * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_reference_bytes_read": n * 4, "copy_reference_bytes_written": n * 4,
+                      "copies": 3}), file=sys.stderr, flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -227,6 +242,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-config lines")
+    ap.add_argument("--only", metavar="CONFIG", default=None,
+                    help="time just this synthetic configuration and print one short JSON line "
+                         "(for profiling the kernel another configuration runs)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="after the benchmark, run 3 plain device copies of this many MiB "
                          "(a known-size reference for the HBM byte counters)")
@@ -249,6 +267,17 @@ def main():
         sys.exit(1)
     sa3.load_library()
     torch.cuda.set_device(0)
+
+    if args.only:
+        c = synth.config(args.only)
+        r = Bench(torch, sa3, synth, c).run(args.steps, args.warmup)
+        f = flops(c)
+        print(json.dumps({"config": args.only, "ms_per_call": round(r["ms_mean"], 5),
+                          "tflops": round(f / (r["ms_mean"] * 1e-3) / 1e12, 2),
+                          "gbs_compulsory": round(compulsory_bytes(c) / (r["ms_mean"] * 1e-3) / 1e9, 1)}),
+              flush=True)
+        copy_reference(torch, args.copy_mb)
+        return
 
     cfg = synth.config(HEAD_CONFIG)
     bench = Bench(torch, sa3, synth, cfg)
@@ -320,16 +349,7 @@ def main():
     }
     print(json.dumps(line), flush=True)
 
-    if args.copy_mb > 0:
-        n = args.copy_mb * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_reference_bytes_read": n * 4, "copy_reference_bytes_written": n * 4,
-                          "copies": 3}), file=sys.stderr, flush=True)
-
+    copy_reference(torch, args.copy_mb)
 
 if __name__ == "__main__":
     main()
