@@ -33,7 +33,7 @@ constexpr int OUT_F32 = 2;
 constexpr int HD = 64;            // head dim
 constexpr int ROWB = HD * 2;      // bytes per q/k/v row, and per cos/sin row (32 floats)
 constexpr int BN = 64;            // keys per tile
-constexpr int NBUF = 4;           // LDS stages
+constexpr int NBUF = 3;           // LDS stages of the long-span kernel
 constexpr int KS_STRIDE = 72;     // LDS row stride of the K tile in 16-bit elements
 constexpr int VT_STRIDE = 72;     // LDS row stride of the V^T tile in 16-bit elements
 constexpr uint32_t RSRC_WORD3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9)
@@ -177,17 +177,59 @@ __device__ __forceinline__ void softmax_p(const f32x16 (&s)[2], float c, float n
     rowsum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
-// Maximum of 32 values as a tree of 3-input maxima (depth 4) rather than a chain.
-__device__ __forceinline__ float max32(const float (&v)[32]) {
-    float a[11];
+// softmax of one 32-query block over one 32-key half (kb) of a 64-key tile against the
+// exponent base -nb: P^T packed as fp16 MFMA B operands [tt], and the FP32 sum of the
+// rounded P (two chains).
+template <bool MASK>
+__device__ __forceinline__ void softmax_half(const f32x16 &s, int kb, float c, float nb, TileMask mk,
+                                             u32x4 (&p)[2], float &rowsum) {
+    const float NEG_INF = -__builtin_inff();
+    float e[16];
 #pragma unroll
-    for (int i = 0; i < 10; ++i) a[i] = fmaxf(fmaxf(v[3 * i], v[3 * i + 1]), v[3 * i + 2]);
-    a[10] = fmaxf(v[30], v[31]);
-    const float b0 = fmaxf(fmaxf(a[0], a[1]), a[2]);
-    const float b1 = fmaxf(fmaxf(a[3], a[4]), a[5]);
-    const float b2 = fmaxf(fmaxf(a[6], a[7]), a[8]);
-    const float b3 = fmaxf(a[9], a[10]);
-    return fmaxf(fmaxf(b0, b1), fmaxf(b2, b3));
+    for (int i = 0; i < 16; ++i) {
+        float t = __builtin_fmaf(s[i], c, nb);
+        if constexpr (MASK) {
+            const int o = kb * 32 + (i >> 2) * 8 + (i & 3);
+            t = ((uint32_t)(o - mk.lo) <= mk.span) ? t : NEG_INF;
+        }
+        e[i] = __builtin_amdgcn_exp2f(t);
+    }
+    float acc[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        u32x4 w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const f16x2 h = {(_Float16)e[8 * tt + 2 * j], (_Float16)e[8 * tt + 2 * j + 1]};
+            w[j] = __builtin_bit_cast(uint32_t, h);
+            acc[tt] = __builtin_amdgcn_fdot2(h, f16x2{(_Float16)1.0f, (_Float16)1.0f}, acc[tt], false);
+        }
+        p[tt] = w;
+    }
+    rowsum = acc[0] + acc[1];
+}
+
+// max(a, b, c) as one v_max3_f32. MFMA results and -inf are never signalling NaNs, so
+// the quieting that fmaxf implies (an extra v_max_f32 x, x, x per operand) is not needed;
+// a quiet NaN operand is ignored, as fmaxf does.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float d;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
+}
+
+// Maximum of 32 values as a tree of 3-input maxima (depth 3) rather than a chain.
+__device__ __forceinline__ float max32(const float (&v)[32]) {
+    float a[12];
+#pragma unroll
+    for (int i = 0; i < 10; ++i) a[i] = max3f(v[3 * i], v[3 * i + 1], v[3 * i + 2]);
+    a[10] = v[30];
+    a[11] = v[31];
+    const float b0 = max3f(a[0], a[1], a[2]);
+    const float b1 = max3f(a[3], a[4], a[5]);
+    const float b2 = max3f(a[6], a[7], a[8]);
+    const float b3 = max3f(a[9], a[10], a[11]);
+    return max3f(max3f(b0, b1, b2), b3, b3);
 }
 
 // exact maximum of c * s over the valid keys of this lane pair (log2 units)

@@ -24,22 +24,23 @@
 //    accumulator layout); A = V^T from a transposed V tile in LDS whose key positions
 //    carry the same permutation, so each lane's operand is one 16-byte LDS read (the
 //    8-byte reads run at half the LDS bandwidth). For bf16 inputs V is converted to
-//    fp16 as it is staged,
-//    so P (rounded to fp16, 11 significant bits) and V meet in fp16.
+//    fp16 as it is staged, so P (rounded to fp16, 11 significant bits) and V meet in
+//    fp16.
 //  * K is rotated (FP32, fixed operation order, no contraction) and rounded to the IO
 //    dtype while it is staged into LDS; Q once into registers.
-//  * Software pipeline over key tiles with four LDS buffers and one barrier per
-//    tile. In the body for tile t the softmax of tile t (VALU) is independent of the
-//    P.V product of tile t-1 and of the QK^T product of tile t+1 (MFMA) and of the
-//    staging of tile t+2 (VALU + LDS), so the scheduler can overlap them; the global
-//    loads of tile t+3 are in flight meanwhile.
+//  * Software pipeline over key tiles with three LDS buffers and one barrier per tile.
+//    The block for tile t first issues QK^T(t+1) into the second score set, so those
+//    MFMAs run under the softmax of tile t (VALU); P.V(t) follows each 32-key half of
+//    that softmax; then tile t+2 is rotated/transposed into LDS while the global loads
+//    of tile t+3 are in flight.
 //  * Online softmax in base 2 (scale * log2 e folded into one FMA) with a lazy
 //    rescale: each row keeps an exponent base m; a tile moves it only when the tile's
 //    maximum exceeds m by more than TAU (and on the row's first valid keys, where m is
 //    set to the exact maximum). So P = 2^(s*c - m) <= 2^TAU fits fp16; O and the
-//    running sum carry the factor 2^(m_old - m_new), which is exactly 1 except on
-//    those rare tiles. Any common base cancels in O / l, so the result is the same
-//    softmax.
+//    running sum are multiplied on every tile by 2^(m_old - m_new), which is exactly 1
+//    except on those rare tiles (a branch around the product made the register
+//    allocator copy the 32 accumulator registers every tile). Any common base cancels
+//    in O / l, so the result is the same softmax.
 //  * Out-of-range rows read as zeros through buffer loads (the hardware returns 0
 //    past num_records), so tails need no branches; scores of keys >= L and outside
 //    the window are set to -inf in the tiles that need a mask.
@@ -233,12 +234,6 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(Params P) {
     };
 
     // ---- prologue ----------------------------------------------------------------
-    // The first block multiplies a zero P by the V tile of stage t_begin - 1: clear it.
-    {
-        uint32_t *vz = reinterpret_cast<uint32_t *>(smem + ((t_begin + NBUF - 1) % NBUF) * BUF_ELEMS +
-                                                    NBS * KS_ELEMS);
-        for (int i = tid; i < VT_ELEMS / 2; i += NT) vz[i] = 0u;
-    }
     load_raw(t_begin);
     stage(t_begin % NBUF);
     load_raw(t_begin + 1);
@@ -246,78 +241,39 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(Params P) {
     load_raw(t_begin + 2);
     __syncthreads();
 
-    // Scores: one set, consumed by the softmax of tile t, then rewritten with tile t+1.
-    // P ping-pongs: the block of tile t writes pbuf[P] (and its row sums rsum[P]) and
-    // multiplies pbuf[P^1], the P of tile t-1. P is the parity of t - t_begin, known at
-    // compile time in the unrolled loop.
-    f32x16 sbuf[2];
-    u32x4 pbuf[2][2][2];
-    float rsum[2];
-    rsum[1] = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) pbuf[1][kb][tt] = u32x4{0, 0, 0, 0};
-    qk(t_begin % NBUF, sbuf);
-
-    // Bring O and l to the base of tile t-1 (whose P is pbuf[PP]) before its P.V
-    // product: O *= alpha, l = l * alpha + its row sum. alpha is exactly 1 unless the
-    // row's base moved, so the product is exact; it is done on every tile because a
-    // wave-uniform branch around it made the register allocator copy all 32 accumulator
-    // registers on every tile.
-    auto carry = [&](auto pp_tag) __attribute__((always_inline)) {
-        constexpr int PP = decltype(pp_tag)::value;
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) st.o[db][i] *= st.a;
-        st.l = __builtin_fmaf(st.l, st.a, rsum[PP]);
-        st.a = 1.0f;
-    };
-
-    // O^T += V^T P^T for the given V^T operands and P
-    auto pv_sum = [&](const u32x4 (&va)[2][2][2], const u32x4 (&p)[2][2]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                st.o[0] = mfma_pv(va[0][kb][tt], p[kb][tt], st.o[0]);
-                st.o[1] = mfma_pv(va[1][kb][tt], p[kb][tt], st.o[1]);
-            }
-    };
-    auto load_v_operands = [&](int buf, u32x4 (&va)[2][2][2]) __attribute__((always_inline)) {
-        const uint16_t *Vt = smem + buf * BUF_ELEMS + NBS * KS_ELEMS;
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt)
-                    va[db][kb][tt] = lds16(Vt + (db * 32 + r) * VT_STRIDE + kb * 32 + 16 * tt + 8 * g);
-    };
-
-    // One tile step: carry; softmax(t) alongside P.V(t-1) and QK^T(t+1); stage(t+2);
-    // the loads of tile t+3.
+    // Two score sets: the block of tile t starts QK^T(t+1) into sb[P^1] so its MFMAs run
+    // under the softmax of tile t (sb[P]); P.V(t) follows each 32-key half of the softmax.
+    f32x16 sb[2][2];
+    qk(t_begin % NBUF, sb[0]);
     auto block = [&](int t, auto mask_tag, auto par_tag) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_tag)::value;
         constexpr int PC = decltype(par_tag)::value;
         constexpr int PN = PC ^ 1;
-        carry(std::integral_constant<int, PN>{});
+        qk((t + 1) % NBUF, sb[PN]);
         const TileMask mk = MASK ? tile_mask(t) : TileMask{0, 0};
-        // MFMA operands read from LDS first so their latency overlaps the softmax
-        u32x4 va[2][2][2];
-        load_v_operands((t + NBUF - 1) % NBUF, va);
-        // softmax of tile t: the tile maximum decides whether the base moves (lazily:
-        // only past TAU), then P = 2^(s*c - m) in fp16
-        {
-            const float mt = tile_max<MASK>(sbuf, c, mk);
-            const float mn = (mt > st.m + TAU) ? mt : st.m;
-            st.a = (mn == st.m) ? 1.0f : ((st.m == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(st.m - mn));
-            st.m = mn;
-            softmax_p<MASK>(sbuf, c, (mn == NEG_INF) ? 0.0f : -mn, mk, pbuf[PC], rsum[PC]);
+        const float mt = tile_max<MASK>(sb[PC], c, mk);
+        const float mn = (mt > st.m + TAU) ? mt : st.m;
+        const float a = (mn == st.m) ? 1.0f : ((st.m == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(st.m - mn));
+        st.m = mn;
+        const float nb = (mn == NEG_INF) ? 0.0f : -mn;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) st.o[db][i] *= a;
+        const uint16_t *Vt = smem + (t % NBUF) * BUF_ELEMS + NBS * KS_ELEMS;
+        float part[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            u32x4 p[2];
+            softmax_half<MASK>(sb[PC][kb], kb, c, nb, mk, p, part[kb]);
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int db = 0; db < 2; ++db)
+                    st.o[db] = mfma_pv(lds16(Vt + (db * 32 + r) * VT_STRIDE + kb * 32 + 16 * tt + 8 * g), p[tt],
+                                       st.o[db]);
         }
-        pv_sum(va, pbuf[PN]);
-        qk((t + 1) % NBUF, sbuf);
+        st.l = __builtin_fmaf(st.l, a, part[0] + part[1]);
         stage((t + 2) % NBUF);
         load_raw(t + 3);
         __syncthreads();
@@ -337,18 +293,6 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(Params P) {
         step(t + 1, P1{});
     }
     if (t < t_end) step(t, P0{});
-    // the last tile's P sits in pbuf[parity of t_end - 1 - t_begin]
-    {
-        u32x4 va[2][2][2];
-        load_v_operands((t_end + NBUF - 1) % NBUF, va);
-        if ((t_end - t_begin) & 1) {
-            carry(P0{});
-            pv_sum(va, pbuf[0]);
-        } else {
-            carry(P1{});
-            pv_sum(va, pbuf[1]);
-        }
-    }
 
     // ---- epilogue: normalise, subtract, cast, store rows < L -------------------------
     const float inv = 1.0f / pair_sum(st.l);
