@@ -25,7 +25,9 @@
  * Conventions shared by every entry point
  *  - Layout: every tensor is row-major contiguous [B][H][L][D], D fastest.
  *    Differential q and k are stacked [2][B][H][L][D] (branch 1, then branch 2);
- *    v is [B][H][L][D] and shared by both branches.
+ *    v is [B][H][L][D] and shared by both branches. sa3attn_forward_strided takes
+ *    the same tensors with explicit strides instead (below).
+ *  - Every device pointer (q, k, v, cos, sin, out) is 16-byte aligned.
  *  - RoPE rotates adjacent pairs (x[2i], x[2i+1]) at position m = 0..L-1 of each
  *    (b, h) slab: r0 = fl(fl(x0 c) - fl(x1 s)), r1 = fl(fl(x0 s) + fl(x1 c)) in FP32,
  *    then rounds to nearest-even to the IO dtype.
@@ -60,7 +62,7 @@ extern "C" {
 #endif
 
 #define SA3ATTN_VERSION_MAJOR 0
-#define SA3ATTN_VERSION_MINOR 1
+#define SA3ATTN_VERSION_MINOR 2
 
 /* Status codes. */
 enum {
@@ -68,7 +70,8 @@ enum {
     SA3_ERR_NULL = -1,         /* a required pointer is NULL                          */
     SA3_ERR_SHAPE = -2,        /* B, H, L or D < 1, D odd, or a size overflows        */
     SA3_ERR_UNSUPPORTED = -3,  /* D != 64, or an unknown dtype                         */
-    SA3_ERR_ARG = -4,          /* non-finite scale or lambda, or out overlaps an input */
+    SA3_ERR_ARG = -4,          /* non-finite scale or lambda, out overlaps an input,
+                                  a misaligned pointer, or unusable strides           */
     SA3_ERR_DEVICE = -5,       /* no HIP device, or the current device is not gfx950  */
     SA3_ERR_LAUNCH = -6        /* the kernel launch failed (hipGetLastError)          */
 };
@@ -118,6 +121,32 @@ typedef struct sa3attn_desc {
 } sa3attn_desc;
 
 int sa3attn_forward_ex(const sa3attn_desc *desc);
+
+/*
+ * sa3attn_strides / sa3attn_forward_strided -- the explicit form over strided views.
+ * Element (b, h, l, d) of q is at q + q[0]*b + q[1]*h + q[2]*l + d (in elements of
+ * the tensor's own type; the head dim is contiguous), and likewise for k, v and out.
+ * Differential branch 2 of q (of k) starts q_branch (k_branch) elements after
+ * branch 1. The layout a fused QKV projection writes, [B][L][H][D], is
+ * {L*H*D, D, H*D}; sa3attn_forward_ex is this call with contiguous [B][H][L][D]
+ * strides {H*L*D, L*D, D} and branch strides B*H*L*D.
+ * Requirements (SA3_ERR_ARG otherwise, before anything is enqueued): every stride
+ * >= 0 and a multiple of 8 elements; the l stride >= 64; (L + 128) * l stride * 2
+ * < 2^32 for q, k, v and out; the output view gives every (b, h, l) its own row;
+ * out overlaps no input. Inputs may alias each other (they are only read).
+ * A NULL strides pointer returns SA3_ERR_NULL. The strides are copied; the
+ * caller keeps ownership of the struct.
+ */
+typedef struct sa3attn_strides {
+    long long q[3];
+    long long k[3];
+    long long v[3];
+    long long out[3];
+    long long q_branch;
+    long long k_branch;
+} sa3attn_strides;
+
+int sa3attn_forward_strided(const sa3attn_desc *desc, const sa3attn_strides *strides);
 
 /*
  * sa3attn_rope_table -- fill a host FP32 cos/sin table [L][D/2].

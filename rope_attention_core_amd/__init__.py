@@ -27,6 +27,7 @@ EXPORTS = (
     "sa3attn_forward",
     "sa3attn_forward_bf16",
     "sa3attn_forward_ex",
+    "sa3attn_forward_strided",
     "sa3attn_rope_table",
     "sa3attn_status_string",
     "sa3attn_version",
@@ -49,6 +50,13 @@ class _Desc(ctypes.Structure):
         ("window", ctypes.c_int), ("lambda_", ctypes.c_float), ("scale", ctypes.c_float),
         ("dtype", ctypes.c_int), ("out_dtype", ctypes.c_int), ("differential", ctypes.c_int),
         ("stream", ctypes.c_void_p),
+    ]
+
+
+class _Strides(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_longlong * 3), ("k", ctypes.c_longlong * 3), ("v", ctypes.c_longlong * 3),
+        ("out", ctypes.c_longlong * 3), ("q_branch", ctypes.c_longlong), ("k_branch", ctypes.c_longlong),
     ]
 
 
@@ -76,6 +84,8 @@ def load_library():
         fn.restype = i
     lib.sa3attn_forward_ex.argtypes = [ctypes.POINTER(_Desc)]
     lib.sa3attn_forward_ex.restype = i
+    lib.sa3attn_forward_strided.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_Strides)]
+    lib.sa3attn_forward_strided.restype = i
     lib.sa3attn_rope_table.argtypes = [vp, vp, i, i, ctypes.c_double]
     lib.sa3attn_rope_table.restype = i
     lib.sa3attn_status_string.argtypes = [i]
@@ -134,12 +144,16 @@ def rope_table(L, D=64, base=10000.0):
 
 def forward(q, k, v, cos, sin, *, window=-1, lam=0.0, scale=None, out=None, out_dtype=None,
             differential=None, stream=None):
-    """Run the fused core through sa3attn_forward_ex.
+    """Run the fused core through sa3attn_forward_ex, or sa3attn_forward_strided when a
+    tensor is a strided view.
 
     q, k: [B, H, L, D] (plain) or [2, B, H, L, D] (differential), fp16 or bf16, on the
-    GPU and contiguous; v: [B, H, L, D], same dtype; cos, sin: FP32 [>=L, D/2] on the
-    GPU. ``differential`` defaults to q.dim() == 5. ``out_dtype`` defaults to the IO
-    dtype; ``scale`` to 1/sqrt(D). Returns ``out`` (allocated if not given).
+    GPU; v: [B, H, L, D], same dtype; out: [B, H, L, D]. Any of them may be a view with
+    a contiguous last dimension (for instance ``x.view(B, L, H, D).transpose(1, 2)`` of
+    a [B, L, H*D] projection output); the strides go to the library as they are.
+    cos, sin: contiguous FP32 [>=L, D/2] on the GPU. ``differential`` defaults to
+    q.dim() == 5. ``out_dtype`` defaults to the IO dtype; ``scale`` to 1/sqrt(D).
+    Returns ``out`` (allocated contiguous if not given).
     """
     torch = _torch()
     if differential is None:
@@ -158,8 +172,12 @@ def forward(q, k, v, cos, sin, *, window=-1, lam=0.0, scale=None, out=None, out_
     for name, t in (("q", q), ("k", k), ("v", v), ("cos", cos), ("sin", sin), ("out", out)):
         if not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor")
+    for name, t in (("cos", cos), ("sin", sin)):
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if t.stride(-1) != 1:
+            raise ValueError(f"{name} must have a contiguous last dimension")
     if q.dtype != v.dtype or k.dtype != v.dtype:
         raise TypeError("q, k and v must share one dtype")
     if cos.dtype != torch.float32 or sin.dtype != torch.float32:
@@ -168,13 +186,28 @@ def forward(q, k, v, cos, sin, *, window=-1, lam=0.0, scale=None, out=None, out_
         raise ValueError(f"cos/sin must be [>= {L}, {D // 2}]")
     if out.dtype != out_dtype:
         raise TypeError("out dtype does not match out_dtype")
-    d = _Desc(_ptr(q), _ptr(k), _ptr(v), _ptr(cos), _ptr(sin), _ptr(out),
+    # for a differential q / k, the data pointer is branch 1; branch 2 is one stride on
+    qq, kk = (q[0], k[0]) if differential else (q, k)
+    d = _Desc(_ptr(qq), _ptr(kk), _ptr(v), _ptr(cos), _ptr(sin), _ptr(out),
               B, H, L, D, int(window), float(lam), float(scale),
               _dt_code(v.dtype), _dt_code(out.dtype), 1 if differential else 0,
               _stream_handle(stream, v.device))
-    rc = load_library().sa3attn_forward_ex(ctypes.byref(d))
+    lib = load_library()
+    if all(t.is_contiguous() for t in (q, k, v, out)):
+        rc = lib.sa3attn_forward_ex(ctypes.byref(d))
+        what = "sa3attn_forward_ex"
+    else:
+        st = _Strides()
+        st.q[:] = qq.stride()[:3]
+        st.k[:] = kk.stride()[:3]
+        st.v[:] = v.stride()[:3]
+        st.out[:] = out.stride()[:3]
+        st.q_branch = q.stride(0) if differential else 0
+        st.k_branch = k.stride(0) if differential else 0
+        rc = lib.sa3attn_forward_strided(ctypes.byref(d), ctypes.byref(st))
+        what = "sa3attn_forward_strided"
     if rc != 0:
-        raise SA3Error(rc, "sa3attn_forward_ex")
+        raise SA3Error(rc, what)
     return out
 
 

@@ -48,7 +48,52 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
-int forward_impl(const sa3attn_desc *d) {
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Bytes from the first to one past the last element a [B][H][L][64] view with element
+// strides s = {b, h, l} (d contiguous) can touch; non-negative strides.
+unsigned long long extent_bytes(const long long s[3], int B, int H, int L, int elem) {
+    const unsigned long long last = (unsigned long long)(B - 1) * (unsigned long long)s[0] +
+                                    (unsigned long long)(H - 1) * (unsigned long long)s[1] +
+                                    (unsigned long long)(L - 1) * (unsigned long long)s[2] + 64ull;
+    return last * (unsigned long long)elem;
+}
+
+// Strides the kernels can use: non-negative, multiples of 8 elements (16-byte chunks),
+// a position stride of at least one row, and 32-bit row offsets: the kernels read up
+// to 64 rows past either end of a slab and rely on those offsets (negative ones wrap
+// modulo 2^32) landing at or above the slab's buffer range, which then reads zeros.
+bool strides_ok(const long long s[3], int L) {
+    for (int i = 0; i < 3; ++i)
+        if (s[i] < 0 || (s[i] & 7) != 0 || s[i] > (1ll << 40)) return false;
+    if (s[2] < 64) return false;
+    return (unsigned long long)(L + 128) * (unsigned long long)s[2] * 2ull < (1ull << 32);
+}
+
+// The output view maps every (b, h, l) row to its own 64 elements: with the dimensions
+// of size > 1 sorted by stride, each stride is at least the span of the ones inside it.
+bool rows_distinct(const long long s[3], int B, int H, int L) {
+    long long st[3] = {s[0], s[1], s[2]};
+    long long n[3] = {B, H, L};
+    for (int i = 0; i < 3; ++i)
+        for (int j = i + 1; j < 3; ++j)
+            if (st[j] < st[i]) {
+                const long long a = st[i], b = n[i];
+                st[i] = st[j];
+                n[i] = n[j];
+                st[j] = a;
+                n[j] = b;
+            }
+    long long span = 64;
+    for (int i = 0; i < 3; ++i) {
+        if (n[i] == 1) continue;
+        if (st[i] < span) return false;
+        span = st[i] * n[i];
+    }
+    return true;
+}
+
+int forward_impl(const sa3attn_desc *d, const sa3attn_strides *sp) {
     if (!d) return SA3_ERR_NULL;
     if (!d->q || !d->k || !d->v || !d->cos || !d->sin || !d->out) return SA3_ERR_NULL;
     if (d->B < 1 || d->H < 1 || d->L < 1 || d->D < 1 || (d->D & 1)) return SA3_ERR_SHAPE;
@@ -60,15 +105,38 @@ int forward_impl(const sa3attn_desc *d) {
     if (d->differential != 0 && d->differential != 1) return SA3_ERR_ARG;
     if (!std::isfinite(d->scale) || !std::isfinite(d->lambda)) return SA3_ERR_ARG;
 
-    // sizes in elements / bytes, with overflow checks
     const unsigned long long bh = (unsigned long long)d->B * (unsigned long long)d->H;
     const unsigned long long elems = bh * (unsigned long long)d->L * 64ull;
     if (bh > (1ull << 31) || elems > (1ull << 56)) return SA3_ERR_SHAPE;
-    const size_t in_bytes = (size_t)elems * 2 * (d->differential ? 2 : 1);
-    const size_t v_bytes = (size_t)elems * 2;
-    const size_t out_bytes = (size_t)elems * (d->out_dtype == SA3_F32 ? 4 : 2);
+
+    // strides: given, or those of contiguous [B][H][L][64] (q, k stacked [2][...])
+    sa3attn_strides s;
+    if (sp) {
+        s = *sp;
+    } else {
+        const long long c[3] = {(long long)d->H * d->L * 64, (long long)d->L * 64, 64};
+        for (int i = 0; i < 3; ++i) s.q[i] = s.k[i] = s.v[i] = s.out[i] = c[i];
+        s.q_branch = s.k_branch = (long long)elems;
+    }
+    if (!strides_ok(s.q, d->L) || !strides_ok(s.k, d->L) || !strides_ok(s.v, d->L) || !strides_ok(s.out, d->L))
+        return SA3_ERR_ARG;
+    if (d->differential && (s.q_branch < 0 || (s.q_branch & 7) || s.k_branch < 0 || (s.k_branch & 7)))
+        return SA3_ERR_ARG;
+    if (!rows_distinct(s.out, d->B, d->H, d->L)) return SA3_ERR_ARG;
+    if (!aligned16(d->q) || !aligned16(d->k) || !aligned16(d->v) || !aligned16(d->out) || !aligned16(d->cos) ||
+        !aligned16(d->sin))
+        return SA3_ERR_ARG;
+
+    // out must not overlap any input (byte ranges the views can reach)
+    const int osz = d->out_dtype == SA3_F32 ? 4 : 2;
+    const size_t out_bytes = (size_t)extent_bytes(s.out, d->B, d->H, d->L, osz);
+    const size_t q_bytes = (size_t)(extent_bytes(s.q, d->B, d->H, d->L, 2) +
+                                    (d->differential ? (unsigned long long)s.q_branch * 2ull : 0ull));
+    const size_t k_bytes = (size_t)(extent_bytes(s.k, d->B, d->H, d->L, 2) +
+                                    (d->differential ? (unsigned long long)s.k_branch * 2ull : 0ull));
+    const size_t v_bytes = (size_t)extent_bytes(s.v, d->B, d->H, d->L, 2);
     const size_t tab_bytes = (size_t)d->L * 32 * sizeof(float);
-    if (overlaps(d->out, out_bytes, d->q, in_bytes) || overlaps(d->out, out_bytes, d->k, in_bytes) ||
+    if (overlaps(d->out, out_bytes, d->q, q_bytes) || overlaps(d->out, out_bytes, d->k, k_bytes) ||
         overlaps(d->out, out_bytes, d->v, v_bytes) || overlaps(d->out, out_bytes, d->cos, tab_bytes) ||
         overlaps(d->out, out_bytes, d->sin, tab_bytes))
         return SA3_ERR_ARG;
@@ -80,6 +148,22 @@ int forward_impl(const sa3attn_desc *d) {
     a.cos = d->cos;
     a.sin = d->sin;
     a.out = d->out;
+    for (int i = 0; i < 3; ++i) {
+        a.qs[i] = s.q[i];
+        a.ks[i] = s.k[i];
+        a.vs[i] = s.v[i];
+        a.os[i] = s.out[i];
+    }
+    a.q_br = s.q_branch;
+    a.k_br = s.k_branch;
+    {
+        const long long c[3] = {(long long)d->H * d->L * 64, (long long)d->L * 64, 64};
+        bool contig = true;
+        for (int i = 0; i < 3; ++i)
+            contig = contig && s.q[i] == c[i] && s.k[i] == c[i] && s.v[i] == c[i] && s.out[i] == c[i];
+        if (d->differential) contig = contig && s.q_branch == (long long)elems && s.k_branch == (long long)elems;
+        a.contig = contig ? 1 : 0;
+    }
     a.B = d->B;
     a.H = d->H;
     a.L = d->L;
@@ -108,7 +192,12 @@ int forward_impl(const sa3attn_desc *d) {
 
 extern "C" {
 
-int sa3attn_forward_ex(const sa3attn_desc *desc) { return forward_impl(desc); }
+int sa3attn_forward_ex(const sa3attn_desc *desc) { return forward_impl(desc, nullptr); }
+
+int sa3attn_forward_strided(const sa3attn_desc *desc, const sa3attn_strides *strides) {
+    if (!strides) return SA3_ERR_NULL;
+    return forward_impl(desc, strides);
+}
 
 static int forward_short(const void *q, const void *k, const void *v, const float *cos, const float *sin,
                          void *out, int B, int H, int L, int D, int window, float lambda, float scale,
@@ -131,7 +220,7 @@ static int forward_short(const void *q, const void *k, const void *v, const floa
     d.out_dtype = dtype;
     d.differential = lambda != 0.0f ? 1 : 0;
     d.stream = stream;
-    return forward_impl(&d);
+    return forward_impl(&d, nullptr);
 }
 
 int sa3attn_forward(const void *q, const void *k, const void *v, const float *cos, const float *sin, void *out,
@@ -151,7 +240,9 @@ const char *sa3attn_status_string(int status) {
         case SA3_ERR_NULL: return "SA3_ERR_NULL: a required pointer is NULL";
         case SA3_ERR_SHAPE: return "SA3_ERR_SHAPE: B, H, L or D out of range, D odd, or a size overflows";
         case SA3_ERR_UNSUPPORTED: return "SA3_ERR_UNSUPPORTED: head dim or dtype not supported";
-        case SA3_ERR_ARG: return "SA3_ERR_ARG: non-finite scale or lambda, or out overlaps an input";
+        case SA3_ERR_ARG:
+            return "SA3_ERR_ARG: non-finite scale or lambda, out overlaps an input, a misaligned pointer, "
+                   "or unusable strides";
         case SA3_ERR_DEVICE: return "SA3_ERR_DEVICE: no HIP device, or the current device is not gfx950";
         case SA3_ERR_LAUNCH: return "SA3_ERR_LAUNCH: kernel launch failed";
         default: return "unknown sa3attn status";

@@ -43,10 +43,46 @@ struct Params {
     const uint16_t *q, *k, *v;
     const float *cos, *sin;
     void *out;
-    long long branch_stride;      // elements from branch 1 to branch 2 of q / k
-    int L, window, n_qtiles, out_dtype, neg_scale;
+    long long q_br, k_br;         // elements from branch 1 to branch 2 of q / k
+    long long qb, qh, kb, kh, vb, vh, ob, oh, ol;   // element strides of b and h (and l for out)
+    uint32_t q_rowb, k_rowb, v_rowb;                // bytes from one position to the next
+    int H, L, window, n_qtiles, out_dtype, neg_scale;
     float lam, c;                 // c = |scale| * log2(e)
 };
+
+// Kernel parameters common to every instance (n_qtiles and window are set by the caller).
+inline Params make_params(const LaunchArgs &a) {
+    Params P;
+    P.q = static_cast<const uint16_t *>(a.q);
+    P.k = static_cast<const uint16_t *>(a.k);
+    P.v = static_cast<const uint16_t *>(a.v);
+    P.cos = a.cos;
+    P.sin = a.sin;
+    P.out = a.out;
+    P.q_br = a.q_br;
+    P.k_br = a.k_br;
+    P.qb = a.qs[0];
+    P.qh = a.qs[1];
+    P.kb = a.ks[0];
+    P.kh = a.ks[1];
+    P.vb = a.vs[0];
+    P.vh = a.vs[1];
+    P.ob = a.os[0];
+    P.oh = a.os[1];
+    P.ol = a.os[2];
+    P.q_rowb = (uint32_t)(a.qs[2] * 2);
+    P.k_rowb = (uint32_t)(a.ks[2] * 2);
+    P.v_rowb = (uint32_t)(a.vs[2] * 2);
+    P.H = a.H;
+    P.L = a.L;
+    P.window = a.window;
+    P.n_qtiles = 1;
+    P.out_dtype = a.out_dtype;
+    P.neg_scale = a.neg_scale;
+    P.lam = a.lam;
+    P.c = a.scale_log2;
+    return P;
+}
 
 // ---- element conversions -------------------------------------------------------
 
@@ -120,6 +156,13 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Buffer over the L positions of one (b, h) slab whose rows are rowb bytes apart: the
+// last row's 128 bytes end the range, so rows >= L (and negative rows, whose 32-bit
+// offsets wrap far above it) read as zeros.
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes);
+__device__ __forceinline__ rsrc_t slab_rsrc(const uint16_t *base, long long elems, uint32_t rowb, int L) {
+    return make_rsrc(base + elems, (uint32_t)(L - 1) * rowb + (uint32_t)ROWB);
+}
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, (int)RSRC_WORD3);
 }

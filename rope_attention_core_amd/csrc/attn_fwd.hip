@@ -65,7 +65,9 @@ struct Branch {
 // wave w the first softmax branch (Q1, K1) and wave w + 4 the second (Q2, K2); both
 // multiply the same staged V tile, BM = 128, and the second branch hands O2 / l2 to the
 // first through LDS at the end.
-template <int IO, bool DIFF>
+// CONTIG: q, k, v and out are contiguous [B][H][L][64] (q, k stacked [2][...]); the row
+// strides are then compile-time constants, which keeps scalar registers free.
+template <int IO, bool DIFF, bool CONTIG>
 __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(Params P) {
     constexpr int NW = 8;
     constexpr int NT = NW * 64;
@@ -100,13 +102,21 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(Params P) {
     const int bh = lid / P.n_qtiles;
     const int qt = lid - bh * P.n_qtiles;
 
-    const size_t head = (size_t)bh * (size_t)L * HD;
-    const uint32_t nrec = (uint32_t)L * ROWB;
+    const int bb = bh / P.H, hh = bh - bb * P.H;
+    const uint32_t qrb = CONTIG ? (uint32_t)ROWB : P.q_rowb;
+    const uint32_t krb = CONTIG ? (uint32_t)ROWB : P.k_rowb;
+    const uint32_t vrb = CONTIG ? (uint32_t)ROWB : P.v_rowb;
+    const long long slab = (long long)bh * L * HD;   // contiguous offset of this (b, h)
+    // contiguous stacked branches are B*H*L*64 elements apart (B*H = workgroups / tiles)
+    const long long qbr = CONTIG ? (long long)(nblk / P.n_qtiles) * L * HD : P.q_br;
+    const long long kbr = CONTIG ? qbr : P.k_br;
     rsrc_t rk[NBS];
 #pragma unroll
-    for (int br = 0; br < NBS; ++br) rk[br] = make_rsrc(P.k + br * P.branch_stride + head, nrec);
-    const rsrc_t rq = make_rsrc(P.q + wbr * P.branch_stride + head, nrec);
-    const rsrc_t rv = make_rsrc(P.v + head, nrec);
+    for (int br = 0; br < NBS; ++br)
+        rk[br] = slab_rsrc(P.k, br * kbr + (CONTIG ? slab : bb * P.kb + hh * P.kh), krb, L);
+    const rsrc_t rq = slab_rsrc(P.q, wbr * qbr + (CONTIG ? slab : bb * P.qb + hh * P.qh), qrb, L);
+    const rsrc_t rv = slab_rsrc(P.v, CONTIG ? slab : bb * P.vb + hh * P.vh, vrb, L);
+    const uint32_t nrec = (uint32_t)L * ROWB;   // cos/sin: [L][32] floats, 128 bytes per row
     const rsrc_t rc = make_rsrc(P.cos, nrec);
     const rsrc_t rs = make_rsrc(P.sin, nrec);
 
@@ -117,11 +127,12 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(Params P) {
     u32x4 qreg[4];
     const uint32_t qsign = P.neg_scale ? 0x80008000u : 0u;
     {
-        const uint32_t row = (uint32_t)(qw + r) * ROWB;
+        const uint32_t row = (uint32_t)(qw + r);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const uint32_t off = row + (uint32_t)(16 * ks + 8 * g) * 2;
-            qreg[ks] = rope8<IO>(bload(rq, off), bload(rc, off), bload(rs, off)) ^ qsign;
+            const uint32_t col = (uint32_t)(16 * ks + 8 * g) * 2;
+            const uint32_t offc = row * ROWB + col;
+            qreg[ks] = rope8<IO>(bload(rq, row * qrb + col), bload(rc, offc), bload(rs, offc)) ^ qsign;
         }
     }
 
@@ -143,16 +154,19 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(Params P) {
     u32x4 rawk[NBS], rawc, raws;
     u32x2 rawv[2];
 
+    // per-lane parts of the staging offsets (one multiply each, here); the per-tile part
+    // k0 * row bytes is wave-uniform and comes from the scalar unit
+    const uint32_t kl = (uint32_t)(tid >> 3) * krb + (uint32_t)(tid & 7) * 16;
+    const uint32_t cl = (uint32_t)(tid >> 3) * ROWB + (uint32_t)(tid & 7) * 16;
+    const uint32_t vl = (uint32_t)(2 * vp) * vrb + (uint32_t)vd0 * 2;
     auto load_raw = [&](int t) __attribute__((always_inline)) {
         const uint32_t k0 = (uint32_t)(t * BN);
-        const uint32_t off = (k0 + (uint32_t)(tid >> 3)) * ROWB + (uint32_t)(tid & 7) * 16;
 #pragma unroll
-        for (int br = 0; br < NBS; ++br) rawk[br] = bload(rk[br], off);
-        rawc = bload(rc, off);
-        raws = bload(rs, off);
-        const uint32_t offv = (k0 + 2u * vp) * ROWB + (uint32_t)vd0 * 2;
-        rawv[0] = bload8(rv, offv);
-        rawv[1] = bload8(rv, offv + ROWB);
+        for (int br = 0; br < NBS; ++br) rawk[br] = bload(rk[br], kl + k0 * krb);
+        rawc = bload(rc, cl + k0 * ROWB);
+        raws = bload(rs, cl + k0 * ROWB);
+        rawv[0] = bload8(rv, vl + k0 * vrb);
+        rawv[1] = bload8(rv, vl + k0 * vrb + vrb);
     };
 
     // V^T key positions: bits 2 and 3 of the key index swapped, so that the 8 keys one
@@ -314,7 +328,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(Params P) {
         if (wbr == 1) return;
     }
     if (qi >= L) return;
-    const size_t row = head + (size_t)qi * HD;
+    const long long row = CONTIG ? slab + (long long)qi * HD : bb * P.ob + hh * P.oh + (long long)qi * P.ol;
     const float *xb = reinterpret_cast<const float *>(smem);
 #pragma unroll
     for (int db = 0; db < 2; ++db)
@@ -339,25 +353,12 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(Params P) {
         }
 }
 
-template <int IO, bool DIFF>
+template <int IO, bool DIFF, bool CONTIG>
 hipError_t launch(const LaunchArgs &a, int n_qtiles) {
-    Params P;
-    P.q = static_cast<const uint16_t *>(a.q);
-    P.k = static_cast<const uint16_t *>(a.k);
-    P.v = static_cast<const uint16_t *>(a.v);
-    P.cos = a.cos;
-    P.sin = a.sin;
-    P.out = a.out;
-    P.branch_stride = (long long)a.B * a.H * a.L * HD;
-    P.L = a.L;
-    P.window = a.window;
+    Params P = make_params(a);
     P.n_qtiles = n_qtiles;
-    P.out_dtype = a.out_dtype;
-    P.neg_scale = a.neg_scale;
-    P.lam = a.lam;
-    P.c = a.scale_log2;
     const unsigned grid = (unsigned)n_qtiles * (unsigned)a.B * (unsigned)a.H;
-    hipLaunchKernelGGL((attn_fwd_kernel<IO, DIFF>), dim3(grid), dim3(512), 0, static_cast<hipStream_t>(a.stream), P);
+    hipLaunchKernelGGL((attn_fwd_kernel<IO, DIFF, CONTIG>), dim3(grid), dim3(512), 0, static_cast<hipStream_t>(a.stream), P);
     return hipGetLastError();
 }
 
@@ -379,10 +380,17 @@ int launch_forward(const LaunchArgs &a) {
     const int n_qtiles = (a.L + bm - 1) / bm;
     const bool bf = a.dtype == 1;
     hipError_t e;
-    if (a.diff)
-        e = bf ? launch<IO_BF16, true>(a, n_qtiles) : launch<IO_F16, true>(a, n_qtiles);
-    else
-        e = bf ? launch<IO_BF16, false>(a, n_qtiles) : launch<IO_F16, false>(a, n_qtiles);
+    if (a.contig) {
+        if (a.diff)
+            e = bf ? launch<IO_BF16, true, true>(a, n_qtiles) : launch<IO_F16, true, true>(a, n_qtiles);
+        else
+            e = bf ? launch<IO_BF16, false, true>(a, n_qtiles) : launch<IO_F16, false, true>(a, n_qtiles);
+    } else {
+        if (a.diff)
+            e = bf ? launch<IO_BF16, true, false>(a, n_qtiles) : launch<IO_F16, true, false>(a, n_qtiles);
+        else
+            e = bf ? launch<IO_BF16, false, false>(a, n_qtiles) : launch<IO_F16, false, false>(a, n_qtiles);
+    }
     return (int)e;
 }
 

@@ -50,7 +50,9 @@ struct NarrowShape {
 
 // Windowed mode keeps registers <= 168 so that three workgroups share a CU (their LDS
 // fits too); short-sequence mode may use up to 256.
-template <int IO, bool DIFF, int NKF>
+// CONTIG: contiguous [B][H][L][64] tensors (q, k stacked [2][...]); the row strides
+// are then compile-time constants.
+template <int IO, bool DIFF, int NKF, bool CONTIG>
 __global__ __launch_bounds__(256, NKF ? 2 : 3) void attn_narrow_kernel(Params P) {
     using S = NarrowShape<DIFF, NKF>;
     constexpr int NT = S::NT, NBS = S::NBS, WPB = S::WPB, BM = S::BM, NK = S::NK, NKB = S::NKB;
@@ -80,13 +82,20 @@ __global__ __launch_bounds__(256, NKF ? 2 : 3) void attn_narrow_kernel(Params P)
     const int bh = lid / P.n_qtiles;
     const int qt = lid - bh * P.n_qtiles;
 
-    const size_t head = (size_t)bh * (size_t)L * HD;
-    const uint32_t nrec = (uint32_t)L * ROWB;
+    const int bb = bh / P.H, hh = bh - bb * P.H;
+    const uint32_t qrb = CONTIG ? (uint32_t)ROWB : P.q_rowb;
+    const uint32_t krb = CONTIG ? (uint32_t)ROWB : P.k_rowb;
+    const uint32_t vrb = CONTIG ? (uint32_t)ROWB : P.v_rowb;
+    const long long slab = (long long)bh * L * HD;   // contiguous offset of this (b, h)
+    const long long qbr = CONTIG ? (long long)(nblk / P.n_qtiles) * L * HD : P.q_br;
+    const long long kbr = CONTIG ? qbr : P.k_br;
     rsrc_t rk[NBS];
 #pragma unroll
-    for (int br = 0; br < NBS; ++br) rk[br] = make_rsrc(P.k + br * P.branch_stride + head, nrec);
-    const rsrc_t rq = make_rsrc(P.q + wbr * P.branch_stride + head, nrec);
-    const rsrc_t rv = make_rsrc(P.v + head, nrec);
+    for (int br = 0; br < NBS; ++br)
+        rk[br] = slab_rsrc(P.k, br * kbr + (CONTIG ? slab : bb * P.kb + hh * P.kh), krb, L);
+    const rsrc_t rq = slab_rsrc(P.q, wbr * qbr + (CONTIG ? slab : bb * P.qb + hh * P.qh), qrb, L);
+    const rsrc_t rv = slab_rsrc(P.v, CONTIG ? slab : bb * P.vb + hh * P.vh, vrb, L);
+    const uint32_t nrec = (uint32_t)L * ROWB;   // cos/sin: [L][32] floats, 128 bytes per row
     const rsrc_t rc = make_rsrc(P.cos, nrec);
     const rsrc_t rs = make_rsrc(P.sin, nrec);
 
@@ -97,24 +106,27 @@ __global__ __launch_bounds__(256, NKF ? 2 : 3) void attn_narrow_kernel(Params P)
     // ---- issue every load: Q rows of this wave, then the K / cos / sin / V span ------
     u32x4 rq_raw[4], rqc[4], rqs[4];
     {
-        const uint32_t row = (uint32_t)(qw + r) * ROWB;
+        const uint32_t row = (uint32_t)(qw + r);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const uint32_t off = row + (uint32_t)(16 * ks + 8 * g) * 2;
-            rq_raw[ks] = bload(rq, off);
-            rqc[ks] = bload(rc, off);
-            rqs[ks] = bload(rs, off);
+            const uint32_t col = (uint32_t)(16 * ks + 8 * g) * 2;
+            rq_raw[ks] = bload(rq, row * qrb + col);
+            rqc[ks] = bload(rc, row * ROWB + col);
+            rqs[ks] = bload(rs, row * ROWB + col);
         }
     }
+    // K item i: span row (tid >> 3) + i * NT / 8, chunk tid & 7. The per-lane part of
+    // the offset is one multiply here; the per-item part is wave-uniform (scalar unit).
     u32x4 rawk[NBS][KC], rawc[KC], raws[KC];
+    const uint32_t kl = (uint32_t)(tid >> 3) * krb + (uint32_t)(tid & 7) * 16;
+    const uint32_t cl = (uint32_t)(tid >> 3) * ROWB + (uint32_t)(tid & 7) * 16;
 #pragma unroll
     for (int i = 0; i < KC; ++i) {
-        const int it = tid + NT * i;
-        const uint32_t off = (uint32_t)(ks0 + (it >> 3)) * ROWB + (uint32_t)(it & 7) * 16;
+        const uint32_t r0 = (uint32_t)(ks0 + i * (NT / 8));
 #pragma unroll
-        for (int br = 0; br < NBS; ++br) rawk[br][i] = bload(rk[br], off);
-        rawc[i] = bload(rc, off);
-        raws[i] = bload(rs, off);
+        for (int br = 0; br < NBS; ++br) rawk[br][i] = bload(rk[br], kl + r0 * krb);
+        rawc[i] = bload(rc, cl + r0 * ROWB);
+        raws[i] = bload(rs, cl + r0 * ROWB);
     }
     // V item: keys 2p, 2p + 1 of the span and 8 values of d from 8 * ch
     u32x4 rawv[VC][2];
@@ -122,9 +134,9 @@ __global__ __launch_bounds__(256, NKF ? 2 : 3) void attn_narrow_kernel(Params P)
     for (int i = 0; i < VC; ++i) {
         const int it = tid + NT * i;
         const int p = it % (NK / 2), ch = it / (NK / 2);
-        const uint32_t off = (uint32_t)(ks0 + 2 * p) * ROWB + (uint32_t)ch * 16;
+        const uint32_t off = (uint32_t)(ks0 + 2 * p) * vrb + (uint32_t)ch * 16;
         rawv[i][0] = bload(rv, off);
-        rawv[i][1] = bload(rv, off + ROWB);
+        rawv[i][1] = bload(rv, off + vrb);
     }
 
     // ---- rotate Q into registers; rotate / transpose the span into LDS ---------------
@@ -245,7 +257,7 @@ __global__ __launch_bounds__(256, NKF ? 2 : 3) void attn_narrow_kernel(Params P)
         if (wbr == 1) return;
     }
     if (qi >= L) return;
-    const size_t row = head + (size_t)qi * HD;
+    const long long row = CONTIG ? slab + (long long)qi * HD : bb * P.ob + hh * P.oh + (long long)qi * P.ol;
     const float *xb = reinterpret_cast<const float *>(smem);
 #pragma unroll
     for (int db = 0; db < 2; ++db)
@@ -270,36 +282,28 @@ __global__ __launch_bounds__(256, NKF ? 2 : 3) void attn_narrow_kernel(Params P)
         }
 }
 
-template <int IO, bool DIFF, int NKF>
+template <int IO, bool DIFF, int NKF, bool CONTIG>
 hipError_t launch_n(const LaunchArgs &a) {
     using S = NarrowShape<DIFF, NKF>;
-    Params P;
-    P.q = static_cast<const uint16_t *>(a.q);
-    P.k = static_cast<const uint16_t *>(a.k);
-    P.v = static_cast<const uint16_t *>(a.v);
-    P.cos = a.cos;
-    P.sin = a.sin;
-    P.out = a.out;
-    P.branch_stride = (long long)a.B * a.H * a.L * HD;
-    P.L = a.L;
+    Params P = make_params(a);
     // short-sequence mode: every key of [0, L) is staged, so a window only masks
     P.window = (NKF && a.window < 0) ? a.L : a.window;
     P.n_qtiles = (a.L + S::BM - 1) / S::BM;
-    P.out_dtype = a.out_dtype;
-    P.neg_scale = a.neg_scale;
-    P.lam = a.lam;
-    P.c = a.scale_log2;
     const unsigned grid = (unsigned)P.n_qtiles * (unsigned)a.B * (unsigned)a.H;
-    hipLaunchKernelGGL((attn_narrow_kernel<IO, DIFF, NKF>), dim3(grid), dim3(S::NT), 0,
+    hipLaunchKernelGGL((attn_narrow_kernel<IO, DIFF, NKF, CONTIG>), dim3(grid), dim3(S::NT), 0,
                        static_cast<hipStream_t>(a.stream), P);
     return hipGetLastError();
 }
 
+template <int NKF, bool CONTIG>
+hipError_t launch_nkc(const LaunchArgs &a) {
+    const bool bf = a.dtype == 1;
+    if (a.diff) return bf ? launch_n<IO_BF16, true, NKF, CONTIG>(a) : launch_n<IO_F16, true, NKF, CONTIG>(a);
+    return bf ? launch_n<IO_BF16, false, NKF, CONTIG>(a) : launch_n<IO_F16, false, NKF, CONTIG>(a);
+}
 template <int NKF>
 hipError_t launch_nk(const LaunchArgs &a) {
-    const bool bf = a.dtype == 1;
-    if (a.diff) return bf ? launch_n<IO_BF16, true, NKF>(a) : launch_n<IO_F16, true, NKF>(a);
-    return bf ? launch_n<IO_BF16, false, NKF>(a) : launch_n<IO_F16, false, NKF>(a);
+    return a.contig ? launch_nkc<NKF, true>(a) : launch_nkc<NKF, false>(a);
 }
 
 // Short-sequence mode for L <= 256 (span of 64, 128 or 256 keys), else windowed mode.

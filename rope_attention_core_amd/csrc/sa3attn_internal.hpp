@@ -8,12 +8,14 @@ namespace sa3 {
 
 // Fully validated launch description. Pointers are device pointers.
 struct LaunchArgs {
-    const void *q;          // [B][H][L][64] (stacked [2][...] when diff)
-    const void *k;          // same layout as q
-    const void *v;          // [B][H][L][64]
+    const void *q;          // element (b, h, l, d) at b*qs[0] + h*qs[1] + l*qs[2] + d (+ q_br: branch 2)
+    const void *k;          // likewise with ks and k_br
+    const void *v;          // likewise with vs
     const float *cos;       // [>=L][32]
     const float *sin;       // [>=L][32]
-    void *out;              // [B][H][L][64]
+    void *out;              // likewise with os
+    long long qs[3], ks[3], vs[3], os[3];   // element strides of b, h, l (d is contiguous)
+    long long q_br, k_br;   // elements from branch 1 to branch 2 (differential)
     int B, H, L;
     int window;             // half-width; -1 = full (normalised: window < L - 1)
     float lam;              // differential weight
@@ -22,6 +24,7 @@ struct LaunchArgs {
     int dtype;              // SA3_F16 / SA3_BF16
     int out_dtype;          // SA3_F16 / SA3_BF16 / SA3_F32
     int diff;               // two branches
+    int contig;             // strides are those of contiguous [B][H][L][64] (and stacked [2][...])
     void *stream;           // hipStream_t
 };
 

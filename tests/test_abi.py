@@ -46,7 +46,7 @@ def test_status_strings_and_version(lib):
         s = sa3.status_string(code)
         assert s.startswith("SA3_ERR_"), s
     assert "unknown" in sa3.status_string(12345)
-    assert sa3.version() == (0, 1)
+    assert sa3.version() == (0, 2)
 
 
 @pytest.mark.parametrize("L,D", [(1, 2), (37, 8), (8192, 16), (8192, 64), (8192, 128)])
@@ -164,3 +164,73 @@ def test_short_forms_validate_like_ex(lib):
     assert f(None, _fake(2), _fake(3), _fake(4), _fake(5), _fake(6), 1, 2, 64, 64, -1, 0.0, 0.125, None) == SA3_ERR_NULL
     assert f(_fake(1), _fake(2), _fake(3), _fake(4), _fake(5), _fake(6), 1, 2, 64, 32, -1, 0.0, 0.125, None) == SA3_ERR_UNSUPPORTED
     assert f(_fake(1), _fake(2), _fake(3), _fake(4), _fake(5), _fake(6), 1, 2, 64, 64, -1, float("inf"), 0.125, None) == SA3_ERR_ARG
+
+
+# ---- strided views (sa3attn_forward_strided) -----------------------------------------
+
+def _strides(B=1, H=2, L=64, layout="bhld", **kw):
+    """Element strides of a [B][H][L][64] view: "bhld" contiguous, "blhd" the
+    [B][L][H][64] buffer a fused projection writes."""
+    c = (H * L * 64, L * 64, 64) if layout == "bhld" else (L * H * 64, 64, H * 64)
+    st = sa3._Strides()
+    for f in ("q", "k", "v", "out"):
+        getattr(st, f)[:] = kw.get(f, c)
+    st.q_branch = kw.get("q_branch", B * H * L * 64)
+    st.k_branch = kw.get("k_branch", B * H * L * 64)
+    return st
+
+
+def _call_strided(lib, st, **kw):
+    return lib.sa3attn_forward_strided(ctypes.byref(_desc(**kw)), ctypes.byref(st))
+
+
+def test_strided_null_strides_rejected(lib):
+    assert lib.sa3attn_forward_strided(ctypes.byref(_desc()), None) == SA3_ERR_NULL
+    assert lib.sa3attn_forward_strided(None, ctypes.byref(_strides())) == SA3_ERR_NULL
+
+
+@pytest.mark.parametrize("field,val", [
+    ("q", (2 * 64 * 64, 64 * 64, 60)),        # position stride shorter than a row
+    ("k", (2 * 64 * 64, 64 * 64 + 4, 64)),    # not a multiple of 8 elements
+    ("v", (-64, 64 * 64, 64)),                # negative
+    ("out", (2 * 64 * 64, 64 * 64, 36)),
+    ("q", (0, 0, 1 << 26)),                   # 32-bit row offsets would overflow
+])
+def test_strided_bad_strides_rejected(lib, field, val):
+    assert _call_strided(lib, _strides(**{field: val})) == SA3_ERR_ARG
+
+
+def test_strided_output_rows_must_be_distinct(lib):
+    # H = 2 heads written to the same rows
+    assert _call_strided(lib, _strides(out=(64 * 64, 0, 64))) == SA3_ERR_ARG
+    # positions of one head interleaved with the other's: rows 64 apart, heads 64 apart
+    assert _call_strided(lib, _strides(out=(2 * 64 * 64, 64, 64))) == SA3_ERR_ARG
+
+
+def test_strided_out_overlapping_an_input_rejected(lib):
+    # [B][L][H][64] q of 2 heads x 64 positions spans 2*64*64 elements; out starts inside
+    base = _fake(9).value
+    st = _strides(layout="blhd")
+    assert _call_strided(lib, st, q=ctypes.c_void_p(base), out=ctypes.c_void_p(base + 64 * 64 * 2)) == SA3_ERR_ARG
+
+
+def test_misaligned_pointer_rejected(lib):
+    assert _call(lib, q=ctypes.c_void_p(_fake(1).value + 8)) == SA3_ERR_ARG
+    assert _call(lib, out=ctypes.c_void_p(_fake(6).value + 2)) == SA3_ERR_ARG
+    assert _call(lib, cos=ctypes.c_void_p(_fake(4).value + 4)) == SA3_ERR_ARG
+
+
+def test_strided_differential_branch_stride_checked(lib):
+    assert _call_strided(lib, _strides(q_branch=12), differential=1) == SA3_ERR_ARG
+    assert _call_strided(lib, _strides(k_branch=-64), differential=1) == SA3_ERR_ARG
+
+
+@pytest.mark.skipif(_gpu_present(), reason="placeholder pointers must never reach a real GPU")
+def test_valid_strided_call_without_gpu_reports_device_error(lib):
+    assert _call_strided(lib, _strides()) == SA3_ERR_DEVICE
+    assert _call_strided(lib, _strides(layout="blhd")) == SA3_ERR_DEVICE
+    assert _call_strided(lib, _strides(layout="blhd"), differential=1) == SA3_ERR_DEVICE
+    # inputs may alias one another (they are only read): q, k, v in one buffer
+    base = _fake(9).value
+    assert _call_strided(lib, _strides(layout="blhd"), q=ctypes.c_void_p(base), k=ctypes.c_void_p(base),
+                         v=ctypes.c_void_p(base)) == SA3_ERR_DEVICE
