@@ -95,42 +95,60 @@ def _core(qr, kr, v, scale, window, lam, q2r, k2r):
     return out
 
 
-def attn_def(q, k, v, scale, window=-1, lam=0.0, q2=None, k2=None, base=10000.0):
+def _rope_kw(pairing, rotary_dim):
+    # the default (adjacent, full width) is passed as no keywords at all
+    kw = {}
+    if pairing != "adjacent":
+        kw["pairing"] = pairing
+    if rotary_dim is not None:
+        kw["rotary_dim"] = rotary_dim
+    return kw
+
+
+def attn_def(q, k, v, scale, window=-1, lam=0.0, q2=None, k2=None, base=10000.0,
+             pairing="adjacent", rotary_dim=None):
     """def mode: RoPE in exact fp64 math (fp64 cos/sin), then fp64 attention.
 
     q, k, v, q2, k2: [B, H, L, D] fp64 values. Differential when q2/k2 are given.
+    pairing / rotary_dim: the RoPE options of oracle.rope (default adjacent, full).
     """
     v = np.asarray(v, dtype=np.float64)
     L, D = v.shape[-2], v.shape[-1]
-    phi = rope_angles(L, D, base)
+    R = D if rotary_dim is None else rotary_dim
+    phi = rope_angles(L, R, base)
     c, s = np.cos(phi), np.sin(phi)
-    qr, kr = rotate_def(q, c, s), rotate_def(k, c, s)
-    q2r = rotate_def(q2, c, s) if q2 is not None else None
-    k2r = rotate_def(k2, c, s) if k2 is not None else None
+    kw = _rope_kw(pairing, rotary_dim)
+    qr, kr = rotate_def(q, c, s, **kw), rotate_def(k, c, s, **kw)
+    q2r = rotate_def(q2, c, s, **kw) if q2 is not None else None
+    k2r = rotate_def(k2, c, s, **kw) if k2 is not None else None
     return _core(qr, kr, v, scale, window, lam, q2r, k2r)
 
 
-def attn_method(q, k, v, cos32, sin32, io, scale, window=-1, lam=0.0, q2=None, k2=None):
+def attn_method(q, k, v, cos32, sin32, io, scale, window=-1, lam=0.0, q2=None, k2=None,
+                pairing="adjacent", rotary_dim=None):
     """method mode: FP32 RoPE with the FP32 table, RNE cast to ``io``, fp64 after.
 
     q, k, v, q2, k2: [B, H, L, D] fp64 values exactly representable in ``io``.
-    cos32, sin32: the FP32 table [>=L, D/2]. Differential when q2/k2 are given.
+    cos32, sin32: the FP32 table [>=L, R/2] (R = rotary_dim, default D). Differential
+    when q2/k2 are given.
     """
     v = np.asarray(v, dtype=np.float64)
-    qr = rotate_method(q, cos32, sin32, io)
-    kr = rotate_method(k, cos32, sin32, io)
-    q2r = rotate_method(q2, cos32, sin32, io) if q2 is not None else None
-    k2r = rotate_method(k2, cos32, sin32, io) if k2 is not None else None
+    kw = _rope_kw(pairing, rotary_dim)
+    qr = rotate_method(q, cos32, sin32, io, **kw)
+    kr = rotate_method(k, cos32, sin32, io, **kw)
+    q2r = rotate_method(q2, cos32, sin32, io, **kw) if q2 is not None else None
+    k2r = rotate_method(k2, cos32, sin32, io, **kw) if k2 is not None else None
     return _core(qr, kr, v, scale, window, lam, q2r, k2r)
 
 
 def attn_method_rows(q, k, v, cos32, sin32, io, scale, b, h, rows,
-                     window=-1, lam=0.0, q2=None, k2=None):
+                     window=-1, lam=0.0, q2=None, k2=None, pairing="adjacent", rotary_dim=None):
     """method mode for selected query rows of one (b, h); returns [len(rows), D].
 
     Only the selected Q rows are rotated; all keys of the head are. Used to check
     sampled outputs of full-size runs one row at a time.
     """
+    kw = _rope_kw(pairing, rotary_dim)
     rows = np.asarray(rows, dtype=np.int64)
     L = v.shape[-2]
     c = np.asarray(cos32, dtype=np.float32)[:L]
@@ -138,23 +156,23 @@ def attn_method_rows(q, k, v, cos32, sin32, io, scale, b, h, rows,
 
     def rot_rows(x):
         # rotate only the requested rows: the table row follows the position
-        return rotate_method_rows(np.asarray(x[b, h], dtype=np.float64)[rows], c[rows], s[rows], io)
+        return rotate_method_rows(np.asarray(x[b, h], dtype=np.float64)[rows], c[rows], s[rows], io, **kw)
 
     vh = np.asarray(v[b, h], dtype=np.float64)
     qr = np.zeros((L, v.shape[-1]))
     qr[rows] = rot_rows(q)
-    kr = rotate_method(np.asarray(k[b, h], dtype=np.float64), c, s, io)
+    kr = rotate_method(np.asarray(k[b, h], dtype=np.float64), c, s, io, **kw)
     out = masked_attention(qr, kr, vh, scale, window, rows=rows)
     if q2 is not None:
         q2r = np.zeros_like(qr)
         q2r[rows] = rot_rows(q2)
-        k2r = rotate_method(np.asarray(k2[b, h], dtype=np.float64), c, s, io)
+        k2r = rotate_method(np.asarray(k2[b, h], dtype=np.float64), c, s, io, **kw)
         out = out - lam * masked_attention(q2r, k2r, vh, scale, window, rows=rows)
     return out
 
 
-def rotate_method_rows(x_rows, c_rows, s_rows, io):
+def rotate_method_rows(x_rows, c_rows, s_rows, io, **kw):
     """rotate_method for rows whose table rows are given alongside (one per row)."""
     # rotate_method slices the table by the row count; passing per-row table rows
     # as a table of the same length keeps position m paired with its own cos/sin.
-    return rotate_method(x_rows, c_rows, s_rows, io)
+    return rotate_method(x_rows, c_rows, s_rows, io, **kw)

@@ -82,36 +82,46 @@ def brute_theta(D, base):
     return [base ** (-2.0 * i / D) for i in range(D // 2)]
 
 
-def brute_rotate_def(x, D, base):
-    """x: list over positions of lists of D floats. Exact-math RoPE (fp64 trig)."""
-    th = brute_theta(D, base)
+def _pair_index(i, R, pairing):
+    """Dims of pair i: (2i, 2i+1) adjacent, (i, i + R/2) half-split."""
+    return (2 * i, 2 * i + 1) if pairing == "adjacent" else (i, i + R // 2)
+
+
+def brute_rotate_def(x, D, base, pairing="adjacent", rotary_dim=None):
+    """x: list over positions of lists of D floats. Exact-math RoPE (fp64 trig) of the
+    first R = rotary_dim (default D) dims, pairs chosen by ``pairing``; the rest copied."""
+    R = D if rotary_dim is None else rotary_dim
+    th = brute_theta(R, base)
     out = []
     for m, row in enumerate(x):
-        r = [0.0] * D
-        for i in range(D // 2):
+        r = list(row)
+        for i in range(R // 2):
             phi = m * th[i]
             c, s = math.cos(phi), math.sin(phi)
-            a, b = row[2 * i], row[2 * i + 1]
-            r[2 * i] = math.fsum([a * c, -b * s])
-            r[2 * i + 1] = math.fsum([a * s, b * c])
+            j0, j1 = _pair_index(i, R, pairing)
+            a, b = row[j0], row[j1]
+            r[j0] = math.fsum([a * c, -b * s])
+            r[j1] = math.fsum([a * s, b * c])
         out.append(r)
     return out
 
 
-def brute_rotate_method(x, cos32, sin32, io_fmt):
+def brute_rotate_method(x, cos32, sin32, io_fmt, pairing="adjacent", rotary_dim=None):
     """FP32 rotation with every product and sum rounded on its own, exact rationals.
 
     x: list over positions of lists of D floats (exact IO values); cos32, sin32:
-    lists over positions of lists of D/2 floats holding FP32 table values.
-    io_fmt=None returns the FP32 results without the cast back.
+    lists over positions of lists of R/2 floats holding FP32 table values.
+    io_fmt=None returns the FP32 results without the cast back. Dims >= R are copied.
     """
     out = []
     for m, row in enumerate(x):
         D = len(row)
-        r = [0.0] * D
-        for i in range(D // 2):
+        R = D if rotary_dim is None else rotary_dim
+        r = list(row)
+        for i in range(R // 2):
+            j0, j1 = _pair_index(i, R, pairing)
             c, s = Fraction(cos32[m][i]), Fraction(sin32[m][i])
-            a, b = Fraction(row[2 * i]), Fraction(row[2 * i + 1])
+            a, b = Fraction(row[j0]), Fraction(row[j1])
             ac = round_fraction(a * c, FMT_F32)
             bs = round_fraction(b * s, FMT_F32)
             as_ = round_fraction(a * s, FMT_F32)
@@ -120,8 +130,8 @@ def brute_rotate_method(x, cos32, sin32, io_fmt):
             r1 = round_fraction(as_ + bc, FMT_F32)
             if io_fmt is not None:
                 r0, r1 = round_fraction(r0, io_fmt), round_fraction(r1, io_fmt)
-            r[2 * i] = float(r0)
-            r[2 * i + 1] = float(r1)
+            r[j0] = float(r0)
+            r[j1] = float(r1)
         out.append(r)
     return out
 
@@ -144,19 +154,20 @@ def _attend(qr, kr, v, scale, window):
 
 
 def brute_attention(q, k, v, scale, window=-1, lam=0.0, q2=None, k2=None,
-                    base=10000.0, method=None):
+                    base=10000.0, method=None, pairing="adjacent", rotary_dim=None):
     """Attention for one head, lists [L][D]. Differential when q2/k2 are given.
 
     method=None rotates in exact math (def mode); method=(cos32, sin32, io_fmt)
     rotates with the FP32 emulation and casts to the IO format (method mode).
+    pairing / rotary_dim as in the rotations.
     """
     D = len(q[0])
 
     def rot(x):
         if method is None:
-            return brute_rotate_def(x, D, base)
+            return brute_rotate_def(x, D, base, pairing, rotary_dim)
         cos32, sin32, io_fmt = method
-        return brute_rotate_method(x, cos32, sin32, io_fmt)
+        return brute_rotate_method(x, cos32, sin32, io_fmt, pairing, rotary_dim)
 
     o = _attend(rot(q), rot(k), v, scale, window)
     if q2 is not None:

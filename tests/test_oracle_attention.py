@@ -64,6 +64,37 @@ def test_method_mode_matches_brute(io, fmt, diff):
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("pairing,rd", [("half", 8), ("half", 4), ("adjacent", 4)])
+@pytest.mark.parametrize("diff", [False, True])
+def test_method_mode_rope_options_match_brute(pairing, rd, diff):
+    L, D, w = 10, 8, 2
+    io, fmt = "bf16", FMT_BF16
+    q, k, q2, k2, v = (_rand((1, 1, L, D), s, io) for s in range(60, 65))
+    c32, s32 = P.rope_table_f32(L, rd)
+    scale = 1 / np.sqrt(D)
+    kw = dict(lam=0.8, q2=q2, k2=k2) if diff else {}
+    got = A.attn_method(q, k, v, c32, s32, io, scale, window=w, pairing=pairing, rotary_dim=rd, **kw)[0, 0]
+    bkw = dict(lam=0.8, q2=q2[0, 0].tolist(), k2=k2[0, 0].tolist()) if diff else {}
+    want = np.array(brute_attention(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), scale, w,
+                                    method=(c32.astype(float).tolist(), s32.astype(float).tolist(), fmt),
+                                    pairing=pairing, rotary_dim=rd, **bkw))
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+    # the rows entry point agrees with the full one
+    rows = np.array([0, 3, 9])
+    r = A.attn_method_rows(q, k, v, c32, s32, io, scale, 0, 0, rows, window=w, pairing=pairing, rotary_dim=rd,
+                           **kw)
+    np.testing.assert_allclose(r, got[rows], rtol=0, atol=1e-14)
+
+
+def test_def_mode_rope_options_match_brute():
+    L, D = 9, 8
+    q, k, v = (_rand((1, 1, L, D), s) for s in (70, 71, 72))
+    got = A.attn_def(q, k, v, 0.3, window=-1, pairing="half", rotary_dim=4)[0, 0]
+    want = np.array(brute_attention(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), 0.3, -1,
+                                    pairing="half", rotary_dim=4))
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
 def test_rows_of_p_sum_to_one():
     L, D = 300, 64
     for w in (-1, 0, 5, 100):

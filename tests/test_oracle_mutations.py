@@ -17,6 +17,13 @@ import test_oracle_rope as TP
 import test_oracle_rounding as TR
 
 
+def _interleave(r0, r1):
+    out = np.empty(r0.shape[:-1] + (2 * r0.shape[-1],), dtype=r0.dtype)
+    out[..., 0::2] = r0
+    out[..., 1::2] = r1
+    return out
+
+
 def _fails(fn, *args):
     try:
         fn(*args)
@@ -31,15 +38,15 @@ def _any_fails(checks):
 
 # --- rope mutations --------------------------------------------------------------
 
-def _rot_sign_flip(x, cos, sin):
+def _rot_sign_flip(x, cos, sin, **kw):
     x = np.asarray(x, dtype=np.float64)
     L = x.shape[-2]
     c, s = np.asarray(cos, float)[:L], np.asarray(sin, float)[:L]
     x0, x1 = x[..., 0::2], x[..., 1::2]
-    return P._interleave(x0 * c + x1 * s, -x0 * s + x1 * c)
+    return _interleave(x0 * c + x1 * s, -x0 * s + x1 * c)
 
 
-def _rot_half_split(x, cos, sin):
+def _rot_half_split(x, cos, sin, **kw):
     # pairs (i, i + D/2) instead of adjacent pairs
     x = np.asarray(x, dtype=np.float64)
     L, D = x.shape[-2], x.shape[-1]
@@ -53,17 +60,17 @@ def _freq_wrong(D, base=10000.0):
     return np.power(np.float64(base), -1.0 * i / D)
 
 
-def _rot_f32_fused(x, cos32, sin32):
+def _rot_f32_fused(x, cos32, sin32, **kw):
     # rounds once at the end instead of after every FP32 operation
     x = np.asarray(x, dtype=np.float64)
     L = x.shape[-2]
     c = np.asarray(cos32, np.float64)[:L]
     s = np.asarray(sin32, np.float64)[:L]
     x0, x1 = x[..., 0::2], x[..., 1::2]
-    return P._interleave(x0 * c - x1 * s, x0 * s + x1 * c).astype(np.float32)
+    return _interleave(x0 * c - x1 * s, x0 * s + x1 * c).astype(np.float32)
 
 
-def _rot_f32_fma(x, cos32, sin32):
+def _rot_f32_fma(x, cos32, sin32, **kw):
     # r0 = fma(x0, c, -fl(x1 s)): one product left unrounded
     x = np.asarray(x, dtype=np.float64)
     L = x.shape[-2]
@@ -72,15 +79,15 @@ def _rot_f32_fma(x, cos32, sin32):
     x0, x1 = x[..., 0::2], x[..., 1::2]
     b = (x1 * s).astype(np.float32).astype(np.float64)
     d = (x1 * c).astype(np.float32).astype(np.float64)
-    return P._interleave((x0 * c - b).astype(np.float32), (x0 * s + d).astype(np.float32))
+    return _interleave((x0 * c - b).astype(np.float32), (x0 * s + d).astype(np.float32))
 
 
-def _rot_method_no_cast(x, cos32, sin32, io):
+def _rot_method_no_cast(x, cos32, sin32, io, **kw):
     x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
     L = x32.shape[-2]
     c, s = np.asarray(cos32, np.float32)[:L], np.asarray(sin32, np.float32)[:L]
     x0, x1 = x32[..., 0::2], x32[..., 1::2]
-    return P._interleave(x0 * c - x1 * s, x0 * s + x1 * c).astype(np.float64)
+    return _interleave(x0 * c - x1 * s, x0 * s + x1 * c).astype(np.float64)
 
 
 ROPE_DEF_PINS = [
@@ -195,3 +202,40 @@ def test_softmax_without_normalisation_is_caught(monkeypatch):
     monkeypatch.setattr(A, "softmax_rows", unnormalised)
     assert _fails(TA.test_rows_of_p_sum_to_one)
     assert _fails(TA.test_def_mode_matches_brute, 8, 4, -1)
+
+
+# --- RoPE option mutations -------------------------------------------------------
+
+_rotate_f32 = P.rotate_f32
+
+
+def _half_wrong_partner(x, cos32, sin32, pairing="adjacent", rotary_dim=None):
+    # half-split pairs taken as (i, i + R/2 - 1): off by one in the partner index
+    if pairing != "half":
+        return _rotate_f32(x, cos32, sin32, pairing, rotary_dim)
+    R = x.shape[-1] if rotary_dim is None else rotary_dim
+    y = np.array(x, copy=True)
+    y[..., R // 2:R] = np.roll(np.asarray(x)[..., R // 2:R], 1, axis=-1)
+    return _rotate_f32(y, cos32, sin32, pairing, rotary_dim)
+
+
+def _partial_rotates_tail(x, cos32, sin32, pairing="adjacent", rotary_dim=None):
+    # the table is reused cyclically over the whole head dim instead of stopping at R
+    R = x.shape[-1] if rotary_dim is None else rotary_dim
+    if R == x.shape[-1]:
+        return _rotate_f32(x, cos32, sin32, pairing, rotary_dim)
+    c = np.concatenate([np.asarray(cos32)] * (x.shape[-1] // R), axis=-1)
+    s = np.concatenate([np.asarray(sin32)] * (x.shape[-1] // R), axis=-1)
+    return _rotate_f32(x, c, s, pairing)
+
+
+@pytest.mark.parametrize("mut", [_half_wrong_partner, _partial_rotates_tail])
+def test_rotation_option_mistakes_are_caught(monkeypatch, mut):
+    monkeypatch.setattr(P, "rotate_f32", mut)
+    checks = [(TP.test_half_split_is_adjacent_on_permuted_dims, 32),
+              (TP.test_partial_rotary_leaves_the_tail_and_rotates_the_head, 32, "adjacent"),
+              (TP.test_partial_rotary_leaves_the_tail_and_rotates_the_head, 32, "half")]
+    from oracle.brute import FMT_F16
+    checks += [(TP.test_rotation_options_bit_exact_vs_rational, r, p, "f16", FMT_F16)
+               for r, p in ((32, "half"), (64, "half"), (32, "adjacent"))]
+    assert _any_fails(checks)

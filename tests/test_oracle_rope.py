@@ -170,3 +170,106 @@ def test_negative_control_bf16_angle_breaks_relative_position():
         errbf = max(errbf, abs(dot(cb, sb, m, n) - dot(cb, sb, m + t, n + t)))
     assert err32 < 1e-4
     assert errbf > 1.0
+
+
+# ---- RoPE options: half-split pairing and partial rotary width -------------------
+
+ROTARY = [(16, "adjacent"), (32, "adjacent"), (48, "adjacent"), (16, "half"), (32, "half"), (48, "half"),
+          (64, "half")]
+
+
+def _half_to_adjacent(x, rd):
+    """Permutation taking half-split pair members to adjacent slots: y[2i] = x[i],
+    y[2i+1] = x[i + rd/2] for i < rd/2; dims >= rd in place."""
+    y = np.array(x, copy=True)
+    y[..., 0:rd:2] = x[..., :rd // 2]
+    y[..., 1:rd:2] = x[..., rd // 2:rd]
+    return y
+
+
+@pytest.mark.parametrize("rd", [16, 32, 48, 64])
+def test_half_split_is_adjacent_on_permuted_dims(rd):
+    """The half-split FP32 rotation is the adjacent one applied to permuted dims, bit
+    for bit: the same FP32 operations on the same operand pairs."""
+    rng = np.random.default_rng(20 + rd)
+    L, D = 50, 64
+    pos = rng.integers(0, 8192, L)
+    c32, s32 = P.rope_table_f32(8192, rd)
+    c32, s32 = c32[pos], s32[pos]
+    x = R_round((rng.standard_normal((L, D)) * 3))
+    got = P.rotate_f32(x, c32, s32, pairing="half", rotary_dim=rd)
+    want = P.rotate_f32(_half_to_adjacent(x, rd), c32, s32, rotary_dim=rd)
+    np.testing.assert_array_equal(_half_to_adjacent(got, rd), want)
+
+
+def R_round(x):
+    return R.round_io(np.asarray(x, dtype=np.float32), "bf16")
+
+
+@pytest.mark.parametrize("rd,pairing", ROTARY)
+def test_partial_rotary_leaves_the_tail_and_rotates_the_head(rd, pairing):
+    rng = np.random.default_rng(30 + rd)
+    L, D = 40, 64
+    c32, s32 = P.rope_table_f32(L, rd)
+    x = R_round(rng.standard_normal((L, D)) * 2)
+    got = P.rotate_f32(x, c32, s32, pairing=pairing, rotary_dim=rd)
+    # trailing dims are the input, exactly
+    np.testing.assert_array_equal(got[:, rd:].astype(np.float64), x[:, rd:])
+    # leading dims are the full-width rotation of a head of dim rd
+    head = P.rotate_f32(x[:, :rd], c32, s32, pairing=pairing)
+    np.testing.assert_array_equal(got[:, :rd], head)
+
+
+@pytest.mark.parametrize("rd,pairing", ROTARY + [(64, "adjacent")])
+@pytest.mark.parametrize("io,fmt", [("f16", FMT_F16), ("bf16", FMT_BF16)])
+def test_rotation_options_bit_exact_vs_rational(rd, pairing, io, fmt):
+    rng = np.random.default_rng(40 + rd)
+    L, D = 24, 64
+    pos = np.concatenate([np.arange(8), rng.integers(8, 8192, 16)])
+    c32, s32 = P.rope_table_f32(8192, rd)
+    c32, s32 = c32[pos], s32[pos]
+    x = R.round_io((rng.standard_normal((L, D)) * 2).astype(np.float32), io)
+    got = P.rotate_method(x, c32, s32, io, pairing=pairing, rotary_dim=rd)
+    want = np.array(brute_rotate_method(x.tolist(), c32.astype(float).tolist(), s32.astype(float).tolist(),
+                                        fmt, pairing=pairing, rotary_dim=rd))
+    np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("rd,pairing", ROTARY)
+def test_rotate_def_options_match_brute(rd, pairing):
+    rng = np.random.default_rng(50 + rd)
+    L, D = 12, 64
+    x = rng.standard_normal((L, D))
+    phi = P.rope_angles(L, rd)
+    got = P.rotate_def(x, np.cos(phi), np.sin(phi), pairing=pairing, rotary_dim=rd)
+    want = np.array(brute_rotate_def(x.tolist(), D, 10000.0, pairing=pairing, rotary_dim=rd))
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("rd,pairing", ROTARY)
+def test_dot_depends_only_on_offset_with_options(rd, pairing):
+    rng = np.random.default_rng(60 + rd)
+    D = 64
+    th = P.rope_frequencies(rd)
+
+    def rot(x, m):
+        phi = m * th
+        return P.rotate_def(x[None, :], np.cos(phi)[None, :], np.sin(phi)[None, :], pairing=pairing,
+                            rotary_dim=rd)[0]
+
+    for _ in range(100):
+        q, k = rng.standard_normal(D), rng.standard_normal(D)
+        m, n, t = (int(v) for v in rng.integers(0, 8192, 3))
+        a, b = rot(q, m) @ rot(k, n), rot(q, m + t) @ rot(k, n + t)
+        assert abs(a - b) < 1e-9 * (1 + abs(a))
+
+
+def test_rotation_option_errors():
+    x = np.zeros((2, 64))
+    c, s = P.rope_table_f32(2, 64)
+    with pytest.raises(ValueError):
+        P.rotate_f32(x, c, s, pairing="interleaved")
+    with pytest.raises(ValueError):
+        P.rotate_f32(x, c, s, rotary_dim=66)
+    with pytest.raises(ValueError):
+        P.rotate_f32(x, c, s, rotary_dim=15)
