@@ -31,7 +31,8 @@
  *  - RoPE rotates adjacent pairs (x[2i], x[2i+1]) at position m = 0..L-1 of each
  *    (b, h) slab: r0 = fl(fl(x0 c) - fl(x1 s)), r1 = fl(fl(x0 s) + fl(x1 c)) in FP32,
  *    then rounds to nearest-even to the IO dtype.
- *  - cos, sin: FP32 tables [L_tab][D/2], L_tab >= L; row m holds cos(m theta_i) and
+ *  - cos, sin: FP32 tables [L_tab][D/2] ([L_tab][R/2] with a partial rotary width
+ *    R, see sa3attn_forward_general), L_tab >= L; row m holds cos(m theta_i) and
  *    sin(m theta_i), shared across B and H. Only rows < L are read. The library
  *    cannot check L_tab: passing a shorter table is a caller error.
  *  - window: half-width w; key j is masked for query i when |i - j| > w.
@@ -62,7 +63,7 @@ extern "C" {
 #endif
 
 #define SA3ATTN_VERSION_MAJOR 0
-#define SA3ATTN_VERSION_MINOR 2
+#define SA3ATTN_VERSION_MINOR 3
 
 /* Status codes. */
 enum {
@@ -147,6 +148,29 @@ typedef struct sa3attn_strides {
 } sa3attn_strides;
 
 int sa3attn_forward_strided(const sa3attn_desc *desc, const sa3attn_strides *strides);
+
+/*
+ * sa3attn_rope / sa3attn_forward_general -- RoPE options and the most general form.
+ * The pages do not pin which dims RoPE pairs up; the default (every other entry
+ * point) is adjacent pairs over the whole head dim. Options:
+ *   pairing:    SA3_ROPE_ADJACENT, pairs (x[2i], x[2i+1]), or SA3_ROPE_HALF, pairs
+ *               (x[i], x[i + R/2]) (the rotate-half convention), i = 0 .. R/2 - 1;
+ *   rotary_dim: R, the leading dims rotated: a multiple of 16, 16 <= R <= D; dims
+ *               R .. D-1 pass through unchanged.
+ * Pair i uses table column i: cos and sin are then [L_tab][R/2] (sa3attn_rope_table
+ * with D = R gives theta_i = base^(-2i/R)). The FP32 arithmetic per pair and the
+ * cast back are the same as for the default.
+ * strides NULL = contiguous [B][H][L][D] (as sa3attn_forward_ex); rope NULL =
+ * the default. Bad options return SA3_ERR_ARG before anything is enqueued.
+ */
+enum { SA3_ROPE_ADJACENT = 0, SA3_ROPE_HALF = 1 };
+typedef struct sa3attn_rope {
+    int pairing;
+    int rotary_dim;
+} sa3attn_rope;
+
+int sa3attn_forward_general(const sa3attn_desc *desc, const sa3attn_strides *strides,
+                            const sa3attn_rope *rope);
 
 /*
  * sa3attn_rope_table -- fill a host FP32 cos/sin table [L][D/2].

@@ -28,6 +28,7 @@ EXPORTS = (
     "sa3attn_forward_bf16",
     "sa3attn_forward_ex",
     "sa3attn_forward_strided",
+    "sa3attn_forward_general",
     "sa3attn_rope_table",
     "sa3attn_status_string",
     "sa3attn_version",
@@ -60,6 +61,12 @@ class _Strides(ctypes.Structure):
     ]
 
 
+class _Rope(ctypes.Structure):
+    _fields_ = [("pairing", ctypes.c_int), ("rotary_dim", ctypes.c_int)]
+
+
+ROPE_PAIRINGS = {"adjacent": 0, "half": 1}
+
 _lib = None
 
 
@@ -86,6 +93,8 @@ def load_library():
     lib.sa3attn_forward_ex.restype = i
     lib.sa3attn_forward_strided.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_Strides)]
     lib.sa3attn_forward_strided.restype = i
+    lib.sa3attn_forward_general.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_Strides), ctypes.POINTER(_Rope)]
+    lib.sa3attn_forward_general.restype = i
     lib.sa3attn_rope_table.argtypes = [vp, vp, i, i, ctypes.c_double]
     lib.sa3attn_rope_table.restype = i
     lib.sa3attn_status_string.argtypes = [i]
@@ -143,9 +152,12 @@ def rope_table(L, D=64, base=10000.0):
 
 
 def forward(q, k, v, cos, sin, *, window=-1, lam=0.0, scale=None, out=None, out_dtype=None,
-            differential=None, stream=None):
-    """Run the fused core through sa3attn_forward_ex, or sa3attn_forward_strided when a
-    tensor is a strided view.
+            differential=None, stream=None, pairing="adjacent", rotary_dim=None):
+    """Run the fused core through sa3attn_forward_ex, or sa3attn_forward_general when a
+    tensor is a strided view or a RoPE option is set.
+
+    pairing: "adjacent" (default) or "half" (pairs x[i], x[i + R/2]); rotary_dim: R,
+    the leading dims rotated (default D; a multiple of 16), cos/sin then [>=L, R/2].
 
     q, k: [B, H, L, D] (plain) or [2, B, H, L, D] (differential), fp16 or bf16, on the
     GPU; v: [B, H, L, D], same dtype; out: [B, H, L, D]. Any of them may be a view with
@@ -182,8 +194,11 @@ def forward(q, k, v, cos, sin, *, window=-1, lam=0.0, scale=None, out=None, out_
         raise TypeError("q, k and v must share one dtype")
     if cos.dtype != torch.float32 or sin.dtype != torch.float32:
         raise TypeError("cos and sin must be float32")
-    if cos.dim() != 2 or cos.shape[0] < L or cos.shape[1] != D // 2 or tuple(sin.shape) != tuple(cos.shape):
-        raise ValueError(f"cos/sin must be [>= {L}, {D // 2}]")
+    R = D if rotary_dim is None else int(rotary_dim)
+    if pairing not in ROPE_PAIRINGS:
+        raise ValueError(f"pairing must be one of {tuple(ROPE_PAIRINGS)}")
+    if cos.dim() != 2 or cos.shape[0] < L or cos.shape[1] != R // 2 or tuple(sin.shape) != tuple(cos.shape):
+        raise ValueError(f"cos/sin must be [>= {L}, {R // 2}]")
     if out.dtype != out_dtype:
         raise TypeError("out dtype does not match out_dtype")
     # for a differential q / k, the data pointer is branch 1; branch 2 is one stride on
@@ -193,19 +208,25 @@ def forward(q, k, v, cos, sin, *, window=-1, lam=0.0, scale=None, out=None, out_
               _dt_code(v.dtype), _dt_code(out.dtype), 1 if differential else 0,
               _stream_handle(stream, v.device))
     lib = load_library()
-    if all(t.is_contiguous() for t in (q, k, v, out)):
+    contiguous = all(t.is_contiguous() for t in (q, k, v, out))
+    default_rope = pairing == "adjacent" and R == D
+    if contiguous and default_rope:
         rc = lib.sa3attn_forward_ex(ctypes.byref(d))
         what = "sa3attn_forward_ex"
     else:
-        st = _Strides()
-        st.q[:] = qq.stride()[:3]
-        st.k[:] = kk.stride()[:3]
-        st.v[:] = v.stride()[:3]
-        st.out[:] = out.stride()[:3]
-        st.q_branch = q.stride(0) if differential else 0
-        st.k_branch = k.stride(0) if differential else 0
-        rc = lib.sa3attn_forward_strided(ctypes.byref(d), ctypes.byref(st))
-        what = "sa3attn_forward_strided"
+        st = None
+        if not contiguous:
+            st = _Strides()
+            st.q[:] = qq.stride()[:3]
+            st.k[:] = kk.stride()[:3]
+            st.v[:] = v.stride()[:3]
+            st.out[:] = out.stride()[:3]
+            st.q_branch = q.stride(0) if differential else 0
+            st.k_branch = k.stride(0) if differential else 0
+        rope = None if default_rope else _Rope(ROPE_PAIRINGS[pairing], R)
+        rc = lib.sa3attn_forward_general(ctypes.byref(d), ctypes.byref(st) if st is not None else None,
+                                         ctypes.byref(rope) if rope is not None else None)
+        what = "sa3attn_forward_general"
     if rc != 0:
         raise SA3Error(rc, what)
     return out

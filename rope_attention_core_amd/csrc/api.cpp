@@ -93,7 +93,7 @@ bool rows_distinct(const long long s[3], int B, int H, int L) {
     return true;
 }
 
-int forward_impl(const sa3attn_desc *d, const sa3attn_strides *sp) {
+int forward_impl(const sa3attn_desc *d, const sa3attn_strides *sp, const sa3attn_rope *rp) {
     if (!d) return SA3_ERR_NULL;
     if (!d->q || !d->k || !d->v || !d->cos || !d->sin || !d->out) return SA3_ERR_NULL;
     if (d->B < 1 || d->H < 1 || d->L < 1 || d->D < 1 || (d->D & 1)) return SA3_ERR_SHAPE;
@@ -123,6 +123,11 @@ int forward_impl(const sa3attn_desc *d, const sa3attn_strides *sp) {
     if (d->differential && (s.q_branch < 0 || (s.q_branch & 7) || s.k_branch < 0 || (s.k_branch & 7)))
         return SA3_ERR_ARG;
     if (!rows_distinct(s.out, d->B, d->H, d->L)) return SA3_ERR_ARG;
+    // RoPE options: adjacent or half-split pairs over the leading R dims
+    const int pairing = rp ? rp->pairing : SA3_ROPE_ADJACENT;
+    const int rot_dim = rp ? rp->rotary_dim : d->D;
+    if (pairing != SA3_ROPE_ADJACENT && pairing != SA3_ROPE_HALF) return SA3_ERR_ARG;
+    if (rot_dim < 16 || rot_dim > d->D || (rot_dim & 15)) return SA3_ERR_ARG;
     if (!aligned16(d->q) || !aligned16(d->k) || !aligned16(d->v) || !aligned16(d->out) || !aligned16(d->cos) ||
         !aligned16(d->sin))
         return SA3_ERR_ARG;
@@ -135,7 +140,7 @@ int forward_impl(const sa3attn_desc *d, const sa3attn_strides *sp) {
     const size_t k_bytes = (size_t)(extent_bytes(s.k, d->B, d->H, d->L, 2) +
                                     (d->differential ? (unsigned long long)s.k_branch * 2ull : 0ull));
     const size_t v_bytes = (size_t)extent_bytes(s.v, d->B, d->H, d->L, 2);
-    const size_t tab_bytes = (size_t)d->L * 32 * sizeof(float);
+    const size_t tab_bytes = (size_t)d->L * (size_t)(rot_dim / 2) * sizeof(float);
     if (overlaps(d->out, out_bytes, d->q, q_bytes) || overlaps(d->out, out_bytes, d->k, k_bytes) ||
         overlaps(d->out, out_bytes, d->v, v_bytes) || overlaps(d->out, out_bytes, d->cos, tab_bytes) ||
         overlaps(d->out, out_bytes, d->sin, tab_bytes))
@@ -162,8 +167,11 @@ int forward_impl(const sa3attn_desc *d, const sa3attn_strides *sp) {
         for (int i = 0; i < 3; ++i)
             contig = contig && s.q[i] == c[i] && s.k[i] == c[i] && s.v[i] == c[i] && s.out[i] == c[i];
         if (d->differential) contig = contig && s.q_branch == (long long)elems && s.k_branch == (long long)elems;
+        contig = contig && pairing == SA3_ROPE_ADJACENT && rot_dim == d->D;
         a.contig = contig ? 1 : 0;
     }
+    a.rope_half = pairing == SA3_ROPE_HALF ? 1 : 0;
+    a.rot_dim = rot_dim;
     a.B = d->B;
     a.H = d->H;
     a.L = d->L;
@@ -192,11 +200,15 @@ int forward_impl(const sa3attn_desc *d, const sa3attn_strides *sp) {
 
 extern "C" {
 
-int sa3attn_forward_ex(const sa3attn_desc *desc) { return forward_impl(desc, nullptr); }
+int sa3attn_forward_ex(const sa3attn_desc *desc) { return forward_impl(desc, nullptr, nullptr); }
 
 int sa3attn_forward_strided(const sa3attn_desc *desc, const sa3attn_strides *strides) {
     if (!strides) return SA3_ERR_NULL;
-    return forward_impl(desc, strides);
+    return forward_impl(desc, strides, nullptr);
+}
+
+int sa3attn_forward_general(const sa3attn_desc *desc, const sa3attn_strides *strides, const sa3attn_rope *rope) {
+    return forward_impl(desc, strides, rope);
 }
 
 static int forward_short(const void *q, const void *k, const void *v, const float *cos, const float *sin,
@@ -220,7 +232,7 @@ static int forward_short(const void *q, const void *k, const void *v, const floa
     d.out_dtype = dtype;
     d.differential = lambda != 0.0f ? 1 : 0;
     d.stream = stream;
-    return forward_impl(&d, nullptr);
+    return forward_impl(&d, nullptr, nullptr);
 }
 
 int sa3attn_forward(const void *q, const void *k, const void *v, const float *cos, const float *sin, void *out,

@@ -48,6 +48,8 @@ struct Params {
     uint32_t q_rowb, k_rowb, v_rowb;                // bytes from one position to the next
     int H, L, window, n_qtiles, out_dtype, neg_scale;
     float lam, c;                 // c = |scale| * log2(e)
+    int rope_half, rot_dim;       // RoPE of the general instances: half-split pairs, rotary width
+    uint32_t tab_rowb;            // bytes per cos/sin table row (rot_dim / 2 floats)
 };
 
 // Kernel parameters common to every instance (n_qtiles and window are set by the caller).
@@ -81,6 +83,9 @@ inline Params make_params(const LaunchArgs &a) {
     P.neg_scale = a.neg_scale;
     P.lam = a.lam;
     P.c = a.scale_log2;
+    P.rope_half = a.rope_half;
+    P.rot_dim = a.rot_dim;
+    P.tab_rowb = (uint32_t)(a.rot_dim / 2 * 4);
     return P;
 }
 
@@ -127,6 +132,72 @@ __device__ __forceinline__ u32x4 rope8(u32x4 x, u32x4 cw, u32x4 sw) {
         const float e = x0 * s;
         const float f = x1 * c;
         r[j] = pack2<IO>(a - b, e + f);
+    }
+    return r;
+}
+
+// ---- RoPE of the general instances --------------------------------------------
+// Chunk c of a position (dims 8c .. 8c+7) under pairing `half` and rotary width R
+// (a multiple of 16, <= 64): mode 0 passes it through (c >= R/8); mode 1 rotates
+// adjacent pairs with table floats 4c .. 4c+3; mode 2 (half-split, c < R/16) pairs
+// it with chunk c + R/16 as the first members, mode 3 (R/16 <= c < R/8) with chunk
+// c - R/16 as the second members, both with table floats 8j .. 8j+7 of j = c mod R/16.
+struct RopeChunk {
+    int mode;
+    int partner;      // chunk index of the other pair members (modes 2 and 3)
+    uint32_t toff;    // byte offset of the table floats inside a table row
+};
+__device__ __forceinline__ RopeChunk rope_chunk(int c, int half, int R) {
+    RopeChunk k;
+    const int h = R >> 4;     // chunks per half of the rotated dims
+    if (c >= (R >> 3)) {
+        k.mode = 0;
+        k.partner = c;
+        k.toff = 0;
+    } else if (!half) {
+        k.mode = 1;
+        k.partner = c;
+        k.toff = (uint32_t)c * 16;
+    } else if (c < h) {
+        k.mode = 2;
+        k.partner = c + h;
+        k.toff = (uint32_t)c * 32;
+    } else {
+        k.mode = 3;
+        k.partner = c - h;
+        k.toff = (uint32_t)(c - h) * 32;
+    }
+    return k;
+}
+
+// The rotation of one chunk in FP32, every product and sum rounded on its own, then
+// RNE to the IO dtype. own / partner: the chunk and its partner chunk; c0, c1 / s0,
+// s1: table floats 0-3 and 4-7 of the chunk's table slice (mode 1 uses c0 / s0).
+template <int IO>
+__device__ __forceinline__ u32x4 rope8_general(u32x4 own, u32x4 partner, u32x4 c0, u32x4 c1, u32x4 s0,
+                                               u32x4 s1, int mode) {
+#pragma clang fp contract(off)
+    if (mode == 0) return own;
+    if (mode == 1) return rope8<IO>(own, c0, s0);
+    u32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float o0, o1, p0, p1;
+        unpack2<IO>(own[j], o0, o1);
+        unpack2<IO>(partner[j], p0, p1);
+        const float ca = __uint_as_float(j < 2 ? c0[2 * j] : c1[2 * j - 4]);
+        const float cb = __uint_as_float(j < 2 ? c0[2 * j + 1] : c1[2 * j - 3]);
+        const float sa = __uint_as_float(j < 2 ? s0[2 * j] : s1[2 * j - 4]);
+        const float sb = __uint_as_float(j < 2 ? s0[2 * j + 1] : s1[2 * j - 3]);
+        float ra, rb;
+        if (mode == 2) {            // first members: x0 c - x1 s with x0 = own, x1 = partner
+            ra = o0 * ca - p0 * sa;
+            rb = o1 * cb - p1 * sb;
+        } else {                    // second members: x0 s + x1 c with x0 = partner, x1 = own
+            ra = p0 * sa + o0 * ca;
+            rb = p1 * sb + o1 * cb;
+        }
+        r[j] = pack2<IO>(ra, rb);
     }
     return r;
 }

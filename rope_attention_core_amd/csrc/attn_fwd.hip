@@ -116,9 +116,12 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(Params P) {
         rk[br] = slab_rsrc(P.k, br * kbr + (CONTIG ? slab : bb * P.kb + hh * P.kh), krb, L);
     const rsrc_t rq = slab_rsrc(P.q, wbr * qbr + (CONTIG ? slab : bb * P.qb + hh * P.qh), qrb, L);
     const rsrc_t rv = slab_rsrc(P.v, CONTIG ? slab : bb * P.vb + hh * P.vh, vrb, L);
-    const uint32_t nrec = (uint32_t)L * ROWB;   // cos/sin: [L][32] floats, 128 bytes per row
-    const rsrc_t rc = make_rsrc(P.cos, nrec);
-    const rsrc_t rs = make_rsrc(P.sin, nrec);
+    // cos/sin: [L][R/2] floats (R = 64 in the contiguous instances: 128 bytes per row)
+    const uint32_t trb = CONTIG ? (uint32_t)ROWB : P.tab_rowb;
+    const rsrc_t rc = make_rsrc(P.cos, (uint32_t)L * trb);
+    const rsrc_t rs = make_rsrc(P.sin, (uint32_t)L * trb);
+    const int rhalf = P.rope_half, rdim = P.rot_dim;
+    constexpr uint32_t NOWHERE = 0xfffffff0u;   // an offset past every buffer: reads zeros
 
     const int q0 = qt * BM;
     const int qw = q0 + wq * 32;
@@ -131,8 +134,17 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(Params P) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const uint32_t col = (uint32_t)(16 * ks + 8 * g) * 2;
-            const uint32_t offc = row * ROWB + col;
-            qreg[ks] = rope8<IO>(bload(rq, row * qrb + col), bload(rc, offc), bload(rs, offc)) ^ qsign;
+            if constexpr (CONTIG) {
+                const uint32_t offc = row * ROWB + col;
+                qreg[ks] = rope8<IO>(bload(rq, row * qrb + col), bload(rc, offc), bload(rs, offc)) ^ qsign;
+            } else {
+                const RopeChunk rc8 = rope_chunk(2 * ks + g, rhalf, rdim);
+                const uint32_t to = rc8.mode ? row * trb + rc8.toff : NOWHERE;
+                const uint32_t t1 = rc8.mode >= 2 ? to + 16 : NOWHERE;
+                const uint32_t po = rc8.mode >= 2 ? row * qrb + (uint32_t)rc8.partner * 16 : NOWHERE;
+                qreg[ks] = rope8_general<IO>(bload(rq, row * qrb + col), bload(rq, po), bload(rc, to), bload(rc, t1),
+                                             bload(rs, to), bload(rs, t1), rc8.mode) ^ qsign;
+            }
         }
     }
 
@@ -152,19 +164,35 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(Params P) {
     const int vp = tid & 31;
     const int vd0 = (tid >> 5) * VD;
     u32x4 rawk[NBS], rawc, raws;
+    u32x4 rawp[NBS], rawc1, raws1;   // general instances: partner chunks, table floats 4-7
     u32x2 rawv[2];
 
     // per-lane parts of the staging offsets (one multiply each, here); the per-tile part
     // k0 * row bytes is wave-uniform and comes from the scalar unit
+    const RopeChunk kch = rope_chunk(tid & 7, rhalf, rdim);
     const uint32_t kl = (uint32_t)(tid >> 3) * krb + (uint32_t)(tid & 7) * 16;
-    const uint32_t cl = (uint32_t)(tid >> 3) * ROWB + (uint32_t)(tid & 7) * 16;
+    const uint32_t kpl = (uint32_t)(tid >> 3) * krb + (uint32_t)kch.partner * 16;
+    const uint32_t cl = CONTIG ? (uint32_t)(tid >> 3) * ROWB + (uint32_t)(tid & 7) * 16
+                               : (uint32_t)(tid >> 3) * trb + kch.toff;
     const uint32_t vl = (uint32_t)(2 * vp) * vrb + (uint32_t)vd0 * 2;
     auto load_raw = [&](int t) __attribute__((always_inline)) {
         const uint32_t k0 = (uint32_t)(t * BN);
 #pragma unroll
         for (int br = 0; br < NBS; ++br) rawk[br] = bload(rk[br], kl + k0 * krb);
-        rawc = bload(rc, cl + k0 * ROWB);
-        raws = bload(rs, cl + k0 * ROWB);
+        if constexpr (CONTIG) {
+            rawc = bload(rc, cl + k0 * ROWB);
+            raws = bload(rs, cl + k0 * ROWB);
+        } else {
+            const uint32_t to = kch.mode ? cl + k0 * trb : NOWHERE;
+            const uint32_t t1 = kch.mode >= 2 ? to + 16 : NOWHERE;
+            const uint32_t po = kch.mode >= 2 ? kpl + k0 * krb : NOWHERE;
+#pragma unroll
+            for (int br = 0; br < NBS; ++br) rawp[br] = bload(rk[br], po);
+            rawc = bload(rc, to);
+            raws = bload(rs, to);
+            rawc1 = bload(rc, t1);
+            raws1 = bload(rs, t1);
+        }
         rawv[0] = bload8(rv, vl + k0 * vrb);
         rawv[1] = bload8(rv, vl + k0 * vrb + vrb);
     };
@@ -177,8 +205,14 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(Params P) {
         uint16_t *Ks = smem + buf * BUF_ELEMS;
         uint16_t *Vt = Ks + NBS * KS_ELEMS;
 #pragma unroll
-        for (int br = 0; br < NBS; ++br)
-            *reinterpret_cast<u32x4 *>(Ks + br * KS_ELEMS + kat) = rope8<IO>(rawk[br], rawc, raws);
+        for (int br = 0; br < NBS; ++br) {
+            u32x4 rot;
+            if constexpr (CONTIG)
+                rot = rope8<IO>(rawk[br], rawc, raws);
+            else
+                rot = rope8_general<IO>(rawk[br], rawp[br], rawc, rawc1, raws, raws1, kch.mode);
+            *reinterpret_cast<u32x4 *>(Ks + br * KS_ELEMS + kat) = rot;
+        }
 #pragma unroll
         for (int j = 0; j < VD; ++j) {
             const uint32_t wa = rawv[0][j >> 1], wb = rawv[1][j >> 1];

@@ -49,11 +49,12 @@ struct NarrowShape {
 };
 
 // Windowed mode keeps registers <= 168 so that three workgroups share a CU (their LDS
-// fits too); short-sequence mode may use up to 256.
+// fits too); short-sequence mode and the general instances may use up to 256 (512 for
+// the general 256-key span).
 // CONTIG: contiguous [B][H][L][64] tensors (q, k stacked [2][...]); the row strides
 // are then compile-time constants.
 template <int IO, bool DIFF, int NKF, bool CONTIG>
-__global__ __launch_bounds__(256, NKF ? 2 : 3) void attn_narrow_kernel(Params P) {
+__global__ __launch_bounds__(256, CONTIG ? (NKF ? 2 : 3) : (NKF == 256 ? 1 : 2)) void attn_narrow_kernel(Params P) {
     using S = NarrowShape<DIFF, NKF>;
     constexpr int NT = S::NT, NBS = S::NBS, WPB = S::WPB, BM = S::BM, NK = S::NK, NKB = S::NKB;
     constexpr int KC = NK * 8 / NT;          // K chunks (8 elements) per thread per branch
@@ -95,15 +96,22 @@ __global__ __launch_bounds__(256, NKF ? 2 : 3) void attn_narrow_kernel(Params P)
         rk[br] = slab_rsrc(P.k, br * kbr + (CONTIG ? slab : bb * P.kb + hh * P.kh), krb, L);
     const rsrc_t rq = slab_rsrc(P.q, wbr * qbr + (CONTIG ? slab : bb * P.qb + hh * P.qh), qrb, L);
     const rsrc_t rv = slab_rsrc(P.v, CONTIG ? slab : bb * P.vb + hh * P.vh, vrb, L);
-    const uint32_t nrec = (uint32_t)L * ROWB;   // cos/sin: [L][32] floats, 128 bytes per row
-    const rsrc_t rc = make_rsrc(P.cos, nrec);
-    const rsrc_t rs = make_rsrc(P.sin, nrec);
+    // cos/sin: [L][R/2] floats (R = 64 in the contiguous instances: 128 bytes per row)
+    const uint32_t trb = CONTIG ? (uint32_t)ROWB : P.tab_rowb;
+    const rsrc_t rc = make_rsrc(P.cos, (uint32_t)L * trb);
+    const rsrc_t rs = make_rsrc(P.sin, (uint32_t)L * trb);
+    const int rhalf = P.rope_half, rdim = P.rot_dim;
+    constexpr uint32_t NOWHERE = 0xfffffff0u;   // an offset past every buffer: reads zeros
 
     const int q0 = qt * BM;
     const int qw = q0 + wq * 32;
     const int ks0 = NKF ? 0 : q0 - w;        // first staged key (may be negative)
 
     // ---- issue every load: Q rows of this wave, then the K / cos / sin / V span ------
+    // Q: the rotated chunks go straight to registers; general instances also load the
+    // partner chunks and table floats 4-7 (half-split pairs)
+    u32x4 qreg[4];
+    const uint32_t qsign = P.neg_scale ? 0x80008000u : 0u;
     u32x4 rq_raw[4], rqc[4], rqs[4];
     {
         const uint32_t row = (uint32_t)(qw + r);
@@ -111,22 +119,47 @@ __global__ __launch_bounds__(256, NKF ? 2 : 3) void attn_narrow_kernel(Params P)
         for (int ks = 0; ks < 4; ++ks) {
             const uint32_t col = (uint32_t)(16 * ks + 8 * g) * 2;
             rq_raw[ks] = bload(rq, row * qrb + col);
-            rqc[ks] = bload(rc, row * ROWB + col);
-            rqs[ks] = bload(rs, row * ROWB + col);
+            if constexpr (CONTIG) {
+                rqc[ks] = bload(rc, row * ROWB + col);
+                rqs[ks] = bload(rs, row * ROWB + col);
+            } else {
+                const RopeChunk rc8 = rope_chunk(2 * ks + g, rhalf, rdim);
+                const uint32_t to = rc8.mode ? row * trb + rc8.toff : NOWHERE;
+                const uint32_t t1 = rc8.mode >= 2 ? to + 16 : NOWHERE;
+                const uint32_t po = rc8.mode >= 2 ? row * qrb + (uint32_t)rc8.partner * 16 : NOWHERE;
+                qreg[ks] = rope8_general<IO>(rq_raw[ks], bload(rq, po), bload(rc, to), bload(rc, t1), bload(rs, to),
+                                             bload(rs, t1), rc8.mode) ^ qsign;
+            }
         }
     }
     // K item i: span row (tid >> 3) + i * NT / 8, chunk tid & 7. The per-lane part of
     // the offset is one multiply here; the per-item part is wave-uniform (scalar unit).
     u32x4 rawk[NBS][KC], rawc[KC], raws[KC];
+    u32x4 rawp[CONTIG ? 1 : NBS][CONTIG ? 1 : KC], rawc1[CONTIG ? 1 : KC], raws1[CONTIG ? 1 : KC];
+    const RopeChunk kch = rope_chunk(tid & 7, rhalf, rdim);
     const uint32_t kl = (uint32_t)(tid >> 3) * krb + (uint32_t)(tid & 7) * 16;
-    const uint32_t cl = (uint32_t)(tid >> 3) * ROWB + (uint32_t)(tid & 7) * 16;
+    const uint32_t kpl = (uint32_t)(tid >> 3) * krb + (uint32_t)kch.partner * 16;
+    const uint32_t cl = CONTIG ? (uint32_t)(tid >> 3) * ROWB + (uint32_t)(tid & 7) * 16
+                               : (uint32_t)(tid >> 3) * trb + kch.toff;
 #pragma unroll
     for (int i = 0; i < KC; ++i) {
         const uint32_t r0 = (uint32_t)(ks0 + i * (NT / 8));
 #pragma unroll
         for (int br = 0; br < NBS; ++br) rawk[br][i] = bload(rk[br], kl + r0 * krb);
-        rawc[i] = bload(rc, cl + r0 * ROWB);
-        raws[i] = bload(rs, cl + r0 * ROWB);
+        if constexpr (CONTIG) {
+            rawc[i] = bload(rc, cl + r0 * ROWB);
+            raws[i] = bload(rs, cl + r0 * ROWB);
+        } else {
+            const uint32_t to = kch.mode ? cl + r0 * trb : NOWHERE;
+            const uint32_t t1 = kch.mode >= 2 ? to + 16 : NOWHERE;
+            const uint32_t po = kch.mode >= 2 ? kpl + r0 * krb : NOWHERE;
+#pragma unroll
+            for (int br = 0; br < NBS; ++br) rawp[br][i] = bload(rk[br], po);
+            rawc[i] = bload(rc, to);
+            raws[i] = bload(rs, to);
+            rawc1[i] = bload(rc, t1);
+            raws1[i] = bload(rs, t1);
+        }
     }
     // V item: keys 2p, 2p + 1 of the span and 8 values of d from 8 * ch
     u32x4 rawv[VC][2];
@@ -140,17 +173,23 @@ __global__ __launch_bounds__(256, NKF ? 2 : 3) void attn_narrow_kernel(Params P)
     }
 
     // ---- rotate Q into registers; rotate / transpose the span into LDS ---------------
-    u32x4 qreg[4];
-    const uint32_t qsign = P.neg_scale ? 0x80008000u : 0u;
+    if constexpr (CONTIG) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qreg[ks] = rope8<IO>(rq_raw[ks], rqc[ks], rqs[ks]) ^ qsign;
+        for (int ks = 0; ks < 4; ++ks) qreg[ks] = rope8<IO>(rq_raw[ks], rqc[ks], rqs[ks]) ^ qsign;
+    }
 #pragma unroll
     for (int i = 0; i < KC; ++i) {
         const int it = tid + NT * i;
         const int at = (it >> 3) * S::KS + (it & 7) * 8;
 #pragma unroll
-        for (int br = 0; br < NBS; ++br)
-            *reinterpret_cast<u32x4 *>(smem + br * S::K_ELEMS + at) = rope8<IO>(rawk[br][i], rawc[i], raws[i]);
+        for (int br = 0; br < NBS; ++br) {
+            u32x4 rot;
+            if constexpr (CONTIG)
+                rot = rope8<IO>(rawk[br][i], rawc[i], raws[i]);
+            else
+                rot = rope8_general<IO>(rawk[br][i], rawp[br][i], rawc[i], rawc1[i], raws[i], raws1[i], kch.mode);
+            *reinterpret_cast<u32x4 *>(smem + br * S::K_ELEMS + at) = rot;
+        }
     }
     uint16_t *Vt = smem + NBS * S::K_ELEMS;
 #pragma unroll

@@ -24,7 +24,9 @@ struct LaunchArgs {
     int dtype;              // SA3_F16 / SA3_BF16
     int out_dtype;          // SA3_F16 / SA3_BF16 / SA3_F32
     int diff;               // two branches
-    int contig;             // strides are those of contiguous [B][H][L][64] (and stacked [2][...])
+    int contig;             // contiguous [B][H][L][64] (and stacked [2][...]), adjacent pairs, R = 64
+    int rope_half;          // RoPE pairs (x[i], x[i + R/2]) instead of (x[2i], x[2i+1])
+    int rot_dim;            // R: leading dims rotated (multiple of 16, <= 64); the table has R/2 columns
     void *stream;           // hipStream_t
 };
 

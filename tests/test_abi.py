@@ -46,7 +46,7 @@ def test_status_strings_and_version(lib):
         s = sa3.status_string(code)
         assert s.startswith("SA3_ERR_"), s
     assert "unknown" in sa3.status_string(12345)
-    assert sa3.version() == (0, 2)
+    assert sa3.version() == (0, 3)
 
 
 @pytest.mark.parametrize("L,D", [(1, 2), (37, 8), (8192, 16), (8192, 64), (8192, 128)])
@@ -234,3 +234,48 @@ def test_valid_strided_call_without_gpu_reports_device_error(lib):
     base = _fake(9).value
     assert _call_strided(lib, _strides(layout="blhd"), q=ctypes.c_void_p(base), k=ctypes.c_void_p(base),
                          v=ctypes.c_void_p(base)) == SA3_ERR_DEVICE
+
+
+# ---- RoPE options (sa3attn_forward_general) ------------------------------------------
+
+def _rope(pairing=0, rotary_dim=64):
+    return sa3._Rope(pairing, rotary_dim)
+
+
+def _call_general(lib, st=None, rope=None, **kw):
+    return lib.sa3attn_forward_general(ctypes.byref(_desc(**kw)), ctypes.byref(st) if st is not None else None,
+                                       ctypes.byref(rope) if rope is not None else None)
+
+
+@pytest.mark.parametrize("pairing,rd", [(2, 64), (-1, 64), (0, 0), (0, 8), (1, 24), (1, 80), (0, 65), (1, -16)])
+def test_bad_rope_options_rejected(lib, pairing, rd):
+    assert _call_general(lib, rope=_rope(pairing, rd)) == SA3_ERR_ARG
+
+
+def test_general_form_validates_like_ex(lib):
+    assert lib.sa3attn_forward_general(None, None, None) == SA3_ERR_NULL
+    assert _call_general(lib, rope=_rope(1, 32), q=ctypes.c_void_p(0)) == SA3_ERR_NULL
+    assert _call_general(lib, rope=_rope(1, 32), D=128) == SA3_ERR_UNSUPPORTED
+    assert _call_general(lib, st=_strides(q=(0, 0, 60)), rope=_rope(1, 32)) == SA3_ERR_ARG
+
+
+def test_partial_rotary_table_extent_in_overlap_check(lib):
+    # a [L][R/2] table of R = 32 is L * 16 floats: out right after it is no overlap,
+    # out inside it is
+    base = _fake(9).value
+    tab = 64 * 16 * 4
+    assert _call_general(lib, rope=_rope(0, 32), cos=ctypes.c_void_p(base),
+                         out=ctypes.c_void_p(base + tab - 16)) == SA3_ERR_ARG
+
+
+@pytest.mark.skipif(_gpu_present(), reason="placeholder pointers must never reach a real GPU")
+def test_valid_general_calls_without_gpu_report_device_error(lib):
+    assert _call_general(lib) == SA3_ERR_DEVICE
+    for pairing in (0, 1):
+        for rd in (16, 32, 48, 64):
+            assert _call_general(lib, rope=_rope(pairing, rd)) == SA3_ERR_DEVICE
+            assert _call_general(lib, st=_strides(layout="blhd"), rope=_rope(pairing, rd), differential=1) == \
+                SA3_ERR_DEVICE
+    base = _fake(9).value
+    assert _call_general(lib, rope=_rope(0, 32), cos=ctypes.c_void_p(base),
+                         out=ctypes.c_void_p(base + 64 * 16 * 4)) == SA3_ERR_DEVICE
