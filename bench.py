@@ -39,6 +39,8 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 WARM_S = 0.3                 # minimum warmup time per timed configuration
 HEAD_CONFIG = "dit_long"
 OTHER_CONFIGS = ["tiny", "dit_short", "dit_2min", "dit_2min_prime", "samel_swa", "samel_w17", "dit_medium_diff"]
+COLD_CONFIGS = {"tiny", "dit_short", "samel_swa", "samel_w17"}   # HBM/latency-bound: also timed cold
+FLUSH_MB = 512                     # larger than the 256 MB MALL plus the L2s
 GRAPH_LENGTHS = [1, 16, 64, 256]   # short-latent sequences captured as one graph of N calls
 GRAPH_CALLS = [96, 40]             # fused attention calls per forward: medium and small DiT
 KERNEL_SOURCE = os.path.join(ROOT, "rope_attention_core_amd", "csrc", "attn_fwd.hip")
@@ -139,6 +141,24 @@ class Bench:
                 "ms_min": per[0], "ms_max": per[-1], "wall_s": wall}
 
 
+def cold_ms(torch, b, reps=7):
+    """Median ms of single calls, each after writing a FLUSH_MB buffer so that no input
+    is left in the L2s or the MALL (the flush is outside the timed event pair)."""
+    flush = torch.empty(FLUSH_MB * (1 << 20) // 4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    times = []
+    for _ in range(reps):
+        flush.fill_(1.0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        b.call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del flush
+    return sorted(times)[len(times) // 2]
+
+
 def graph_per_call_us(torch, fn, n_calls, replays=20):
     """Capture n_calls of fn() into one graph; time replays back to back; us per call."""
     s = torch.cuda.Stream()
@@ -210,7 +230,18 @@ def cpu_baseline(cfg, inputs, budget_s=12.0):
         if t_used >= budget_s:
             break
     per_head_flops = flops(cfg) / (cfg.B * cfg.H)
-    threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    info = threadpool_info()
+    threads = max((p.get("num_threads", 1) for p in info), default=1)
+    blas = ",".join(sorted({f"{p.get('internal_api', '?')} {p.get('version', '')}".strip() for p in info})) or "none"
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": round(per_head_flops * done / t_used / 1e12, 6),
         "unit": "TFLOP/s",
@@ -218,6 +249,8 @@ def cpu_baseline(cfg, inputs, budget_s=12.0):
         "kind": "oracle",
         "sample": f"{done} of {len(heads)} (b,h) heads of {cfg.name}, full output, numpy fp64 method mode; "
                   f"{t_used:.1f} s; ms/call extrapolated {t_used / done * len(heads) * 1e3:.0f}",
+        "cpu": cpu_model,
+        "blas": blas,
     }
 
 
@@ -303,6 +336,10 @@ def main():
                 "frac_mfma_peak": round(f / (r["ms_mean"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                 "gbs_compulsory": round(compulsory_bytes(c) / (r["ms_mean"] * 1e-3) / 1e9, 1),
             }
+            if name in COLD_CONFIGS:
+                cm = cold_ms(torch, b)
+                per_config[name]["ms_cold_median"] = round(cm, 5)
+                per_config[name]["gbs_compulsory_cold"] = round(compulsory_bytes(c) / (cm * 1e-3) / 1e9, 1)
             del b
         torch.cuda.empty_cache()
     graphs = None if args.no_configs else short_graphs(torch, sa3, synth)

@@ -49,12 +49,12 @@ struct NarrowShape {
 };
 
 // Windowed mode keeps registers <= 168 so that three workgroups share a CU (their LDS
-// fits too); short-sequence mode and the general instances may use up to 256 (512 for
-// the general 256-key span).
+// fits too); short-sequence mode and the general instances may use up to 256, and the
+// 256-key span of the differential or general instances up to 512.
 // CONTIG: contiguous [B][H][L][64] tensors (q, k stacked [2][...]); the row strides
 // are then compile-time constants.
 template <int IO, bool DIFF, int NKF, bool CONTIG>
-__global__ __launch_bounds__(256, CONTIG ? (NKF ? 2 : 3) : (NKF == 256 ? 1 : 2)) void attn_narrow_kernel(Params P) {
+__global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTIG && !NKF) ? 3 : 2) void attn_narrow_kernel(Params P) {
     using S = NarrowShape<DIFF, NKF>;
     constexpr int NT = S::NT, NBS = S::NBS, WPB = S::WPB, BM = S::BM, NK = S::NK, NKB = S::NKB;
     constexpr int KC = NK * 8 / NT;          // K chunks (8 elements) per thread per branch

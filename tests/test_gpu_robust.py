@@ -31,7 +31,8 @@ def _fwd(cfg, q, k, v, **kw):
 
 
 @pytest.mark.parametrize("name,kw", [("dit_2min", {}), ("dit_long", dict(H=4, L=2048)),
-                                     ("samel_swa", dict(H=3, L=2500))])
+                                     ("samel_swa", dict(H=3, L=2500)), ("samel_w17", dict(H=3, L=3000)),
+                                     ("dit_short", {})])
 def test_bitwise_run_to_run_determinism(name, kw):
     cfg = synth.config(name, **kw)
     _, q, k, v = _dev_inputs(cfg)
@@ -100,7 +101,11 @@ def _embed(t, pad_elems):
 
 
 @pytest.mark.parametrize("name,kw", [("dit_2min", dict(H=3, L=1291)), ("samel_swa", dict(H=2, L=1000)),
-                                     ("dit_long", dict(H=2, L=333))])
+                                     ("dit_long", dict(H=2, L=333)),
+                                     # the narrow-window kernel stages keys from q0 - w, before
+                                     # the slab for the first block: the guard must not leak in
+                                     ("samel_w17", dict(H=2, L=1000)), ("dit_2min", dict(H=2, L=500, window=5)),
+                                     ("dit_short", dict(L=200)), ("samel_swa", dict(H=2, L=100))])
 def test_nan_guard_bands(name, kw):
     """Inputs and output embedded in NaN-poisoned buffers: results unchanged, guards intact."""
     torch = G.torch_mod()
@@ -127,7 +132,8 @@ def test_nan_guard_bands(name, kw):
     assert torch.isnan(oflat[:pad]).all() and torch.isnan(oflat[pad + clean.numel():]).all()
 
 
-@pytest.mark.parametrize("name,kw", [("dit_short", {}), ("samel_swa", dict(H=2, L=700))])
+@pytest.mark.parametrize("name,kw", [("dit_short", {}), ("samel_swa", dict(H=2, L=700)),
+                                     ("samel_w17", dict(H=2, L=900))])
 def test_graph_capture_replays_match_eager(name, kw):
     torch = G.torch_mod()
     cfg = synth.config(name, **kw)
