@@ -38,7 +38,8 @@ PEAK_BF16_TFLOPS = 2516.6    # MI355X dense FP16/BF16 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 WARM_S = 0.3                 # minimum warmup time per timed configuration
 HEAD_CONFIG = "dit_long"
-OTHER_CONFIGS = ["tiny", "dit_short", "dit_2min", "dit_2min_prime", "samel_swa", "samel_w17", "dit_medium_diff"]
+OTHER_CONFIGS = ["tiny", "dit_short", "dit_2min", "dit_2min_prime", "samel_swa", "samel_w17", "dit_medium_diff",
+                 "dit_long_d128"]
 COLD_CONFIGS = {"tiny", "dit_short", "samel_swa", "samel_w17"}   # HBM/latency-bound: also timed cold
 FLUSH_MB = 512                     # larger than the 256 MB MALL plus the L2s
 GRAPH_LENGTHS = [1, 16, 64, 256]   # short-latent sequences captured as one graph of N calls

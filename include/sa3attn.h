@@ -47,8 +47,9 @@
  *    `out` is untouched. Status codes are below; sa3attn_status_string() names them.
  *  - Thread safety: calls may be made from several threads; the only shared state
  *    is a per-device capability cache filled once.
- *  - Supported: D = 64, IO dtype fp16 or bf16, out dtype fp16, bf16 or fp32,
- *    1 <= L <= 16777216, and grid size (ceil(L/tile) * B * H) below 2^31.
+ *  - Supported: D = 64 or 128, IO dtype fp16 or bf16, out dtype fp16, bf16 or
+ *    fp32, 1 <= L <= 2^30 / D (16777216 at D = 64), and grid size
+ *    (ceil(L/tile) * B * H) below 2^31.
  *  - Numerics: QK^T and P.V run on MFMA with FP32 accumulation; the running
  *    softmax max and sum are FP32. P is rounded to fp16 before P.V for both IO
  *    dtypes; with bf16 inputs V is converted to fp16 as it is staged, which is
@@ -63,14 +64,14 @@ extern "C" {
 #endif
 
 #define SA3ATTN_VERSION_MAJOR 0
-#define SA3ATTN_VERSION_MINOR 3
+#define SA3ATTN_VERSION_MINOR 4
 
 /* Status codes. */
 enum {
     SA3_OK = 0,
     SA3_ERR_NULL = -1,         /* a required pointer is NULL                          */
     SA3_ERR_SHAPE = -2,        /* B, H, L or D < 1, D odd, or a size overflows        */
-    SA3_ERR_UNSUPPORTED = -3,  /* D != 64, or an unknown dtype                         */
+    SA3_ERR_UNSUPPORTED = -3,  /* D not 64 or 128, or an unknown dtype                 */
     SA3_ERR_ARG = -4,          /* non-finite scale or lambda, out overlaps an input,
                                   a misaligned pointer, or unusable strides           */
     SA3_ERR_DEVICE = -5,       /* no HIP device, or the current device is not gfx950  */
@@ -132,7 +133,7 @@ int sa3attn_forward_ex(const sa3attn_desc *desc);
  * {L*H*D, D, H*D}; sa3attn_forward_ex is this call with contiguous [B][H][L][D]
  * strides {H*L*D, L*D, D} and branch strides B*H*L*D.
  * Requirements (SA3_ERR_ARG otherwise, before anything is enqueued): every stride
- * >= 0 and a multiple of 8 elements; the l stride >= 64; (L + 128) * l stride * 2
+ * >= 0 and a multiple of 8 elements; the l stride >= D; (L + 128) * l stride * 2
  * < 2^32 for q, k, v and out; the output view gives every (b, h, l) its own row;
  * out overlaps no input. Inputs may alias each other (they are only read).
  * A NULL strides pointer returns SA3_ERR_NULL. The strides are copied; the

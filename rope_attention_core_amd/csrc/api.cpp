@@ -50,12 +50,12 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Bytes from the first to one past the last element a [B][H][L][64] view with element
+// Bytes from the first to one past the last element a [B][H][L][D] view with element
 // strides s = {b, h, l} (d contiguous) can touch; non-negative strides.
-unsigned long long extent_bytes(const long long s[3], int B, int H, int L, int elem) {
+unsigned long long extent_bytes(const long long s[3], int B, int H, int L, int D, int elem) {
     const unsigned long long last = (unsigned long long)(B - 1) * (unsigned long long)s[0] +
                                     (unsigned long long)(H - 1) * (unsigned long long)s[1] +
-                                    (unsigned long long)(L - 1) * (unsigned long long)s[2] + 64ull;
+                                    (unsigned long long)(L - 1) * (unsigned long long)s[2] + (unsigned long long)D;
     return last * (unsigned long long)elem;
 }
 
@@ -63,16 +63,16 @@ unsigned long long extent_bytes(const long long s[3], int B, int H, int L, int e
 // a position stride of at least one row, and 32-bit row offsets: the kernels read up
 // to 64 rows past either end of a slab and rely on those offsets (negative ones wrap
 // modulo 2^32) landing at or above the slab's buffer range, which then reads zeros.
-bool strides_ok(const long long s[3], int L) {
+bool strides_ok(const long long s[3], int L, int D) {
     for (int i = 0; i < 3; ++i)
         if (s[i] < 0 || (s[i] & 7) != 0 || s[i] > (1ll << 40)) return false;
-    if (s[2] < 64) return false;
+    if (s[2] < D) return false;
     return (unsigned long long)(L + 128) * (unsigned long long)s[2] * 2ull < (1ull << 32);
 }
 
-// The output view maps every (b, h, l) row to its own 64 elements: with the dimensions
+// The output view maps every (b, h, l) row to its own D elements: with the dimensions
 // of size > 1 sorted by stride, each stride is at least the span of the ones inside it.
-bool rows_distinct(const long long s[3], int B, int H, int L) {
+bool rows_distinct(const long long s[3], int B, int H, int L, int D) {
     long long st[3] = {s[0], s[1], s[2]};
     long long n[3] = {B, H, L};
     for (int i = 0; i < 3; ++i)
@@ -84,7 +84,7 @@ bool rows_distinct(const long long s[3], int B, int H, int L) {
                 st[j] = a;
                 n[j] = b;
             }
-    long long span = 64;
+    long long span = D;
     for (int i = 0; i < 3; ++i) {
         if (n[i] == 1) continue;
         if (st[i] < span) return false;
@@ -98,7 +98,8 @@ int forward_impl(const sa3attn_desc *d, const sa3attn_strides *sp, const sa3attn
     if (!d->q || !d->k || !d->v || !d->cos || !d->sin || !d->out) return SA3_ERR_NULL;
     if (d->B < 1 || d->H < 1 || d->L < 1 || d->D < 1 || (d->D & 1)) return SA3_ERR_SHAPE;
     if (d->L > kMaxL) return SA3_ERR_SHAPE;
-    if (d->D != 64) return SA3_ERR_UNSUPPORTED;
+    if (d->D != 64 && d->D != 128) return SA3_ERR_UNSUPPORTED;
+    if ((long long)d->L * d->D > (1ll << 30)) return SA3_ERR_SHAPE;   // 32-bit row offsets
     if (d->dtype != SA3_F16 && d->dtype != SA3_BF16) return SA3_ERR_UNSUPPORTED;
     if (d->out_dtype != SA3_F16 && d->out_dtype != SA3_BF16 && d->out_dtype != SA3_F32)
         return SA3_ERR_UNSUPPORTED;
@@ -106,23 +107,24 @@ int forward_impl(const sa3attn_desc *d, const sa3attn_strides *sp, const sa3attn
     if (!std::isfinite(d->scale) || !std::isfinite(d->lambda)) return SA3_ERR_ARG;
 
     const unsigned long long bh = (unsigned long long)d->B * (unsigned long long)d->H;
-    const unsigned long long elems = bh * (unsigned long long)d->L * 64ull;
+    const unsigned long long elems = bh * (unsigned long long)d->L * (unsigned long long)d->D;
     if (bh > (1ull << 31) || elems > (1ull << 56)) return SA3_ERR_SHAPE;
 
-    // strides: given, or those of contiguous [B][H][L][64] (q, k stacked [2][...])
+    // strides: given, or those of contiguous [B][H][L][D] (q, k stacked [2][...])
     sa3attn_strides s;
     if (sp) {
         s = *sp;
     } else {
-        const long long c[3] = {(long long)d->H * d->L * 64, (long long)d->L * 64, 64};
+        const long long c[3] = {(long long)d->H * d->L * d->D, (long long)d->L * d->D, d->D};
         for (int i = 0; i < 3; ++i) s.q[i] = s.k[i] = s.v[i] = s.out[i] = c[i];
         s.q_branch = s.k_branch = (long long)elems;
     }
-    if (!strides_ok(s.q, d->L) || !strides_ok(s.k, d->L) || !strides_ok(s.v, d->L) || !strides_ok(s.out, d->L))
+    if (!strides_ok(s.q, d->L, d->D) || !strides_ok(s.k, d->L, d->D) || !strides_ok(s.v, d->L, d->D) ||
+        !strides_ok(s.out, d->L, d->D))
         return SA3_ERR_ARG;
     if (d->differential && (s.q_branch < 0 || (s.q_branch & 7) || s.k_branch < 0 || (s.k_branch & 7)))
         return SA3_ERR_ARG;
-    if (!rows_distinct(s.out, d->B, d->H, d->L)) return SA3_ERR_ARG;
+    if (!rows_distinct(s.out, d->B, d->H, d->L, d->D)) return SA3_ERR_ARG;
     // RoPE options: adjacent or half-split pairs over the leading R dims
     const int pairing = rp ? rp->pairing : SA3_ROPE_ADJACENT;
     const int rot_dim = rp ? rp->rotary_dim : d->D;
@@ -134,12 +136,12 @@ int forward_impl(const sa3attn_desc *d, const sa3attn_strides *sp, const sa3attn
 
     // out must not overlap any input (byte ranges the views can reach)
     const int osz = d->out_dtype == SA3_F32 ? 4 : 2;
-    const size_t out_bytes = (size_t)extent_bytes(s.out, d->B, d->H, d->L, osz);
-    const size_t q_bytes = (size_t)(extent_bytes(s.q, d->B, d->H, d->L, 2) +
+    const size_t out_bytes = (size_t)extent_bytes(s.out, d->B, d->H, d->L, d->D, osz);
+    const size_t q_bytes = (size_t)(extent_bytes(s.q, d->B, d->H, d->L, d->D, 2) +
                                     (d->differential ? (unsigned long long)s.q_branch * 2ull : 0ull));
-    const size_t k_bytes = (size_t)(extent_bytes(s.k, d->B, d->H, d->L, 2) +
+    const size_t k_bytes = (size_t)(extent_bytes(s.k, d->B, d->H, d->L, d->D, 2) +
                                     (d->differential ? (unsigned long long)s.k_branch * 2ull : 0ull));
-    const size_t v_bytes = (size_t)extent_bytes(s.v, d->B, d->H, d->L, 2);
+    const size_t v_bytes = (size_t)extent_bytes(s.v, d->B, d->H, d->L, d->D, 2);
     const size_t tab_bytes = (size_t)d->L * (size_t)(rot_dim / 2) * sizeof(float);
     if (overlaps(d->out, out_bytes, d->q, q_bytes) || overlaps(d->out, out_bytes, d->k, k_bytes) ||
         overlaps(d->out, out_bytes, d->v, v_bytes) || overlaps(d->out, out_bytes, d->cos, tab_bytes) ||
@@ -162,7 +164,7 @@ int forward_impl(const sa3attn_desc *d, const sa3attn_strides *sp, const sa3attn
     a.q_br = s.q_branch;
     a.k_br = s.k_branch;
     {
-        const long long c[3] = {(long long)d->H * d->L * 64, (long long)d->L * 64, 64};
+        const long long c[3] = {(long long)d->H * d->L * d->D, (long long)d->L * d->D, d->D};
         bool contig = true;
         for (int i = 0; i < 3; ++i)
             contig = contig && s.q[i] == c[i] && s.k[i] == c[i] && s.v[i] == c[i] && s.out[i] == c[i];
@@ -175,6 +177,7 @@ int forward_impl(const sa3attn_desc *d, const sa3attn_strides *sp, const sa3attn
     a.B = d->B;
     a.H = d->H;
     a.L = d->L;
+    a.D = d->D;
     // a window reaching every key is full attention: |i - j| <= L - 1 always holds
     a.window = (d->window < 0 || d->window >= d->L - 1) ? -1 : d->window;
     a.lam = d->lambda;
@@ -251,7 +254,7 @@ const char *sa3attn_status_string(int status) {
         case SA3_OK: return "SA3_OK";
         case SA3_ERR_NULL: return "SA3_ERR_NULL: a required pointer is NULL";
         case SA3_ERR_SHAPE: return "SA3_ERR_SHAPE: B, H, L or D out of range, D odd, or a size overflows";
-        case SA3_ERR_UNSUPPORTED: return "SA3_ERR_UNSUPPORTED: head dim or dtype not supported";
+        case SA3_ERR_UNSUPPORTED: return "SA3_ERR_UNSUPPORTED: head dim (64 or 128) or dtype not supported";
         case SA3_ERR_ARG:
             return "SA3_ERR_ARG: non-finite scale or lambda, out overlaps an input, a misaligned pointer, "
                    "or unusable strides";

@@ -231,8 +231,9 @@ __device__ __forceinline__ float pair_sum(float x) {
 // last row's 128 bytes end the range, so rows >= L (and negative rows, whose 32-bit
 // offsets wrap far above it) read as zeros.
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes);
-__device__ __forceinline__ rsrc_t slab_rsrc(const uint16_t *base, long long elems, uint32_t rowb, int L) {
-    return make_rsrc(base + elems, (uint32_t)(L - 1) * rowb + (uint32_t)ROWB);
+__device__ __forceinline__ rsrc_t slab_rsrc(const uint16_t *base, long long elems, uint32_t rowb, int L,
+                                            uint32_t rowbytes = ROWB) {
+    return make_rsrc(base + elems, (uint32_t)(L - 1) * rowb + rowbytes);
 }
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, (int)RSRC_WORD3);

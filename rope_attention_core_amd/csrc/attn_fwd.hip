@@ -53,33 +53,48 @@
 namespace sa3 {
 namespace {
 
+template <int NDB>
 struct Branch {
-    f32x16 o[2];     // O^T accumulators for d in [0, 32) and [32, 64)
+    f32x16 o[NDB];   // O^T accumulators for d in [32 db, 32 db + 32)
     float l;         // this lane's partial FP32 sum of P (its 16 keys of each 32)
     float m;         // exponent base in log2 units (-inf: no valid key yet)
     float a;         // factor taking O and l from the previous base to m
 };
 
-// One workgroup = 8 waves (two per SIMD, registers <= 256 per wave). Plain: each wave
-// owns 32 query rows, BM = 256. Differential: waves w and w + 4 own the same 32 rows,
-// wave w the first softmax branch (Q1, K1) and wave w + 4 the second (Q2, K2); both
-// multiply the same staged V tile, BM = 128, and the second branch hands O2 / l2 to the
-// first through LDS at the end.
-// CONTIG: q, k, v and out are contiguous [B][H][L][64] (q, k stacked [2][...]); the row
-// strides are then compile-time constants, which keeps scalar registers free.
-template <int IO, bool DIFF, bool CONTIG>
-__global__ __launch_bounds__(512, 2) void attn_fwd_kernel(Params P) {
-    constexpr int NW = 8;
+// Waves per workgroup: D = 64 runs 8 waves (two per SIMD, registers <= 256 per wave);
+// D = 128 doubles the O accumulator and the rotated Q a wave keeps, so it runs 4 waves
+// (one per SIMD) with the whole 512-entry register file of a lane each.
+template <int D>
+constexpr int waves_for() { return D == 128 ? 4 : 8; }
+
+// Plain: each wave owns 32 query rows, BM = 32 x waves. Differential: waves w and
+// w + waves/2 own the same 32 rows, wave w the first softmax branch (Q1, K1) and the
+// other the second (Q2, K2); both multiply the same staged V tile, BM = 16 x waves, and
+// the second branch hands O2 / l2 to the first through LDS at the end.
+// CONTIG: q, k, v and out are contiguous [B][H][L][D] (q, k stacked [2][...]) with the
+// default RoPE; the row strides are then compile-time constants, which keeps scalar
+// registers free. D: head dim, 64 or 128.
+template <int IO, bool DIFF, bool CONTIG, int D>
+__global__ __launch_bounds__(waves_for<D>() * 64, 8 / waves_for<D>()) void attn_fwd_kernel(Params P) {
+    constexpr int NW = waves_for<D>();
     constexpr int NT = NW * 64;
     constexpr int NBS = DIFF ? 2 : 1;        // K tiles staged per key tile (one per branch)
     constexpr int WPB = NW / NBS;            // waves (32-row query blocks) per branch
     constexpr int BM = WPB * 32;
-    constexpr int VD = 4096 / (2 * NT);      // d values per thread in the V^T staging (2 keys each)
-    static_assert(VD == 4, "staging layout assumes 512 threads");
-    constexpr int KS_ELEMS = BN * KS_STRIDE;
-    constexpr int VT_ELEMS = HD * VT_STRIDE;
+    constexpr int RB = D * 2;                // bytes per q/k/v row, and per default cos/sin row
+    constexpr int CPR = D / 8;               // 16-byte chunks per row
+    constexpr int KC = BN * CPR / NT;        // K chunks per thread per branch
+    constexpr int NKS = D / 16;              // MFMA k-steps of QK^T
+    constexpr int NDB = D / 32;              // 32-wide d blocks of O
+    constexpr int KSTR = D + 8;              // LDS row stride of the K tile (16-bit elements)
+    constexpr int VD = BN * D / (2 * NT);    // d values per thread in the V^T staging (2 keys each)
+    static_assert((D == 64 || D == 128) && KC >= 1 && (VD == 4 || VD % 8 == 0), "head dim 64 or 128");
+    using vraw_t = std::conditional_t<VD >= 8, u32x4, u32x2>;
+    constexpr int NV = VD >= 8 ? VD / 8 : 1;     // V loads per key of a thread
+    constexpr int KS_ELEMS = BN * KSTR;
+    constexpr int VT_ELEMS = D * VT_STRIDE;
     constexpr int BUF_ELEMS = NBS * KS_ELEMS + VT_ELEMS;
-    static_assert(!DIFF || NBUF * BUF_ELEMS * 2 >= WPB * 32 * 64 * 4, "LDS too small for the O2 exchange");
+    static_assert(!DIFF || NBUF * BUF_ELEMS * 2 >= WPB * 32 * D * 4, "LDS too small for the O2 exchange");
     __shared__ __attribute__((aligned(16))) uint16_t smem[NBUF * BUF_ELEMS];
 
     const float NEG_INF = -__builtin_inff();
@@ -103,21 +118,21 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(Params P) {
     const int qt = lid - bh * P.n_qtiles;
 
     const int bb = bh / P.H, hh = bh - bb * P.H;
-    const uint32_t qrb = CONTIG ? (uint32_t)ROWB : P.q_rowb;
-    const uint32_t krb = CONTIG ? (uint32_t)ROWB : P.k_rowb;
-    const uint32_t vrb = CONTIG ? (uint32_t)ROWB : P.v_rowb;
-    const long long slab = (long long)bh * L * HD;   // contiguous offset of this (b, h)
-    // contiguous stacked branches are B*H*L*64 elements apart (B*H = workgroups / tiles)
-    const long long qbr = CONTIG ? (long long)(nblk / P.n_qtiles) * L * HD : P.q_br;
+    const uint32_t qrb = CONTIG ? (uint32_t)RB : P.q_rowb;
+    const uint32_t krb = CONTIG ? (uint32_t)RB : P.k_rowb;
+    const uint32_t vrb = CONTIG ? (uint32_t)RB : P.v_rowb;
+    const long long slab = (long long)bh * L * D;   // contiguous offset of this (b, h)
+    // contiguous stacked branches are B*H*L*D elements apart (B*H = workgroups / tiles)
+    const long long qbr = CONTIG ? (long long)(nblk / P.n_qtiles) * L * D : P.q_br;
     const long long kbr = CONTIG ? qbr : P.k_br;
     rsrc_t rk[NBS];
 #pragma unroll
     for (int br = 0; br < NBS; ++br)
-        rk[br] = slab_rsrc(P.k, br * kbr + (CONTIG ? slab : bb * P.kb + hh * P.kh), krb, L);
-    const rsrc_t rq = slab_rsrc(P.q, wbr * qbr + (CONTIG ? slab : bb * P.qb + hh * P.qh), qrb, L);
-    const rsrc_t rv = slab_rsrc(P.v, CONTIG ? slab : bb * P.vb + hh * P.vh, vrb, L);
-    // cos/sin: [L][R/2] floats (R = 64 in the contiguous instances: 128 bytes per row)
-    const uint32_t trb = CONTIG ? (uint32_t)ROWB : P.tab_rowb;
+        rk[br] = slab_rsrc(P.k, br * kbr + (CONTIG ? slab : bb * P.kb + hh * P.kh), krb, L, RB);
+    const rsrc_t rq = slab_rsrc(P.q, wbr * qbr + (CONTIG ? slab : bb * P.qb + hh * P.qh), qrb, L, RB);
+    const rsrc_t rv = slab_rsrc(P.v, CONTIG ? slab : bb * P.vb + hh * P.vh, vrb, L, RB);
+    // cos/sin: [L][R/2] floats (R = D in the contiguous instances: 2 D bytes per row)
+    const uint32_t trb = CONTIG ? (uint32_t)RB : P.tab_rowb;
     const rsrc_t rc = make_rsrc(P.cos, (uint32_t)L * trb);
     const rsrc_t rs = make_rsrc(P.sin, (uint32_t)L * trb);
     const int rhalf = P.rope_half, rdim = P.rot_dim;
@@ -127,15 +142,15 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(Params P) {
     const int qw = q0 + wq * 32;
 
     // ---- Q: rotate once into registers (MFMA B-operand layout) -------------------
-    u32x4 qreg[4];
+    u32x4 qreg[NKS];
     const uint32_t qsign = P.neg_scale ? 0x80008000u : 0u;
     {
         const uint32_t row = (uint32_t)(qw + r);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+        for (int ks = 0; ks < NKS; ++ks) {
             const uint32_t col = (uint32_t)(16 * ks + 8 * g) * 2;
             if constexpr (CONTIG) {
-                const uint32_t offc = row * ROWB + col;
+                const uint32_t offc = row * RB + col;
                 qreg[ks] = rope8<IO>(bload(rq, row * qrb + col), bload(rc, offc), bload(rs, offc)) ^ qsign;
             } else {
                 const RopeChunk rc8 = rope_chunk(2 * ks + g, rhalf, rdim);
@@ -159,63 +174,78 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(Params P) {
     const int t_end = (k_hi + BN - 1) / BN;
 
     // ---- staging: global -> registers -> (rotate / transpose) -> LDS -------------
-    // K (each branch): 512 chunks of 8 elements; thread tid -> key tid / 8, d0 = 8 * (tid % 8).
-    // V: thread -> keys 2p, 2p+1 (p = tid % 32) and 4 values of d from 4 * (tid / 32).
+    // K (each branch): 64 rows x CPR chunks of 8 elements; chunk item i of a thread is
+    // row (tid / CPR) + i * NT / CPR, dims 8 (tid % CPR) .. +7.
+    // V: thread -> keys 2p, 2p+1 (p = tid % 32) and VD values of d from VD * (tid / 32).
     const int vp = tid & 31;
     const int vd0 = (tid >> 5) * VD;
-    u32x4 rawk[NBS], rawc, raws;
-    u32x4 rawp[NBS], rawc1, raws1;   // general instances: partner chunks, table floats 4-7
-    u32x2 rawv[2];
+    u32x4 rawk[NBS][KC], rawc[KC], raws[KC];
+    u32x4 rawp[NBS][KC], rawc1[KC], raws1[KC];   // general instances: partner chunks, table floats 4-7
+    vraw_t rawv[2][NV];
 
     // per-lane parts of the staging offsets (one multiply each, here); the per-tile part
-    // k0 * row bytes is wave-uniform and comes from the scalar unit
-    const RopeChunk kch = rope_chunk(tid & 7, rhalf, rdim);
-    const uint32_t kl = (uint32_t)(tid >> 3) * krb + (uint32_t)(tid & 7) * 16;
-    const uint32_t kpl = (uint32_t)(tid >> 3) * krb + (uint32_t)kch.partner * 16;
-    const uint32_t cl = CONTIG ? (uint32_t)(tid >> 3) * ROWB + (uint32_t)(tid & 7) * 16
-                               : (uint32_t)(tid >> 3) * trb + kch.toff;
+    // (k0 + i * NT / CPR) * row bytes is wave-uniform and comes from the scalar unit
+    const RopeChunk kch = rope_chunk(tid % CPR, rhalf, rdim);
+    const uint32_t kl = (uint32_t)(tid / CPR) * krb + (uint32_t)(tid % CPR) * 16;
+    const uint32_t kpl = (uint32_t)(tid / CPR) * krb + (uint32_t)kch.partner * 16;
+    const uint32_t cl = CONTIG ? (uint32_t)(tid / CPR) * RB + (uint32_t)(tid % CPR) * 16
+                               : (uint32_t)(tid / CPR) * trb + kch.toff;
     const uint32_t vl = (uint32_t)(2 * vp) * vrb + (uint32_t)vd0 * 2;
     auto load_raw = [&](int t) __attribute__((always_inline)) {
-        const uint32_t k0 = (uint32_t)(t * BN);
 #pragma unroll
-        for (int br = 0; br < NBS; ++br) rawk[br] = bload(rk[br], kl + k0 * krb);
-        if constexpr (CONTIG) {
-            rawc = bload(rc, cl + k0 * ROWB);
-            raws = bload(rs, cl + k0 * ROWB);
-        } else {
-            const uint32_t to = kch.mode ? cl + k0 * trb : NOWHERE;
-            const uint32_t t1 = kch.mode >= 2 ? to + 16 : NOWHERE;
-            const uint32_t po = kch.mode >= 2 ? kpl + k0 * krb : NOWHERE;
+        for (int i = 0; i < KC; ++i) {
+            const uint32_t k0 = (uint32_t)(t * BN + i * (NT / CPR));
 #pragma unroll
-            for (int br = 0; br < NBS; ++br) rawp[br] = bload(rk[br], po);
-            rawc = bload(rc, to);
-            raws = bload(rs, to);
-            rawc1 = bload(rc, t1);
-            raws1 = bload(rs, t1);
+            for (int br = 0; br < NBS; ++br) rawk[br][i] = bload(rk[br], kl + k0 * krb);
+            if constexpr (CONTIG) {
+                rawc[i] = bload(rc, cl + k0 * RB);
+                raws[i] = bload(rs, cl + k0 * RB);
+            } else {
+                const uint32_t to = kch.mode ? cl + k0 * trb : NOWHERE;
+                const uint32_t t1 = kch.mode >= 2 ? to + 16 : NOWHERE;
+                const uint32_t po = kch.mode >= 2 ? kpl + k0 * krb : NOWHERE;
+#pragma unroll
+                for (int br = 0; br < NBS; ++br) rawp[br][i] = bload(rk[br], po);
+                rawc[i] = bload(rc, to);
+                raws[i] = bload(rs, to);
+                rawc1[i] = bload(rc, t1);
+                raws1[i] = bload(rs, t1);
+            }
         }
-        rawv[0] = bload8(rv, vl + k0 * vrb);
-        rawv[1] = bload8(rv, vl + k0 * vrb + vrb);
+        const uint32_t k0 = (uint32_t)(t * BN);
+        if constexpr (VD >= 8) {
+#pragma unroll
+            for (int n = 0; n < NV; ++n) {
+                rawv[0][n] = bload(rv, vl + k0 * vrb + 16 * n);
+                rawv[1][n] = bload(rv, vl + k0 * vrb + vrb + 16 * n);
+            }
+        } else {
+            rawv[0][0] = bload8(rv, vl + k0 * vrb);
+            rawv[1][0] = bload8(rv, vl + k0 * vrb + vrb);
+        }
     };
 
     // V^T key positions: bits 2 and 3 of the key index swapped, so that the 8 keys one
     // lane multiplies in a P.V step (see load_v_operands) are contiguous.
     const int vpos = (2 * vp & ~12) | ((2 * vp & 4) << 1) | ((2 * vp & 8) >> 1);
-    const int kat = (tid >> 3) * KS_STRIDE + (tid & 7) * 8;
+    const int kat = (tid / CPR) * KSTR + (tid % CPR) * 8;
     auto stage = [&](int buf) __attribute__((always_inline)) {
         uint16_t *Ks = smem + buf * BUF_ELEMS;
         uint16_t *Vt = Ks + NBS * KS_ELEMS;
 #pragma unroll
-        for (int br = 0; br < NBS; ++br) {
-            u32x4 rot;
-            if constexpr (CONTIG)
-                rot = rope8<IO>(rawk[br], rawc, raws);
-            else
-                rot = rope8_general<IO>(rawk[br], rawp[br], rawc, rawc1, raws, raws1, kch.mode);
-            *reinterpret_cast<u32x4 *>(Ks + br * KS_ELEMS + kat) = rot;
-        }
+        for (int i = 0; i < KC; ++i)
+#pragma unroll
+            for (int br = 0; br < NBS; ++br) {
+                u32x4 rot;
+                if constexpr (CONTIG)
+                    rot = rope8<IO>(rawk[br][i], rawc[i], raws[i]);
+                else
+                    rot = rope8_general<IO>(rawk[br][i], rawp[br][i], rawc[i], rawc1[i], raws[i], raws1[i], kch.mode);
+                *reinterpret_cast<u32x4 *>(Ks + br * KS_ELEMS + kat + i * (NT / CPR) * KSTR) = rot;
+            }
 #pragma unroll
         for (int j = 0; j < VD; ++j) {
-            const uint32_t wa = rawv[0][j >> 1], wb = rawv[1][j >> 1];
+            const uint32_t wa = rawv[0][j >> 3][(j >> 1) & 3], wb = rawv[1][j >> 3][(j >> 1) & 3];
             uint32_t w;
             if constexpr (IO == IO_BF16) {
                 const float fa = __uint_as_float((j & 1) ? (wa & 0xffff0000u) : (wa << 16));
@@ -234,19 +264,19 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(Params P) {
         const uint16_t *Ks = smem + buf * BUF_ELEMS + wbr * KS_ELEMS;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            u32x4 ka[4];
+            u32x4 ka[NKS];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) ka[ks] = lds16(Ks + (kb * 32 + r) * KS_STRIDE + 16 * ks + 8 * g);
+            for (int ks = 0; ks < NKS; ++ks) ka[ks] = lds16(Ks + (kb * 32 + r) * KSTR + 16 * ks + 8 * g);
             f32x16 acc = {};
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) acc = mfma_qk<IO>(ka[ks], qreg[ks], acc);
+            for (int ks = 0; ks < NKS; ++ks) acc = mfma_qk<IO>(ka[ks], qreg[ks], acc);
             s[kb] = acc;
         }
     };
 
-    Branch st;
-    st.o[0] = f32x16{};
-    st.o[1] = f32x16{};
+    Branch<NDB> st;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) st.o[db] = f32x16{};
     st.l = 0.0f;
     st.m = NEG_INF;
     st.a = 1.0f;
@@ -305,7 +335,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(Params P) {
         st.m = mn;
         const float nb = (mn == NEG_INF) ? 0.0f : -mn;
 #pragma unroll
-        for (int db = 0; db < 2; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int i = 0; i < 16; ++i) st.o[db][i] *= a;
         const uint16_t *Vt = smem + (t % NBUF) * BUF_ELEMS + NBS * KS_ELEMS;
@@ -317,7 +347,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(Params P) {
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                for (int db = 0; db < 2; ++db)
+                for (int db = 0; db < NDB; ++db)
                     st.o[db] = mfma_pv(lds16(Vt + (db * 32 + r) * VT_STRIDE + kb * 32 + 16 * tt + 8 * g), p[tt],
                                        st.o[db]);
         }
@@ -354,25 +384,25 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(Params P) {
         __syncthreads();
         if (wbr == 1) {
 #pragma unroll
-            for (int db = 0; db < 2; ++db)
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) xb[(wq * 32 + db * 16 + i) * 64 + lane] = st.o[db][i] * inv;
+                for (int i = 0; i < 16; ++i) xb[(wq * 16 * NDB + db * 16 + i) * 64 + lane] = st.o[db][i] * inv;
         }
         __syncthreads();
         if (wbr == 1) return;
     }
     if (qi >= L) return;
-    const long long row = CONTIG ? slab + (long long)qi * HD : bb * P.ob + hh * P.oh + (long long)qi * P.ol;
+    const long long row = CONTIG ? slab + (long long)qi * D : bb * P.ob + hh * P.oh + (long long)qi * P.ol;
     const float *xb = reinterpret_cast<const float *>(smem);
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int grp = 0; grp < 4; ++grp) {
             float o[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 o[j] = st.o[db][grp * 4 + j] * inv;
-                if constexpr (DIFF) o[j] = o[j] - P.lam * xb[(wq * 32 + db * 16 + grp * 4 + j) * 64 + lane];
+                if constexpr (DIFF) o[j] = o[j] - P.lam * xb[(wq * 16 * NDB + db * 16 + grp * 4 + j) * 64 + lane];
             }
             const int d = db * 32 + grp * 8 + g * 4;
             if (P.out_dtype == OUT_F32) {
@@ -387,45 +417,46 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_kernel(Params P) {
         }
 }
 
-template <int IO, bool DIFF, bool CONTIG>
+template <int IO, bool DIFF, bool CONTIG, int D>
 hipError_t launch(const LaunchArgs &a, int n_qtiles) {
     Params P = make_params(a);
     P.n_qtiles = n_qtiles;
     const unsigned grid = (unsigned)n_qtiles * (unsigned)a.B * (unsigned)a.H;
-    hipLaunchKernelGGL((attn_fwd_kernel<IO, DIFF, CONTIG>), dim3(grid), dim3(512), 0, static_cast<hipStream_t>(a.stream), P);
+    hipLaunchKernelGGL((attn_fwd_kernel<IO, DIFF, CONTIG, D>), dim3(grid), dim3(waves_for<D>() * 64), 0,
+                       static_cast<hipStream_t>(a.stream), P);
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const LaunchArgs &a, int n_qtiles) {
+    const bool bf = a.dtype == 1;
+    if (a.contig) {
+        if (a.diff) return bf ? launch<IO_BF16, true, true, D>(a, n_qtiles) : launch<IO_F16, true, true, D>(a, n_qtiles);
+        return bf ? launch<IO_BF16, false, true, D>(a, n_qtiles) : launch<IO_F16, false, true, D>(a, n_qtiles);
+    }
+    if (a.diff) return bf ? launch<IO_BF16, true, false, D>(a, n_qtiles) : launch<IO_F16, true, false, D>(a, n_qtiles);
+    return bf ? launch<IO_BF16, false, false, D>(a, n_qtiles) : launch<IO_F16, false, false, D>(a, n_qtiles);
 }
 
 }  // namespace
 
 // Sequences of at most 256 keys and windows of half-width <= 32 go to the single-span
-// kernel (attn_narrow.hip), which stages a query block's whole key span at once.
-bool use_narrow(const LaunchArgs &a) { return narrow_applies(a); }
+// kernel (attn_narrow.hip), which stages a query block's whole key span at once; it is
+// built for D = 64 only, so D = 128 always takes the long-span kernel.
+bool use_narrow(const LaunchArgs &a) { return a.D == 64 && narrow_applies(a); }
 
-// Query rows per workgroup: 256 (8 waves x 32) plain, 128 (4 pairs of waves) differential.
+// Query rows per workgroup: 32 per wave plain, 32 per pair of waves differential.
 int tile_rows(const LaunchArgs &a) {
     if (use_narrow(a)) return narrow_tile_rows(a);
-    return a.diff ? 128 : 256;
+    const int nw = a.D == 128 ? waves_for<128>() : waves_for<64>();
+    return a.diff ? nw * 16 : nw * 32;
 }
 
 int launch_forward(const LaunchArgs &a) {
     if (use_narrow(a)) return launch_narrow(a);
     const int bm = tile_rows(a);
     const int n_qtiles = (a.L + bm - 1) / bm;
-    const bool bf = a.dtype == 1;
-    hipError_t e;
-    if (a.contig) {
-        if (a.diff)
-            e = bf ? launch<IO_BF16, true, true>(a, n_qtiles) : launch<IO_F16, true, true>(a, n_qtiles);
-        else
-            e = bf ? launch<IO_BF16, false, true>(a, n_qtiles) : launch<IO_F16, false, true>(a, n_qtiles);
-    } else {
-        if (a.diff)
-            e = bf ? launch<IO_BF16, true, false>(a, n_qtiles) : launch<IO_F16, true, false>(a, n_qtiles);
-        else
-            e = bf ? launch<IO_BF16, false, false>(a, n_qtiles) : launch<IO_F16, false, false>(a, n_qtiles);
-    }
-    return (int)e;
+    return (int)(a.D == 128 ? launch_d<128>(a, n_qtiles) : launch_d<64>(a, n_qtiles));
 }
 
 }  // namespace sa3

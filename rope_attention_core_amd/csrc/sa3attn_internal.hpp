@@ -17,6 +17,7 @@ struct LaunchArgs {
     long long qs[3], ks[3], vs[3], os[3];   // element strides of b, h, l (d is contiguous)
     long long q_br, k_br;   // elements from branch 1 to branch 2 (differential)
     int B, H, L;
+    int D;                  // head dim: 64 or 128
     int window;             // half-width; -1 = full (normalised: window < L - 1)
     float lam;              // differential weight
     float scale_log2;       // |scale| * log2(e), >= 0
@@ -26,7 +27,7 @@ struct LaunchArgs {
     int diff;               // two branches
     int contig;             // contiguous [B][H][L][64] (and stacked [2][...]), adjacent pairs, R = 64
     int rope_half;          // RoPE pairs (x[i], x[i + R/2]) instead of (x[2i], x[2i+1])
-    int rot_dim;            // R: leading dims rotated (multiple of 16, <= 64); the table has R/2 columns
+    int rot_dim;            // R: leading dims rotated (multiple of 16, <= D); the table has R/2 columns
     void *stream;           // hipStream_t
 };
 

@@ -81,6 +81,9 @@ CONFIGS = {
     # medium-DiT-style differential full attention at the long latent, CFG pair
     "dit_medium_diff": Config("dit_medium_diff", 2, 24, 4096, 64, "bf16", seed=7, lam=0.8,
                               diff=True, out="f32"),
+    # the long latent with the same model width in 12 heads of 128
+    "dit_long_d128": Config("dit_long_d128", 2, 12, 4096, 128, "bf16", seed=10, out="f32",
+                            spike_frac=0.01, spike=8.0),
 }
 
 

@@ -46,7 +46,7 @@ def test_status_strings_and_version(lib):
         s = sa3.status_string(code)
         assert s.startswith("SA3_ERR_"), s
     assert "unknown" in sa3.status_string(12345)
-    assert sa3.version() == (0, 3)
+    assert sa3.version() == (0, 4)
 
 
 @pytest.mark.parametrize("L,D", [(1, 2), (37, 8), (8192, 16), (8192, 64), (8192, 128)])
@@ -101,7 +101,8 @@ def test_null_descriptor_rejected(lib):
     (dict(B=0), SA3_ERR_SHAPE), (dict(H=-1), SA3_ERR_SHAPE), (dict(L=0), SA3_ERR_SHAPE),
     (dict(D=0), SA3_ERR_SHAPE), (dict(D=63), SA3_ERR_SHAPE), (dict(L=(1 << 24) + 1), SA3_ERR_SHAPE),
     (dict(B=1 << 20, H=1 << 12), SA3_ERR_SHAPE),
-    (dict(D=128), SA3_ERR_UNSUPPORTED), (dict(D=32), SA3_ERR_UNSUPPORTED),
+    (dict(D=32), SA3_ERR_UNSUPPORTED), (dict(D=96), SA3_ERR_UNSUPPORTED), (dict(D=256), SA3_ERR_UNSUPPORTED),
+    (dict(D=128, L=(1 << 23) + 8), SA3_ERR_SHAPE),
     (dict(dtype=2), SA3_ERR_UNSUPPORTED), (dict(dtype=7), SA3_ERR_UNSUPPORTED),
     (dict(out_dtype=3), SA3_ERR_UNSUPPORTED),
     (dict(scale=float("nan")), SA3_ERR_ARG), (dict(scale=float("inf")), SA3_ERR_ARG),
@@ -113,7 +114,7 @@ def test_bad_arguments_rejected(lib, kw, code):
 
 
 def test_argument_swap_is_caught(lib):
-    """Distinct prime sizes: a caller that swaps B/H/L/D lands on D != 64."""
+    """Distinct prime sizes: a caller that swaps B/H/L/D lands on an unsupported D."""
     assert _call(lib, B=3, H=5, L=64, D=7) == SA3_ERR_SHAPE
     assert _call(lib, B=64, H=5, L=7, D=3) == SA3_ERR_SHAPE
     assert _call(lib, B=3, H=64, L=5, D=7) == SA3_ERR_SHAPE
@@ -157,6 +158,12 @@ def test_valid_call_without_gpu_reports_device_error(lib):
              None) == SA3_ERR_DEVICE
     assert lib.sa3attn_forward_bf16(_fake(1), _fake(2), _fake(3), _fake(4), _fake(5), _fake(6), 1, 2, 64, 64,
                                     -1, 0.0, 0.125, None) == SA3_ERR_DEVICE
+    # head dim 128, and the largest L it allows
+    assert _call(lib, D=128) == SA3_ERR_DEVICE
+    assert _call(lib, B=1, H=1, D=128, L=1 << 23) == SA3_ERR_DEVICE
+    assert _call(lib, B=1, H=1, D=64, L=1 << 24) == SA3_ERR_DEVICE
+    # rotary widths up to D: 80 is too wide for D = 64 but fits D = 128
+    assert _call_general(lib, rope=_rope(1, 80), D=128) == SA3_ERR_DEVICE
 
 
 def test_short_forms_validate_like_ex(lib):
@@ -255,7 +262,7 @@ def test_bad_rope_options_rejected(lib, pairing, rd):
 def test_general_form_validates_like_ex(lib):
     assert lib.sa3attn_forward_general(None, None, None) == SA3_ERR_NULL
     assert _call_general(lib, rope=_rope(1, 32), q=ctypes.c_void_p(0)) == SA3_ERR_NULL
-    assert _call_general(lib, rope=_rope(1, 32), D=128) == SA3_ERR_UNSUPPORTED
+    assert _call_general(lib, rope=_rope(1, 32), D=96) == SA3_ERR_UNSUPPORTED
     assert _call_general(lib, st=_strides(q=(0, 0, 60)), rope=_rope(1, 32)) == SA3_ERR_ARG
 
 

@@ -187,7 +187,7 @@ def test_errors_leave_out_untouched_on_gpu():
     P = lambda t: ctypes.c_void_p(t.data_ptr())
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     f = lib.sa3attn_forward
-    assert f(P(q), P(k), P(v), P(c), P(s), P(out), 1, 2, 100, 128, -1, 0.0, 0.125, stream) == -3
+    assert f(P(q), P(k), P(v), P(c), P(s), P(out), 1, 2, 100, 96, -1, 0.0, 0.125, stream) == -3
     assert f(P(q), P(k), P(v), P(c), P(s), P(out), 1, 2, 100, 64, -1, 0.0, float("nan"), stream) == -4
     assert f(P(q), P(k), P(v), P(c), P(s), P(q), 1, 2, 100, 64, -1, 0.0, 0.125, stream) == -4
     assert f(None, P(k), P(v), P(c), P(s), P(out), 1, 2, 100, 64, -1, 0.0, 0.125, stream) == -1
