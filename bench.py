@@ -4,8 +4,10 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-configs]
     python bench.py --only CONFIG      # one configuration, one short line (for profiling)
 
-One step = one call of the whole fused core (RoPE on Q/K, QK^T, FP32 online softmax,
-P.V) over one batch of synthetic input already resident in HBM. The headline workload
+One step = one call of the whole core (RoPE on Q/K, QK^T, FP32 online softmax, P.V)
+over one batch of synthetic input already resident in HBM: at the long latent that is
+two kernels, the pre-pass (RoPE of K, fp16 V^T tiles into a workspace allocated once
+before timing) and the attention kernel. The headline workload
 is the DiT long latent: B=2 (a CFG cond + uncond pair), H=24, L=4096, D=64, bf16 with
 1% of K rows scaled by 8, full attention, FP32 output. Rank 0 prints ONE JSON line with
 the metric (TFLOP/s of algorithmic work, 4*D FLOPs per query-key pair), the roofline of
@@ -16,7 +18,9 @@ Timing: W untimed warmups (and at least 0.3 s of calls, so the clocks settle), t
 back-to-back calls bracketed by synchronisation and timed with one pair of HIP events
 recorded on the stream the library launches on (torch's current stream, which the
 binding passes to the C-ABI): ms_per_step is their mean. A second pass gives each call
-its own event pair; its median, min and max are reported as the spread.
+its own event pair; its median, min and max are reported as the spread. In that pass a
+call with the pre-pass is issued as its two kernels (policies "only" then "reuse") with
+an event between them: the roofline uses the attention kernel's own mean duration.
 
 Short latents: per-call time inside one captured graph of 96 and of 40 calls (the
 number of fused attention calls in a medium / small DiT forward) at L = 1, 16, 64, 256,
@@ -44,7 +48,7 @@ COLD_CONFIGS = {"tiny", "dit_short", "samel_swa", "samel_w17"}   # HBM/latency-b
 FLUSH_MB = 512                     # larger than the 256 MB MALL plus the L2s
 GRAPH_LENGTHS = [1, 16, 64, 256]   # short-latent sequences captured as one graph of N calls
 GRAPH_CALLS = [96, 40]             # fused attention calls per forward: medium and small DiT
-KERNEL_SOURCE = os.path.join(ROOT, "rope_attention_core_amd", "csrc", "attn_fwd.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "rope_attention_core_amd", "csrc", f) for f in ("attn_fwd.hip", "attn_common.hpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_dit_long.json")
 
 
@@ -69,8 +73,12 @@ def compulsory_bytes(cfg):
 
 
 def kernel_source_sha():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 over the attention kernel's sources (the counters hold while they are unchanged)."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def load_traffic():
@@ -102,16 +110,24 @@ class Bench:
         dt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[cfg.out_dtype]
         self.out = torch.empty((cfg.B, cfg.H, cfg.L, cfg.D), dtype=dt, device="cuda")
         self.inputs_host = inp
+        # the pre-pass workspace (allocated once, outside every timed region), when the
+        # library runs the pre-pass for this shape
+        nb = sa3.workspace_bytes(cfg.B, cfg.H, cfg.L, cfg.D, window=cfg.window, differential=cfg.diff,
+                                 dtype=sa3.BF16 if cfg.io == "bf16" else sa3.F16)
+        self.ws = torch.empty(nb, dtype=torch.uint8, device="cuda") if nb else None
 
-    def call(self):
+    def call(self, prep="auto"):
         c = self.cfg
         self.sa3.forward(self.q, self.k, self.v, self.cos, self.sin, window=c.window, lam=c.lam,
-                         scale=c.scale, out=self.out, differential=c.diff)
+                         scale=c.scale, out=self.out, differential=c.diff, prep=prep, workspace=self.ws)
 
     def run(self, steps, warmup):
         """Time `steps` back-to-back calls between two HIP events on the launch stream,
         bracketed by device synchronisation (the headline ms/call), then the same number
-        of calls again, each between its own pair of events, for the spread."""
+        of calls again, each between its own pair of events, for the spread. With the
+        pre-pass, each call of the second pass is split into its two kernels (the
+        pre-pass alone, then the attention kernel alone on its workspace) with an event
+        between them, which gives each kernel's own average duration."""
         torch = self.torch
         stream = torch.cuda.current_stream()
         # W warmup calls, and calls for at least WARM_S seconds, so the clocks have
@@ -131,15 +147,25 @@ class Bench:
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
         total = t0.elapsed_time(t1)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        for a, b in ev:
+        split = self.ws is not None
+        ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
+        for a, m, b in ev:
             a.record(stream)
-            self.call()
+            if split:
+                self.call(prep="only")
+                m.record(stream)
+                self.call(prep="reuse")
+            else:
+                self.call()
+                m.record(stream)
             b.record(stream)
         torch.cuda.synchronize()
-        per = sorted(a.elapsed_time(b) for a, b in ev)
+        per = sorted(a.elapsed_time(b) for a, m, b in ev)
+        attn = sum(m.elapsed_time(b) for a, m, b in ev) / steps if split else None
+        prep = sum(a.elapsed_time(m) for a, m, b in ev) / steps if split else None
         return {"ms_total": total, "ms_mean": total / steps, "ms_median": per[len(per) // 2],
-                "ms_min": per[0], "ms_max": per[-1], "wall_s": wall}
+                "ms_min": per[0], "ms_max": per[-1], "wall_s": wall,
+                "ms_attn_kernel": attn if split else sum(per) / steps, "ms_prep_kernel": prep}
 
 
 def cold_ms(torch, b, reps=7):
@@ -307,6 +333,8 @@ def main():
         r = Bench(torch, sa3, synth, c).run(args.steps, args.warmup)
         f = flops(c)
         print(json.dumps({"config": args.only, "ms_per_call": round(r["ms_mean"], 5),
+                          "ms_attn_kernel": round(r["ms_attn_kernel"], 5),
+                          "ms_prep_kernel": None if r["ms_prep_kernel"] is None else round(r["ms_prep_kernel"], 5),
                           "tflops": round(f / (r["ms_mean"] * 1e-3) / 1e12, 2),
                           "gbs_compulsory": round(compulsory_bytes(c) / (r["ms_mean"] * 1e-3) / 1e9, 1)}),
               flush=True)
@@ -319,6 +347,7 @@ def main():
     fl = flops(cfg)
     ms = t["ms_mean"]
     tflops = fl / (ms * 1e-3) / 1e12
+    k_tflops = fl / (t["ms_attn_kernel"] * 1e-3) / 1e12   # the attention kernel alone
     traffic = load_traffic()
 
     per_config = {}
@@ -333,6 +362,7 @@ def main():
                          + (f" diff lam={c.lam}" if c.diff else "") + f" out={c.out_dtype}",
                 "ms_per_call": round(r["ms_mean"], 5),
                 "ms_median": round(r["ms_median"], 5),
+                "prep": r["ms_prep_kernel"] is not None,
                 "tflops": round(f / (r["ms_mean"] * 1e-3) / 1e12, 2),
                 "frac_mfma_peak": round(f / (r["ms_mean"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                 "gbs_compulsory": round(compulsory_bytes(c) / (r["ms_mean"] * 1e-3) / 1e9, 1),
@@ -373,12 +403,17 @@ def main():
         "ms_min": round(t["ms_min"], 5),
         "ms_max": round(t["ms_max"], 5),
         "frac_of_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "kernels_per_step": {
+            "attn_prep_kernel_ms": None if t["ms_prep_kernel"] is None else round(t["ms_prep_kernel"], 5),
+            "attn_fwd_kernel_ms": round(t["ms_attn_kernel"], 5),
+        },
         "roofline": {
             "bound": "mfma",
-            "achieved": round(tflops, 2),
+            "kernel": "attn_fwd_kernel",
+            "achieved": round(k_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "frac": round(k_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
         },
         "cpu_baseline": cpu,

@@ -39,9 +39,11 @@
  *    window < 0 means full attention. There is no causal mask.
  *  - scale multiplies the FP32 QK^T accumulator (not folded into q).
  *  - Ownership: the caller allocates and owns every buffer (device memory for
- *    q, k, v, cos, sin, out). The library never allocates, frees or synchronises
- *    and keeps no pointer after returning. Work is enqueued on `stream`
- *    (a hipStream_t; NULL = the default stream) and can be captured into a graph.
+ *    q, k, v, cos, sin, out, and the workspace of sa3attn_forward_ws). The library
+ *    never allocates, frees or synchronises and keeps no pointer after returning.
+ *    Work (one kernel; two with the pre-pass of sa3attn_forward_ws) is enqueued on
+ *    `stream` (a hipStream_t; NULL = the default stream) and can be captured into a
+ *    graph.
  *  - out must not overlap any input.
  *  - Errors: validation runs before any launch; on error nothing is enqueued and
  *    `out` is untouched. Status codes are below; sa3attn_status_string() names them.
@@ -64,7 +66,7 @@ extern "C" {
 #endif
 
 #define SA3ATTN_VERSION_MAJOR 0
-#define SA3ATTN_VERSION_MINOR 4
+#define SA3ATTN_VERSION_MINOR 5
 
 /* Status codes. */
 enum {
@@ -172,6 +174,49 @@ typedef struct sa3attn_rope {
 
 int sa3attn_forward_general(const sa3attn_desc *desc, const sa3attn_strides *strides,
                             const sa3attn_rope *rope);
+
+/*
+ * sa3attn_workspace_bytes / sa3attn_forward_ws -- the general form with a pre-pass.
+ * The RoPE of a key row (rotate in FP32, round back; the FP16-fix discussion of the
+ * medium DiT's ONNX, section "The fix") does not depend on the query, yet
+ * the fused kernel redoes it, and the fp16 transposition of V, for every query tile
+ * that visits the key: 16 to 32 times per key at L = 4096. With a workspace the
+ * library first runs a pre-pass kernel that rotates K (each branch) and converts and
+ * transposes V once, into the workspace, and the attention kernel then copies its
+ * key tiles from there. Outputs are bitwise identical to sa3attn_forward_general's.
+ *   policy: SA3_PREP_AUTO runs the pre-pass when a key tile is visited by at least
+ *     8 query tiles (full attention: L > 1792 plain and L > 896 differential at
+ *     D = 64, L > 896 and L > 448 at D = 128); SA3_PREP_ALWAYS whenever the call
+ *     takes the long-span kernel; SA3_PREP_NEVER never. SA3_PREP_ONLY enqueues the
+ *     pre-pass alone (out is not written) and SA3_PREP_REUSE the attention kernel
+ *     alone, reading a workspace that an earlier ALWAYS or ONLY call filled from the
+ *     same k, v, cos, sin, shape, strides and RoPE options (so K and V prepared once
+ *     serve several q; the library cannot check the contents: stale ones give wrong
+ *     outputs, never out-of-bounds accesses). Calls that take the single-span kernel
+ *     (windows of half-width <= 32, or L <= 256, at D = 64) have no pre-pass under
+ *     any policy: ONLY then enqueues nothing and REUSE runs the call as usual.
+ *   sa3attn_workspace_bytes: *bytes = the workspace the call shape takes under
+ *     `policy`: (2 or 3, differential) x B x H x ceil(L/64)*64 x D x 2 bytes when
+ *     the pre-pass runs, else 0. Reads only B, H, L, D, window, dtype, out_dtype
+ *     and differential of desc; shape errors as sa3attn_forward_ex's, SA3_ERR_NULL
+ *     for a NULL desc or bytes, SA3_ERR_ARG for an unknown policy.
+ *   sa3attn_forward_ws: sa3attn_forward_general plus
+ *     workspace: device memory of workspace_bytes bytes (at least what
+ *       sa3attn_workspace_bytes gives for the same shape and policy), 16-byte
+ *       aligned, overlapping no input and not out; owned by the caller; its contents
+ *       on entry do not matter and on return are scratch. Calls that may run
+ *       concurrently need workspaces of their own. May be NULL when the size is 0.
+ *   When the pre-pass runs, a NULL workspace returns SA3_ERR_NULL and a smaller,
+ *   misaligned or overlapping one SA3_ERR_ARG; an unknown policy is SA3_ERR_ARG;
+ *   all before anything is enqueued. With the pre-pass, two kernels are enqueued on
+ *   the stream, in order.
+ */
+enum { SA3_PREP_AUTO = 0, SA3_PREP_ALWAYS = 1, SA3_PREP_NEVER = 2, SA3_PREP_ONLY = 3, SA3_PREP_REUSE = 4 };
+
+int sa3attn_workspace_bytes(const sa3attn_desc *desc, int policy, unsigned long long *bytes);
+int sa3attn_forward_ws(const sa3attn_desc *desc, const sa3attn_strides *strides,
+                       const sa3attn_rope *rope, void *workspace,
+                       unsigned long long workspace_bytes, int policy);
 
 /*
  * sa3attn_rope_table -- fill a host FP32 cos/sin table [L][D/2].

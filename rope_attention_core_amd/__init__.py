@@ -15,7 +15,7 @@ import ctypes
 import os
 
 __all__ = [
-    "forward", "forward_short", "rope_table", "status_string", "version", "library_path",
+    "forward", "forward_short", "workspace_bytes", "rope_table", "status_string", "version", "library_path",
     "load_library", "SA3Error", "F16", "BF16", "F32", "EXPORTS",
 ]
 
@@ -29,6 +29,8 @@ EXPORTS = (
     "sa3attn_forward_ex",
     "sa3attn_forward_strided",
     "sa3attn_forward_general",
+    "sa3attn_workspace_bytes",
+    "sa3attn_forward_ws",
     "sa3attn_rope_table",
     "sa3attn_status_string",
     "sa3attn_version",
@@ -66,6 +68,7 @@ class _Rope(ctypes.Structure):
 
 
 ROPE_PAIRINGS = {"adjacent": 0, "half": 1}
+PREP_POLICIES = {"auto": 0, "always": 1, "never": 2, "only": 3, "reuse": 4}
 
 _lib = None
 
@@ -95,6 +98,11 @@ def load_library():
     lib.sa3attn_forward_strided.restype = i
     lib.sa3attn_forward_general.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_Strides), ctypes.POINTER(_Rope)]
     lib.sa3attn_forward_general.restype = i
+    lib.sa3attn_workspace_bytes.argtypes = [ctypes.POINTER(_Desc), i, ctypes.POINTER(ctypes.c_ulonglong)]
+    lib.sa3attn_workspace_bytes.restype = i
+    lib.sa3attn_forward_ws.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_Strides), ctypes.POINTER(_Rope), vp,
+                                       ctypes.c_ulonglong, i]
+    lib.sa3attn_forward_ws.restype = i
     lib.sa3attn_rope_table.argtypes = [vp, vp, i, i, ctypes.c_double]
     lib.sa3attn_rope_table.restype = i
     lib.sa3attn_status_string.argtypes = [i]
@@ -151,10 +159,37 @@ def rope_table(L, D=64, base=10000.0):
     return cos, sin
 
 
+def _shape_desc(B, H, L, D, window, dtype, out_dtype, differential):
+    return _Desc(None, None, None, None, None, None, B, H, L, D, int(window), 0.0, 1.0,
+                 dtype, out_dtype, 1 if differential else 0, None)
+
+
+def workspace_bytes(B, H, L, D, *, window=-1, differential=False, dtype=F16, out_dtype=None, prep="auto"):
+    """Bytes of device workspace the pre-pass of this call shape takes under the
+    policy `prep` (0: it does not run)."""
+    if prep not in PREP_POLICIES:
+        raise ValueError(f"prep must be one of {tuple(PREP_POLICIES)}")
+    n = ctypes.c_ulonglong(0)
+    d = _shape_desc(B, H, L, D, window, dtype, dtype if out_dtype is None else out_dtype, differential)
+    rc = load_library().sa3attn_workspace_bytes(ctypes.byref(d), PREP_POLICIES[prep], ctypes.byref(n))
+    if rc != 0:
+        raise SA3Error(rc, "sa3attn_workspace_bytes")
+    return int(n.value)
+
+
 def forward(q, k, v, cos, sin, *, window=-1, lam=0.0, scale=None, out=None, out_dtype=None,
-            differential=None, stream=None, pairing="adjacent", rotary_dim=None):
-    """Run the fused core through sa3attn_forward_ex, or sa3attn_forward_general when a
-    tensor is a strided view or a RoPE option is set.
+            differential=None, stream=None, pairing="adjacent", rotary_dim=None, prep="auto",
+            workspace=None):
+    """Run the core through sa3attn_forward_ws (prep "auto" / "always"), or with
+    prep="never" through sa3attn_forward_ex, or sa3attn_forward_general when a tensor is
+    a strided view or a RoPE option is set.
+
+    prep: the pre-pass policy ("auto": when each key tile is visited by >= 8 query
+    tiles; "always"; "never"; "only": the pre-pass alone, out not written; "reuse":
+    the attention kernel alone on a workspace an "always" / "only" call filled from
+    the same k, v, cos, sin); workspace: a uint8 GPU tensor of at least
+    workspace_bytes(...) bytes, allocated here (torch's caching allocator) when not
+    given. All policies give bitwise identical outputs.
 
     pairing: "adjacent" (default) or "half" (pairs x[i], x[i + R/2]); rotary_dim: R,
     the leading dims rotated (default D; a multiple of 16), cos/sin then [>=L, R/2].
@@ -210,22 +245,35 @@ def forward(q, k, v, cos, sin, *, window=-1, lam=0.0, scale=None, out=None, out_
     lib = load_library()
     contiguous = all(t.is_contiguous() for t in (q, k, v, out))
     default_rope = pairing == "adjacent" and R == D
-    if contiguous and default_rope:
+    if prep not in PREP_POLICIES:
+        raise ValueError(f"prep must be one of {tuple(PREP_POLICIES)}")
+    st = None
+    if not contiguous:
+        st = _Strides()
+        st.q[:] = qq.stride()[:3]
+        st.k[:] = kk.stride()[:3]
+        st.v[:] = v.stride()[:3]
+        st.out[:] = out.stride()[:3]
+        st.q_branch = q.stride(0) if differential else 0
+        st.k_branch = k.stride(0) if differential else 0
+    rope = None if default_rope else _Rope(ROPE_PAIRINGS[pairing], R)
+    st_p = ctypes.byref(st) if st is not None else None
+    rope_p = ctypes.byref(rope) if rope is not None else None
+    need = workspace_bytes(B, H, L, D, window=window, differential=differential, dtype=d.dtype,
+                           out_dtype=d.out_dtype, prep=prep)
+    if need > 0:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=v.device)
+        elif not workspace.is_cuda or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 GPU tensor")
+        rc = lib.sa3attn_forward_ws(ctypes.byref(d), st_p, rope_p, _ptr(workspace), workspace.numel(),
+                                    PREP_POLICIES[prep])
+        what = "sa3attn_forward_ws"
+    elif st is None and rope is None:
         rc = lib.sa3attn_forward_ex(ctypes.byref(d))
         what = "sa3attn_forward_ex"
     else:
-        st = None
-        if not contiguous:
-            st = _Strides()
-            st.q[:] = qq.stride()[:3]
-            st.k[:] = kk.stride()[:3]
-            st.v[:] = v.stride()[:3]
-            st.out[:] = out.stride()[:3]
-            st.q_branch = q.stride(0) if differential else 0
-            st.k_branch = k.stride(0) if differential else 0
-        rope = None if default_rope else _Rope(ROPE_PAIRINGS[pairing], R)
-        rc = lib.sa3attn_forward_general(ctypes.byref(d), ctypes.byref(st) if st is not None else None,
-                                         ctypes.byref(rope) if rope is not None else None)
+        rc = lib.sa3attn_forward_general(ctypes.byref(d), st_p, rope_p)
         what = "sa3attn_forward_general"
     if rc != 0:
         raise SA3Error(rc, what)

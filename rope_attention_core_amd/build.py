@@ -4,8 +4,9 @@
 
 The library is one shared object: the C-ABI layer (csrc/api.cpp), the host RoPE
 table (csrc/rope_table.cpp) and the kernels (csrc/attn_fwd.hip for full attention and
-wide windows, csrc/attn_narrow.hip for windows of half-width <= 32). It is written next
-to this file so that it travels with the source tree.
+wide windows, csrc/attn_prep.hip its optional pre-pass, csrc/attn_narrow.hip for
+windows of half-width <= 32 and short sequences). It is written next to this file so
+that it travels with the source tree.
 """
 
 import argparse
@@ -21,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsa3attn.so")
 
 ARCH = "gfx950"
-SOURCES = ["attn_fwd.hip", "attn_narrow.hip", "api.cpp", "rope_table.cpp"]
+SOURCES = ["attn_fwd.hip", "attn_narrow.hip", "attn_prep.hip", "api.cpp", "rope_table.cpp"]
 # Packed FP32 instructions are kept out of the device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
@@ -47,24 +48,30 @@ def _run(cmd, verbose):
 
 
 def build(verbose=False, asm_dir=None):
-    """Compile every source and link libsa3attn.so (always rebuilds)."""
+    """Compile every source (in parallel, one process each) and link libsa3attn.so
+    (always rebuilds)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     cc = hipcc()
     objdir = os.path.join(ROOT, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
+    jobs, objs = [], []
     for src in SOURCES:
         path = os.path.join(CSRC, src)
         obj = os.path.join(objdir, src + ".o")
         cmd = [cc, f"--offload-arch={ARCH}", *COMMON]
         if src.endswith(".hip"):
             cmd += ["-x", "hip", *DEVICE_FLAGS]
-        cmd += ["-c", path, "-o", obj]
-        _run(cmd, verbose)
+        jobs.append(cmd + ["-c", path, "-o", obj])
         objs.append(obj)
         if asm_dir and src.endswith(".hip"):
             os.makedirs(asm_dir, exist_ok=True)
-            _run([cc, f"--offload-arch={ARCH}", *COMMON, "-x", "hip", *DEVICE_FLAGS, "--cuda-device-only",
-                  "-S", path, "-o", os.path.join(asm_dir, src + ".s")], verbose)
+            jobs.append([cc, f"--offload-arch={ARCH}", *COMMON, "-x", "hip", *DEVICE_FLAGS, "--cuda-device-only",
+                         "-S", path, "-o", os.path.join(asm_dir, src + ".s")])
+    workers = max(1, min(len(jobs), os.cpu_count() or 1, 8))
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        for f in [pool.submit(_run, cmd, verbose) for cmd in jobs]:
+            f.result()
     tmp = LIB + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)

@@ -93,9 +93,15 @@ bool rows_distinct(const long long s[3], int B, int H, int L, int D) {
     return true;
 }
 
-int forward_impl(const sa3attn_desc *d, const sa3attn_strides *sp, const sa3attn_rope *rp) {
-    if (!d) return SA3_ERR_NULL;
-    if (!d->q || !d->k || !d->v || !d->cos || !d->sin || !d->out) return SA3_ERR_NULL;
+// The workspace arguments of sa3attn_forward_ws (absent for the other entry points).
+struct Workspace {
+    void *ptr;
+    unsigned long long bytes;
+    int policy;
+};
+
+// Shape and type checks shared by every entry point.
+int check_shape(const sa3attn_desc *d) {
     if (d->B < 1 || d->H < 1 || d->L < 1 || d->D < 1 || (d->D & 1)) return SA3_ERR_SHAPE;
     if (d->L > kMaxL) return SA3_ERR_SHAPE;
     if (d->D != 64 && d->D != 128) return SA3_ERR_UNSUPPORTED;
@@ -104,11 +110,47 @@ int forward_impl(const sa3attn_desc *d, const sa3attn_strides *sp, const sa3attn
     if (d->out_dtype != SA3_F16 && d->out_dtype != SA3_BF16 && d->out_dtype != SA3_F32)
         return SA3_ERR_UNSUPPORTED;
     if (d->differential != 0 && d->differential != 1) return SA3_ERR_ARG;
-    if (!std::isfinite(d->scale) || !std::isfinite(d->lambda)) return SA3_ERR_ARG;
-
     const unsigned long long bh = (unsigned long long)d->B * (unsigned long long)d->H;
     const unsigned long long elems = bh * (unsigned long long)d->L * (unsigned long long)d->D;
     if (bh > (1ull << 31) || elems > (1ull << 56)) return SA3_ERR_SHAPE;
+    return SA3_OK;
+}
+
+// The launch fields that decide which kernel runs (and so the workspace size).
+void shape_args(const sa3attn_desc *d, sa3::LaunchArgs &a) {
+    a.B = d->B;
+    a.H = d->H;
+    a.L = d->L;
+    a.D = d->D;
+    // a window reaching every key is full attention: |i - j| <= L - 1 always holds
+    a.window = (d->window < 0 || d->window >= d->L - 1) ? -1 : d->window;
+    a.dtype = d->dtype;
+    a.out_dtype = d->out_dtype;
+    a.diff = d->differential;
+}
+
+bool policy_ok(int p) {
+    return p == SA3_PREP_AUTO || p == SA3_PREP_ALWAYS || p == SA3_PREP_NEVER || p == SA3_PREP_ONLY ||
+           p == SA3_PREP_REUSE;
+}
+
+// Workspace bytes the pre-pass takes under `policy` (0: it does not run).
+unsigned long long prep_need(const sa3::LaunchArgs &a, int policy) {
+    if (policy == SA3_PREP_NEVER || (policy == SA3_PREP_AUTO && !sa3::prep_pays(a))) return 0;
+    return sa3::prep_bytes(a);
+}
+
+int forward_impl(const sa3attn_desc *d, const sa3attn_strides *sp, const sa3attn_rope *rp,
+                 const Workspace *ws = nullptr) {
+    if (!d) return SA3_ERR_NULL;
+    if (!d->q || !d->k || !d->v || !d->cos || !d->sin || !d->out) return SA3_ERR_NULL;
+    const int shape = check_shape(d);
+    if (shape != SA3_OK) return shape;
+    if (!std::isfinite(d->scale) || !std::isfinite(d->lambda)) return SA3_ERR_ARG;
+    if (ws && !policy_ok(ws->policy)) return SA3_ERR_ARG;
+
+    const unsigned long long bh = (unsigned long long)d->B * (unsigned long long)d->H;
+    const unsigned long long elems = bh * (unsigned long long)d->L * (unsigned long long)d->D;
 
     // strides: given, or those of contiguous [B][H][L][D] (q, k stacked [2][...])
     sa3attn_strides s;
@@ -174,20 +216,35 @@ int forward_impl(const sa3attn_desc *d, const sa3attn_strides *sp, const sa3attn
     }
     a.rope_half = pairing == SA3_ROPE_HALF ? 1 : 0;
     a.rot_dim = rot_dim;
-    a.B = d->B;
-    a.H = d->H;
-    a.L = d->L;
-    a.D = d->D;
-    // a window reaching every key is full attention: |i - j| <= L - 1 always holds
-    a.window = (d->window < 0 || d->window >= d->L - 1) ? -1 : d->window;
+    shape_args(d, a);
     a.lam = d->lambda;
     a.scale_log2 = (float)(std::fabs((double)d->scale) * 1.4426950408889634074);
     a.neg_scale = d->scale < 0.0f ? 1 : 0;
-    a.dtype = d->dtype;
-    a.out_dtype = d->out_dtype;
-    a.diff = d->differential;
     a.stream = d->stream;
+    a.ws = nullptr;
+    a.prep = 0;
+    a.run_prep = 0;
+    a.run_main = 1;
     if (!std::isfinite(a.scale_log2)) return SA3_ERR_ARG;
+
+    // workspace of the pre-pass, when the policy runs it for this call: it must hold
+    // prep_bytes, be 16-byte aligned and overlap neither an input nor out
+    const unsigned long long need = ws ? prep_need(a, ws->policy) : 0;
+    if (ws && ws->policy == SA3_PREP_ONLY) a.run_main = 0;
+    if (need > 0) {
+        if (!ws->ptr) return SA3_ERR_NULL;
+        if (ws->bytes < need || !aligned16(ws->ptr)) return SA3_ERR_ARG;
+        const size_t wb = (size_t)need;
+        if (overlaps(ws->ptr, wb, d->q, q_bytes) || overlaps(ws->ptr, wb, d->k, k_bytes) ||
+            overlaps(ws->ptr, wb, d->v, v_bytes) || overlaps(ws->ptr, wb, d->cos, tab_bytes) ||
+            overlaps(ws->ptr, wb, d->sin, tab_bytes) || overlaps(ws->ptr, wb, d->out, out_bytes))
+            return SA3_ERR_ARG;
+        a.ws = ws->ptr;
+        a.prep = 1;
+        a.run_prep = ws->policy != SA3_PREP_REUSE;
+        a.run_main = ws->policy != SA3_PREP_ONLY;
+        if ((((unsigned long long)d->L + 63) / 64) * bh >= (1ull << 31)) return SA3_ERR_SHAPE;
+    }
 
     const unsigned long long tiles = ((unsigned long long)d->L + sa3::tile_rows(a) - 1) / sa3::tile_rows(a);
     if (tiles * bh >= (1ull << 31)) return SA3_ERR_SHAPE;
@@ -212,6 +269,23 @@ int sa3attn_forward_strided(const sa3attn_desc *desc, const sa3attn_strides *str
 
 int sa3attn_forward_general(const sa3attn_desc *desc, const sa3attn_strides *strides, const sa3attn_rope *rope) {
     return forward_impl(desc, strides, rope);
+}
+
+int sa3attn_workspace_bytes(const sa3attn_desc *desc, int policy, unsigned long long *bytes) {
+    if (!desc || !bytes) return SA3_ERR_NULL;
+    const int shape = check_shape(desc);
+    if (shape != SA3_OK) return shape;
+    if (!policy_ok(policy)) return SA3_ERR_ARG;
+    sa3::LaunchArgs a{};
+    shape_args(desc, a);
+    *bytes = prep_need(a, policy);
+    return SA3_OK;
+}
+
+int sa3attn_forward_ws(const sa3attn_desc *desc, const sa3attn_strides *strides, const sa3attn_rope *rope,
+                       void *workspace, unsigned long long workspace_bytes, int policy) {
+    const Workspace w{workspace, workspace_bytes, policy};
+    return forward_impl(desc, strides, rope, &w);
 }
 
 static int forward_short(const void *q, const void *k, const void *v, const float *cos, const float *sin,

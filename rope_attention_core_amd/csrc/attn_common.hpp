@@ -50,6 +50,10 @@ struct Params {
     float lam, c;                 // c = |scale| * log2(e)
     int rope_half, rot_dim;       // RoPE of the general instances: half-split pairs, rotary width
     uint32_t tab_rowb;            // bytes per cos/sin table row (rot_dim / 2 floats)
+    // pre-pass workspace: K' [branch][B*H][Lp][D] rotated, in the IO type; V'
+    // [B*H][Lp/64][D][64] fp16, each 64-key tile transposed (Lp = L rounded up to 64)
+    uint16_t *kw, *vw;
+    int ws_tiles;                 // Lp / 64
 };
 
 // Kernel parameters common to every instance (n_qtiles and window are set by the caller).
@@ -86,6 +90,10 @@ inline Params make_params(const LaunchArgs &a) {
     P.rope_half = a.rope_half;
     P.rot_dim = a.rot_dim;
     P.tab_rowb = (uint32_t)(a.rot_dim / 2 * 4);
+    const long long lp = ((long long)a.L + BN - 1) / BN * BN;
+    P.ws_tiles = (int)(lp / BN);
+    P.kw = a.prep ? static_cast<uint16_t *>(a.ws) : nullptr;
+    P.vw = a.prep ? P.kw + (a.diff ? 2 : 1) * (long long)a.B * a.H * lp * a.D : nullptr;
     return P;
 }
 
@@ -138,7 +146,7 @@ __device__ __forceinline__ u32x4 rope8(u32x4 x, u32x4 cw, u32x4 sw) {
 
 // ---- RoPE of the general instances --------------------------------------------
 // Chunk c of a position (dims 8c .. 8c+7) under pairing `half` and rotary width R
-// (a multiple of 16, <= 64): mode 0 passes it through (c >= R/8); mode 1 rotates
+// (a multiple of 16, <= D): mode 0 passes it through (c >= R/8); mode 1 rotates
 // adjacent pairs with table floats 4c .. 4c+3; mode 2 (half-split, c < R/16) pairs
 // it with chunk c + R/16 as the first members, mode 3 (R/16 <= c < R/8) with chunk
 // c - R/16 as the second members, both with table floats 8j .. 8j+7 of j = c mod R/16.

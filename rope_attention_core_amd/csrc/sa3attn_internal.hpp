@@ -11,8 +11,8 @@ struct LaunchArgs {
     const void *q;          // element (b, h, l, d) at b*qs[0] + h*qs[1] + l*qs[2] + d (+ q_br: branch 2)
     const void *k;          // likewise with ks and k_br
     const void *v;          // likewise with vs
-    const float *cos;       // [>=L][32]
-    const float *sin;       // [>=L][32]
+    const float *cos;       // [>=L][R/2]
+    const float *sin;       // [>=L][R/2]
     void *out;              // likewise with os
     long long qs[3], ks[3], vs[3], os[3];   // element strides of b, h, l (d is contiguous)
     long long q_br, k_br;   // elements from branch 1 to branch 2 (differential)
@@ -25,9 +25,13 @@ struct LaunchArgs {
     int dtype;              // SA3_F16 / SA3_BF16
     int out_dtype;          // SA3_F16 / SA3_BF16 / SA3_F32
     int diff;               // two branches
-    int contig;             // contiguous [B][H][L][64] (and stacked [2][...]), adjacent pairs, R = 64
+    int contig;             // contiguous [B][H][L][D] (and stacked [2][...]), adjacent pairs, R = D
     int rope_half;          // RoPE pairs (x[i], x[i + R/2]) instead of (x[2i], x[2i+1])
     int rot_dim;            // R: leading dims rotated (multiple of 16, <= D); the table has R/2 columns
+    void *ws;               // workspace of the pre-pass (prep_bytes(a) bytes), or nullptr
+    int prep;               // the long-span kernel reads K and V from the pre-pass workspace
+    int run_prep;           // with prep: enqueue the pre-pass (0: ws already holds its result)
+    int run_main;           // enqueue the attention kernel (0: only the pre-pass)
     void *stream;           // hipStream_t
 };
 
@@ -37,6 +41,16 @@ int launch_forward(const LaunchArgs &a);
 // Query rows handled by one workgroup of the instance launch_forward picks, so the
 // host can check the grid size before launching.
 int tile_rows(const LaunchArgs &a);
+
+// The pre-pass (attn_prep.hip): K of each branch rotated and V converted to fp16 and
+// transposed, once per key tile, into a workspace the long-span kernel then copies
+// from. prep_bytes: the workspace it needs (0 when the call takes the single-span
+// kernel, which has no use for it); prep_pays: whether the saving in the long-span
+// kernel (each key tile is rotated by every query tile that visits it) outweighs the
+// extra pass; launch_prep: enqueues it (a.ws set).
+unsigned long long prep_bytes(const LaunchArgs &a);
+bool prep_pays(const LaunchArgs &a);
+int launch_prep(const LaunchArgs &a);
 
 // The single-span kernel (sequences of <= 256 keys, or windows of half-width <= 32):
 // whether it takes this call, its launcher and its query rows per workgroup.

@@ -46,7 +46,7 @@ def test_status_strings_and_version(lib):
         s = sa3.status_string(code)
         assert s.startswith("SA3_ERR_"), s
     assert "unknown" in sa3.status_string(12345)
-    assert sa3.version() == (0, 4)
+    assert sa3.version() == (0, 5)
 
 
 @pytest.mark.parametrize("L,D", [(1, 2), (37, 8), (8192, 16), (8192, 64), (8192, 128)])
@@ -286,3 +286,110 @@ def test_valid_general_calls_without_gpu_report_device_error(lib):
     base = _fake(9).value
     assert _call_general(lib, rope=_rope(0, 32), cos=ctypes.c_void_p(base),
                          out=ctypes.c_void_p(base + 64 * 16 * 4)) == SA3_ERR_DEVICE
+
+
+# ---- workspace / pre-pass (sa3attn_workspace_bytes, sa3attn_forward_ws) -------------
+
+AUTO, ALWAYS, NEVER, ONLY, REUSE = 0, 1, 2, 3, 4
+
+
+def _ws_bytes(lib, policy=AUTO, **kw):
+    n = ctypes.c_ulonglong(12345)
+    rc = lib.sa3attn_workspace_bytes(ctypes.byref(_desc(**kw)), policy, ctypes.byref(n))
+    return rc, n.value
+
+
+def _lp(L):
+    return (L + 63) // 64 * 64
+
+
+@pytest.mark.parametrize("kw,policy,want", [
+    # full attention: AUTO from 8 query tiles of 256 (plain) / 128 (differential) rows at D = 64
+    (dict(B=2, H=24, L=4096), AUTO, 2 * 2 * 24 * 4096 * 64 * 2),
+    (dict(B=1, H=3, L=1792), AUTO, 0),
+    (dict(B=1, H=3, L=1793), AUTO, 2 * 3 * _lp(1793) * 64 * 2),
+    (dict(B=1, H=3, L=896, differential=1), AUTO, 0),
+    (dict(B=1, H=3, L=897, differential=1), AUTO, 3 * 3 * _lp(897) * 64 * 2),
+    # D = 128: 128 / 64 rows per query tile
+    (dict(B=1, H=2, L=896, D=128), AUTO, 0),
+    (dict(B=1, H=2, L=897, D=128), AUTO, 2 * 2 * _lp(897) * 128 * 2),
+    (dict(B=1, H=2, L=449, D=128, differential=1), AUTO, 3 * 2 * _lp(449) * 128 * 2),
+    # windows: a key tile of a half-width-256 window is visited by 6 query tiles of 128
+    (dict(B=1, H=16, L=8192, window=256, differential=1), AUTO, 0),
+    (dict(B=1, H=16, L=8192, window=256, differential=1), ALWAYS, 3 * 16 * 8192 * 64 * 2),
+    (dict(B=1, H=16, L=8192, window=1024, differential=1), AUTO, 3 * 16 * 8192 * 64 * 2),
+    # the single-span kernel (w <= 32, or L <= 256 at D = 64) has no pre-pass
+    (dict(B=1, H=16, L=8192, window=17, differential=1), ALWAYS, 0),
+    (dict(B=1, H=2, L=256), ALWAYS, 0),
+    (dict(B=1, H=2, L=256, D=128), ALWAYS, 2 * 2 * 256 * 128 * 2),
+    (dict(B=1, H=2, L=300), ALWAYS, 2 * 2 * _lp(300) * 64 * 2),
+    (dict(B=2, H=24, L=4096), NEVER, 0),
+    (dict(B=1, H=2, L=300), ONLY, 2 * 2 * _lp(300) * 64 * 2),
+    (dict(B=1, H=2, L=300), REUSE, 2 * 2 * _lp(300) * 64 * 2),
+    (dict(B=1, H=2, L=200), ONLY, 0),
+])
+def test_workspace_bytes(lib, kw, policy, want):
+    assert _ws_bytes(lib, policy, **kw) == (SA3_OK, want)
+    B, H, L, D = kw["B"], kw["H"], kw["L"], kw.get("D", 64)
+    prep = {AUTO: "auto", ALWAYS: "always", NEVER: "never", ONLY: "only", REUSE: "reuse"}[policy]
+    assert sa3.workspace_bytes(B, H, L, D, window=kw.get("window", -1), differential=bool(kw.get("differential")),
+                               prep=prep) == want
+
+
+def test_workspace_bytes_errors(lib):
+    n = ctypes.c_ulonglong(0)
+    assert lib.sa3attn_workspace_bytes(None, AUTO, ctypes.byref(n)) == SA3_ERR_NULL
+    assert lib.sa3attn_workspace_bytes(ctypes.byref(_desc()), AUTO, None) == SA3_ERR_NULL
+    assert _ws_bytes(lib, 5)[0] == SA3_ERR_ARG
+    assert _ws_bytes(lib, -1)[0] == SA3_ERR_ARG
+    assert _ws_bytes(lib, D=96)[0] == SA3_ERR_UNSUPPORTED
+    assert _ws_bytes(lib, L=0)[0] == SA3_ERR_SHAPE
+    # pointers are not read: a shape-only descriptor is enough
+    assert _ws_bytes(lib, ALWAYS, q=ctypes.c_void_p(0), out=ctypes.c_void_p(0), L=1000) == \
+        (SA3_OK, 2 * 2 * _lp(1000) * 64 * 2)
+
+
+def _call_ws(lib, ws, nbytes, policy=ALWAYS, st=None, rope=None, **kw):
+    kw.setdefault("L", 1000)
+    return lib.sa3attn_forward_ws(ctypes.byref(_desc(**kw)), ctypes.byref(st) if st is not None else None,
+                                  ctypes.byref(rope) if rope is not None else None, ws, nbytes, policy)
+
+
+def test_forward_ws_validation(lib):
+    need = 2 * 2 * _lp(1000) * 64 * 2
+    ws = _fake(20)
+    assert lib.sa3attn_forward_ws(None, None, None, ws, need, ALWAYS) == SA3_ERR_NULL
+    assert _call_ws(lib, None, need) == SA3_ERR_NULL
+    assert _call_ws(lib, ws, need - 16) == SA3_ERR_ARG
+    assert _call_ws(lib, ctypes.c_void_p(ws.value + 8), need) == SA3_ERR_ARG
+    assert _call_ws(lib, ws, need, policy=5) == SA3_ERR_ARG
+    for policy in (ONLY, REUSE):
+        assert _call_ws(lib, None, need, policy=policy) == SA3_ERR_NULL
+        assert _call_ws(lib, ws, need - 16, policy=policy) == SA3_ERR_ARG
+    # the workspace overlaps an input or out
+    for name in ("q", "k", "v", "cos", "sin", "out"):
+        assert _call_ws(lib, ws, need, **{name: ctypes.c_void_p(ws.value + need - 64)}) == SA3_ERR_ARG, name
+    # the usual checks still run first
+    assert _call_ws(lib, ws, need, D=96) == SA3_ERR_UNSUPPORTED
+    assert _call_ws(lib, ws, need, scale=float("nan")) == SA3_ERR_ARG
+    assert _call_ws(lib, ws, need, rope=_rope(1, 80)) == SA3_ERR_ARG
+
+
+@pytest.mark.skipif(_gpu_present(), reason="placeholder pointers must never reach a real GPU")
+def test_valid_ws_calls_without_gpu_report_device_error(lib):
+    need = 2 * 2 * _lp(1000) * 64 * 2
+    ws = _fake(20)
+    assert _call_ws(lib, ws, need) == SA3_ERR_DEVICE
+    assert _call_ws(lib, ws, need + 4096) == SA3_ERR_DEVICE
+    # no workspace needed: NEVER, AUTO below the threshold, the single-span kernel
+    assert _call_ws(lib, None, 0, policy=NEVER) == SA3_ERR_DEVICE
+    assert _call_ws(lib, None, 0, policy=AUTO) == SA3_ERR_DEVICE
+    assert _call_ws(lib, None, 0, policy=ALWAYS, window=17) == SA3_ERR_DEVICE
+    assert _call_ws(lib, None, 0, policy=ALWAYS, L=200) == SA3_ERR_DEVICE
+    assert _call_ws(lib, ws, need, policy=ONLY) == SA3_ERR_DEVICE
+    assert _call_ws(lib, ws, need, policy=REUSE) == SA3_ERR_DEVICE
+    assert _call_ws(lib, None, 0, policy=ONLY, window=17) == SA3_ERR_DEVICE
+    # the workspace right after out is no overlap
+    assert _call_ws(lib, ws, need, out=ctypes.c_void_p(ws.value - 2 * 1000 * 64 * 2)) == SA3_ERR_DEVICE
+    assert _call_ws(lib, ws, 3 * 2 * _lp(1000) * 64 * 2, differential=1, st=_strides(layout="blhd"),
+                    rope=_rope(1, 32)) == SA3_ERR_DEVICE

@@ -1,0 +1,178 @@
+"""GPU checks of the pre-pass path (sa3attn_forward_ws through the binding).
+
+The pre-pass rotates K and converts / transposes V once into a workspace; the
+long-span kernel then copies its key tiles from there. The arithmetic is the same, so
+every case must give the same bits as the fused path (prep="never"), and the result is
+also compared with the oracle element by element on a subset. Cases cover plain and
+differential attention, full and wide windows, both IO dtypes, ragged lengths (the
+workspace's tail rows), strided views, the RoPE options, head dim 128, a workspace
+full of NaN bits on entry, reuse of one workspace by calls of different shapes, and
+graph capture.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from rope_attention_core_amd import synth
+
+import gpu_common as G
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(cfg, strided=False):
+    inp = synth.make_inputs(cfg)
+    q, k, v = (G.to_device(inp[n], cfg.io) for n in ("q", "k", "v"))
+    if strided:
+        q, k, v = (t.transpose(-2, -3).contiguous().transpose(-2, -3) for t in (q, k, v))
+    return inp, q, k, v
+
+
+def _call(cfg, q, k, v, rd=None, pairing="adjacent", **kw):
+    c, s = G.device_table(cfg.L, rd or cfg.D, cfg.base)
+    return G.sa3.forward(q, k, v, c, s, window=cfg.window, lam=cfg.lam, scale=cfg.scale,
+                         out_dtype=G.out_torch_dtype(cfg.out_dtype), differential=cfg.diff,
+                         pairing=pairing, rotary_dim=rd, **kw)
+
+
+CASES = [
+    # name, overrides, strided, (pairing, rotary_dim) or None
+    ("dit_2min", dict(H=3, L=700), False, None),                           # plain, ragged
+    ("dit_2min", dict(H=2, L=1000, io="bf16", out="f32"), False, None),     # bf16 V conversion
+    ("dit_2min_prime", dict(H=2), False, None),                             # L = 1291
+    ("samel_swa", dict(H=2, L=900, window=-1), False, None),                # differential
+    ("samel_swa", dict(H=2, L=1500, window=200), False, None),              # differential, windowed
+    ("dit_2min", dict(H=2, L=800, window=100, io="bf16", out="bf16"), False, None),
+    ("dit_2min", dict(H=3, L=700), True, None),                             # [B, L, H, D] views
+    ("samel_swa", dict(H=2, L=700, window=-1), True, ("half", 32)),         # views + RoPE options
+    ("dit_2min", dict(H=2, L=600), False, ("half", 64)),
+    ("dit_2min", dict(H=2, L=600), False, ("adjacent", 48)),
+    ("dit_2min", dict(H=2, L=700, D=128), False, None),                     # head dim 128
+    ("samel_swa", dict(H=2, L=600, window=-1, D=128), False, None),
+    ("dit_2min", dict(H=2, L=500, D=128), True, ("half", 96)),
+    ("dit_2min", dict(H=2, L=300), False, None),                            # two key tiles past 256
+]
+
+
+def _rope_kw(opt):
+    return {} if opt is None else dict(pairing=opt[0], rd=opt[1])
+
+
+@pytest.mark.parametrize("name,kw,strided,opt", CASES)
+def test_prep_path_equals_fused_path(name, kw, strided, opt):
+    torch = G.torch_mod()
+    cfg = synth.config(name, seed=9800 + kw.get("L", 0), **kw)
+    inp, q, k, v = _inputs(cfg, strided)
+    G.note(f"  prep: {name} {kw} strided={strided} rope={opt}")
+    fused = _call(cfg, q, k, v, prep="never", **_rope_kw(opt))
+    pre = _call(cfg, q, k, v, prep="always", **_rope_kw(opt))
+    torch.cuda.synchronize()
+    assert torch.equal(pre, fused), f"{name} {kw}: pre-pass path differs from the fused path"
+
+
+@pytest.mark.parametrize("name,kw", [("dit_2min", dict(H=3, L=700)), ("samel_swa", dict(H=2, L=900, window=-1)),
+                                     ("dit_2min", dict(H=2, L=700, D=128))])
+def test_prep_path_parity(name, kw):
+    cfg = synth.config(name, seed=9850, **kw)
+    inp, q, k, v = _inputs(cfg)
+    got = _call(cfg, q, k, v, prep="always")
+    G.torch_mod().cuda.synchronize()
+    G.assert_parity(got.float().cpu().numpy().astype(np.float64), G.run_oracle(cfg, inp),
+                    what=f"prep {name} {kw}", out=cfg.out_dtype)
+
+
+@pytest.mark.parametrize("name", ["dit_long", "dit_medium_diff", "dit_long_d128"])
+def test_auto_policy_at_full_size(name):
+    """The benchmark shapes: AUTO runs the pre-pass there, and matches the fused path."""
+    torch = G.torch_mod()
+    cfg = synth.config(name)
+    assert G.sa3.workspace_bytes(cfg.B, cfg.H, cfg.L, cfg.D, window=cfg.window, differential=cfg.diff) > 0
+    inp, q, k, v = _inputs(cfg)
+    fused = _call(cfg, q, k, v, prep="never")
+    auto = _call(cfg, q, k, v, prep="auto")
+    torch.cuda.synchronize()
+    assert torch.equal(auto, fused)
+    rows = np.array([0, 1, 777, cfg.L - 1])
+    want = G.run_oracle_rows(cfg, inp, cfg.B - 1, cfg.H - 1, rows)
+    G.assert_parity(auto[cfg.B - 1, cfg.H - 1, rows].float().cpu().numpy().astype(np.float64), want,
+                    what=f"{name} auto", out=cfg.out_dtype)
+
+
+def test_workspace_contents_on_entry_do_not_matter():
+    """A workspace full of NaN bits, reused by a larger then a smaller call."""
+    torch = G.torch_mod()
+    big = synth.config("samel_swa", H=2, L=1000, window=-1, seed=9870)
+    small = synth.config("dit_2min", H=1, L=333, seed=9871)
+    nb = G.sa3.workspace_bytes(big.B, big.H, big.L, big.D, differential=True, dtype=G.sa3.BF16, prep="always")
+    ws = torch.full((nb,), 0xFF, dtype=torch.uint8, device="cuda")
+    for cfg in (big, small):
+        _, q, k, v = _inputs(cfg)
+        fused = _call(cfg, q, k, v, prep="never")
+        pre = _call(cfg, q, k, v, prep="always", workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(pre, fused), cfg.name
+
+
+def test_too_small_workspace_is_rejected_and_out_untouched():
+    torch = G.torch_mod()
+    cfg = synth.config("dit_2min", H=2, L=700, seed=9872)
+    _, q, k, v = _inputs(cfg)
+    nb = G.sa3.workspace_bytes(cfg.B, cfg.H, cfg.L, cfg.D, prep="always")
+    ws = torch.empty((nb - 16,), dtype=torch.uint8, device="cuda")
+    out = torch.full_like(v, 7.0)
+    with pytest.raises(G.sa3.SA3Error):
+        _call(cfg, q, k, v, prep="always", workspace=ws, out=out)
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
+
+
+def test_prep_path_in_a_graph():
+    """Two kernels captured into one graph; every replay matches the eager result."""
+    torch = G.torch_mod()
+    cfg = synth.config("samel_swa", H=2, L=1000, window=-1, seed=9873)
+    _, q, k, v = _inputs(cfg)
+    eager = _call(cfg, q, k, v, prep="never")
+    nb = G.sa3.workspace_bytes(cfg.B, cfg.H, cfg.L, cfg.D, differential=True, dtype=G.sa3.BF16, prep="always")
+    ws = torch.empty((nb,), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(eager)
+    c, s = G.device_table(cfg.L, cfg.D, cfg.base)
+    call = dict(window=cfg.window, lam=cfg.lam, scale=cfg.scale, out=out, differential=True, prep="always",
+                workspace=ws)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            G.sa3.forward(q, k, v, c, s, **call)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        G.sa3.forward(q, k, v, c, s, **call)
+    for i in range(4):
+        out.zero_()
+        ws.fill_(0xFF if i % 2 else 0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i} differs from eager"
+
+
+def test_prepare_once_then_reuse_for_several_queries():
+    """The "only" policy fills the workspace from k, v; "reuse" runs the attention
+    kernel alone on it, for the original q and for a second q against the same keys."""
+    torch = G.torch_mod()
+    cfg = synth.config("samel_swa", H=2, L=800, window=-1, seed=9874)
+    _, q, k, v = _inputs(cfg)
+    q2 = torch.flip(q, dims=[-2]).contiguous()
+    nb = G.sa3.workspace_bytes(cfg.B, cfg.H, cfg.L, cfg.D, differential=True, prep="always")
+    ws = torch.full((nb,), 0xFF, dtype=torch.uint8, device="cuda")
+    out = torch.full((cfg.B, cfg.H, cfg.L, cfg.D), 7.0, dtype=torch.float32, device="cuda")
+    _call(cfg, q, k, v, prep="only", workspace=ws, out=out)
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all()), "the pre-pass alone wrote out"
+    for qq in (q, q2):
+        want = _call(cfg, qq, k, v, prep="never")
+        got = _call(cfg, qq, k, v, prep="reuse", workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(got, want)
