@@ -359,12 +359,22 @@ __global__ __launch_bounds__(waves_for<D>() * 64, waves_for<D>() / 4) void attn_
 
     // Two score sets: the block of tile t starts QK^T(t+1) into sb[P^1] so its MFMAs run
     // under the softmax of tile t (sb[P]); P.V(t) follows each 32-key half of the softmax.
+    // Staging t+2 and loading t+3 go first in the block (EARLY: the buffer of t+2 was
+    // last read in tile t-1, which the barrier closed), so that the loads have a whole
+    // tile to arrive before the next block's staging waits for them; placed after the
+    // softmax, the compiler's register reuse makes the softmax wait for them instead.
+    // The general fused instances keep them last: early, they spill.
+    constexpr bool EARLY = PRE || CONTIG;
     f32x16 sb[2][2];
     qk(t_begin % NBUF, sb[0]);
     auto block = [&](int t, auto mask_tag, auto par_tag) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_tag)::value;
         constexpr int PC = decltype(par_tag)::value;
         constexpr int PN = PC ^ 1;
+        if constexpr (EARLY) {
+            stage((t + 2) % NBUF);
+            load_raw(t + 3);
+        }
         qk((t + 1) % NBUF, sb[PN]);
         const TileMask mk = MASK ? tile_mask(t) : TileMask{0, 0};
         const float mt = tile_max<MASK>(sb[PC], c, mk);
@@ -390,8 +400,10 @@ __global__ __launch_bounds__(waves_for<D>() * 64, waves_for<D>() / 4) void attn_
                                        st.o[db]);
         }
         st.l = __builtin_fmaf(st.l, a, part[0] + part[1]);
-        stage((t + 2) % NBUF);
-        load_raw(t + 3);
+        if constexpr (!EARLY) {
+            stage((t + 2) % NBUF);
+            load_raw(t + 3);
+        }
         __syncthreads();
     };
 
