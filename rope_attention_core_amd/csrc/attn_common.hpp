@@ -332,13 +332,14 @@ __device__ __forceinline__ void softmax_half(const f32x16 &s, int kb, float c, f
     rowsum = acc[0] + acc[1];
 }
 
-// max(a, b, c) as one v_max3_f32. MFMA results and -inf are never signalling NaNs, so
-// the quieting that fmaxf implies (an extra v_max_f32 x, x, x per operand) is not needed;
-// a quiet NaN operand is ignored, as fmaxf does.
+// max(a, b, c); the compiler emits one v_max3_f32 for it. MFMA results, selects between
+// them and -inf count as canonical floats, so no quieting instructions are added; and,
+// unlike inline assembly, the compiler sees the read of the MFMA result registers and
+// inserts the wait states the hardware needs between an MFMA and a VALU read of its
+// result (an inline-asm max that reads fresh MFMA results gets none and reads stale
+// registers).
 __device__ __forceinline__ float max3f(float a, float b, float c) {
-    float d;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
-    return d;
+    return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
 }
 
 // Maximum of 32 values as a tree of 3-input maxima (depth 3) rather than a chain.

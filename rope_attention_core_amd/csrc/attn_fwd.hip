@@ -63,11 +63,11 @@ struct Branch {
     float a;         // factor taking O and l from the previous base to m
 };
 
-// Waves per workgroup: D = 64 runs 8 waves (two per SIMD, registers <= 256 per wave);
-// D = 128 doubles the O accumulator and the rotated Q a wave keeps, so it runs 4 waves
-// (one per SIMD) with the whole 512-entry register file of a lane each.
+// Waves per workgroup: 8, two per SIMD, so that one wave's VALU work can issue while the
+// other waits (a single wave issues a VALU op at best every ~5 cycles, half the SIMD's
+// rate); registers <= 256 per wave.
 template <int D>
-constexpr int waves_for() { return D == 128 ? 4 : 8; }
+constexpr int waves_for() { return 8; }
 
 // Plain: each wave owns 32 query rows, BM = 32 x waves. Differential: waves w and
 // w + waves/2 own the same 32 rows, wave w the first softmax branch (Q1, K1) and the
@@ -365,21 +365,31 @@ __global__ __launch_bounds__(waves_for<D>() * 64, waves_for<D>() / 4) void attn_
     // softmax, the compiler's register reuse makes the softmax wait for them instead.
     // The general fused instances keep them last: early, they spill.
     constexpr bool EARLY = PRE || CONTIG;
-    f32x16 sb[2][2];
-    qk(t_begin % NBUF, sb[0]);
+    // D = 128 doubles O and the rotated Q; two score sets would not fit in 256 registers,
+    // so it computes QK^T(t) at the start of block t and relies on the other wave of its
+    // SIMD to fill the wait for the MFMA results.
+    constexpr bool PIPE2 = D == 64;
+    f32x16 sb[PIPE2 ? 2 : 1][2];
+    if constexpr (PIPE2) qk(t_begin % NBUF, sb[0]);
     auto block = [&](int t, auto mask_tag, auto par_tag) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_tag)::value;
-        constexpr int PC = decltype(par_tag)::value;
-        constexpr int PN = PC ^ 1;
+        constexpr int PC = PIPE2 ? decltype(par_tag)::value : 0;
+        constexpr int PN = PIPE2 ? PC ^ 1 : 0;
         if constexpr (EARLY) {
             stage((t + 2) % NBUF);
             load_raw(t + 3);
         }
-        qk((t + 1) % NBUF, sb[PN]);
+        if constexpr (PIPE2)
+            qk((t + 1) % NBUF, sb[PN]);
+        else
+            qk(t % NBUF, sb[0]);
         const TileMask mk = MASK ? tile_mask(t) : TileMask{0, 0};
         const float mt = tile_max<MASK>(sb[PC], c, mk);
         const float mn = (mt > st.m + TAU) ? mt : st.m;
-        const float a = (mn == st.m) ? 1.0f : ((st.m == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(st.m - mn));
+        // branch-free: exp2(-inf) = 0 covers a row that had no valid key yet (the select
+        // keeps the tile one basic block, which the scheduler can interleave)
+        const float ea = __builtin_amdgcn_exp2f(st.m - mn);
+        const float a = (mn == st.m) ? 1.0f : ea;
         st.m = mn;
         const float nb = (mn == NEG_INF) ? 0.0f : -mn;
 #pragma unroll

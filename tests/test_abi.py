@@ -310,10 +310,11 @@ def _lp(L):
     (dict(B=1, H=3, L=1793), AUTO, 2 * 3 * _lp(1793) * 64 * 2),
     (dict(B=1, H=3, L=896, differential=1), AUTO, 0),
     (dict(B=1, H=3, L=897, differential=1), AUTO, 3 * 3 * _lp(897) * 64 * 2),
-    # D = 128: 128 / 64 rows per query tile
-    (dict(B=1, H=2, L=896, D=128), AUTO, 0),
-    (dict(B=1, H=2, L=897, D=128), AUTO, 2 * 2 * _lp(897) * 128 * 2),
-    (dict(B=1, H=2, L=449, D=128, differential=1), AUTO, 3 * 2 * _lp(449) * 128 * 2),
+    # D = 128: the same 256 / 128 rows per query tile
+    (dict(B=1, H=2, L=1792, D=128), AUTO, 0),
+    (dict(B=1, H=2, L=1793, D=128), AUTO, 2 * 2 * _lp(1793) * 128 * 2),
+    (dict(B=1, H=2, L=896, D=128, differential=1), AUTO, 0),
+    (dict(B=1, H=2, L=897, D=128, differential=1), AUTO, 3 * 2 * _lp(897) * 128 * 2),
     # windows: a key tile of a half-width-256 window is visited by 6 query tiles of 128
     (dict(B=1, H=16, L=8192, window=256, differential=1), AUTO, 0),
     (dict(B=1, H=16, L=8192, window=256, differential=1), ALWAYS, 3 * 16 * 8192 * 64 * 2),
