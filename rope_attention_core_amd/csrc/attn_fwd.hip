@@ -523,15 +523,16 @@ unsigned long long prep_bytes(const LaunchArgs &a) {
 }
 
 // The fused staging rotates and transposes a key tile once per query tile that visits
-// it; the pre-pass costs about one extra read and write of K and V. It pays once a key
-// tile is visited by 8 or more query tiles (measured at L = 4096: 5-13% faster; at 5
-// visits, a window of half-width 256 with 128-row tiles, no gain).
+// it; the pre-pass costs about one extra read and write of K and V. Measured: at L = 4096
+// (16 / 32 visits) 5-17% faster; a differential window of half-width 256 (6 visits,
+// two K tiles staged per key tile) 2.5% faster; plain full attention at L = 1292 (6
+// visits) 2% slower. So: 6 or more visits for differential calls, 8 for plain ones.
 bool prep_pays(const LaunchArgs &a) {
     if (use_narrow(a)) return false;
     const int bm = tile_rows(a);
     const long long n_qtiles = ((long long)a.L + bm - 1) / bm;
     const long long visits = a.window < 0 ? n_qtiles : std::min(n_qtiles, (2ll * a.window + BN + bm - 1) / bm + 1);
-    return visits >= 8;
+    return visits >= (a.diff ? 6 : 8);
 }
 
 int launch_forward(const LaunchArgs &a) {

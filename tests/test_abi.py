@@ -304,19 +304,22 @@ def _lp(L):
 
 
 @pytest.mark.parametrize("kw,policy,want", [
-    # full attention: AUTO from 8 query tiles of 256 (plain) / 128 (differential) rows at D = 64
+    # full attention: AUTO from 8 query tiles of 256 rows (plain) / 6 of 128 (differential)
     (dict(B=2, H=24, L=4096), AUTO, 2 * 2 * 24 * 4096 * 64 * 2),
     (dict(B=1, H=3, L=1792), AUTO, 0),
     (dict(B=1, H=3, L=1793), AUTO, 2 * 3 * _lp(1793) * 64 * 2),
-    (dict(B=1, H=3, L=896, differential=1), AUTO, 0),
-    (dict(B=1, H=3, L=897, differential=1), AUTO, 3 * 3 * _lp(897) * 64 * 2),
+    (dict(B=1, H=3, L=640, differential=1), AUTO, 0),
+    (dict(B=1, H=3, L=641, differential=1), AUTO, 3 * 3 * _lp(641) * 64 * 2),
     # D = 128: the same 256 / 128 rows per query tile
     (dict(B=1, H=2, L=1792, D=128), AUTO, 0),
     (dict(B=1, H=2, L=1793, D=128), AUTO, 2 * 2 * _lp(1793) * 128 * 2),
-    (dict(B=1, H=2, L=896, D=128, differential=1), AUTO, 0),
-    (dict(B=1, H=2, L=897, D=128, differential=1), AUTO, 3 * 2 * _lp(897) * 128 * 2),
-    # windows: a key tile of a half-width-256 window is visited by 6 query tiles of 128
-    (dict(B=1, H=16, L=8192, window=256, differential=1), AUTO, 0),
+    (dict(B=1, H=2, L=640, D=128, differential=1), AUTO, 0),
+    (dict(B=1, H=2, L=641, D=128, differential=1), AUTO, 3 * 2 * _lp(641) * 128 * 2),
+    # windows: a key tile of a half-width-256 window is visited by 6 query tiles of 128,
+    # of half-width 128 by 4
+    (dict(B=1, H=16, L=8192, window=256, differential=1), AUTO, 3 * 16 * 8192 * 64 * 2),
+    (dict(B=1, H=16, L=8192, window=128, differential=1), AUTO, 0),
+    (dict(B=1, H=16, L=8192, window=256), AUTO, 0),
     (dict(B=1, H=16, L=8192, window=256, differential=1), ALWAYS, 3 * 16 * 8192 * 64 * 2),
     (dict(B=1, H=16, L=8192, window=1024, differential=1), AUTO, 3 * 16 * 8192 * 64 * 2),
     # the single-span kernel (w <= 32, or L <= 256 at D = 64) has no pre-pass
