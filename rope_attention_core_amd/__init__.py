@@ -164,32 +164,62 @@ def _shape_desc(B, H, L, D, window, dtype, out_dtype, differential):
                  dtype, out_dtype, 1 if differential else 0, None)
 
 
+_ws_sizes = {}
+
+
 def workspace_bytes(B, H, L, D, *, window=-1, differential=False, dtype=F16, out_dtype=None, prep="auto"):
     """Bytes of device workspace the pre-pass of this call shape takes under the
-    policy `prep` (0: it does not run)."""
+    policy `prep` (0: it does not run). Answers are cached per shape."""
+    key = (B, H, L, D, window, bool(differential), dtype, dtype if out_dtype is None else out_dtype, prep)
+    n = _ws_sizes.get(key)
+    if n is not None:
+        return n
     if prep not in PREP_POLICIES:
         raise ValueError(f"prep must be one of {tuple(PREP_POLICIES)}")
-    n = ctypes.c_ulonglong(0)
-    d = _shape_desc(B, H, L, D, window, dtype, dtype if out_dtype is None else out_dtype, differential)
-    rc = load_library().sa3attn_workspace_bytes(ctypes.byref(d), PREP_POLICIES[prep], ctypes.byref(n))
+    c = ctypes.c_ulonglong(0)
+    d = _shape_desc(B, H, L, D, window, dtype, key[7], differential)
+    rc = load_library().sa3attn_workspace_bytes(ctypes.byref(d), PREP_POLICIES[prep], ctypes.byref(c))
     if rc != 0:
         raise SA3Error(rc, "sa3attn_workspace_bytes")
-    return int(n.value)
+    _ws_sizes[key] = int(c.value)
+    return _ws_sizes[key]
+
+
+_dt_codes = None
+# torch's current-stream handle getter that builds no Stream object, looked up on the
+# first call (None: use the public torch.cuda.current_stream)
+_raw_stream = False
+
+
+def _dt_of(dtype):
+    global _dt_codes
+    if _dt_codes is None:
+        torch = _torch()
+        _dt_codes = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
+    code = _dt_codes.get(dtype)
+    if code is None:
+        raise TypeError(f"unsupported dtype {dtype}")
+    return code
+
+
+def _check(cond, exc, msg):
+    if not cond:
+        raise exc(msg)
 
 
 def forward(q, k, v, cos, sin, *, window=-1, lam=0.0, scale=None, out=None, out_dtype=None,
             differential=None, stream=None, pairing="adjacent", rotary_dim=None, prep="auto",
             workspace=None):
-    """Run the core through sa3attn_forward_ws (prep "auto" / "always"), or with
-    prep="never" through sa3attn_forward_ex, or sa3attn_forward_general when a tensor is
-    a strided view or a RoPE option is set.
+    """Run the core through sa3attn_forward_ws when the pre-pass runs (prep "auto" at
+    long sequences, "always"), else through sa3attn_forward_ex, or
+    sa3attn_forward_general when a tensor is a strided view or a RoPE option is set.
 
     prep: the pre-pass policy ("auto": when each key tile is visited by >= 8 query
-    tiles; "always"; "never"; "only": the pre-pass alone, out not written; "reuse":
-    the attention kernel alone on a workspace an "always" / "only" call filled from
-    the same k, v, cos, sin); workspace: a uint8 GPU tensor of at least
-    workspace_bytes(...) bytes, allocated here (torch's caching allocator) when not
-    given. All policies give bitwise identical outputs.
+    tiles, 6 for a differential call; "always"; "never"; "only": the pre-pass alone,
+    out not written; "reuse": the attention kernel alone on a workspace an "always" /
+    "only" call filled from the same k, v, cos, sin); workspace: a uint8 GPU tensor of
+    at least workspace_bytes(...) bytes, allocated here (torch's caching allocator) when
+    not given and the pre-pass runs. All policies give bitwise identical outputs.
 
     pairing: "adjacent" (default) or "half" (pairs x[i], x[i + R/2]); rotary_dim: R,
     the leading dims rotated (default D; a multiple of 16), cos/sin then [>=L, R/2].
@@ -201,73 +231,81 @@ def forward(q, k, v, cos, sin, *, window=-1, lam=0.0, scale=None, out=None, out_
     cos, sin: contiguous FP32 [>=L, D/2] on the GPU. ``differential`` defaults to
     q.dim() == 5. ``out_dtype`` defaults to the IO dtype; ``scale`` to 1/sqrt(D).
     Returns ``out`` (allocated contiguous if not given).
+
+    Every shape, dtype, device and layout condition the library cannot see from raw
+    pointers is checked here before the call.
     """
     torch = _torch()
     if differential is None:
         differential = q.dim() == 5
-    B, H, L, D = v.shape
+    vshape = v.shape
+    B, H, L, D = vshape
     if out_dtype is None:
         out_dtype = out.dtype if out is not None else v.dtype
     if scale is None:
         scale = 1.0 / float(D) ** 0.5
     if out is None:
         out = torch.empty((B, H, L, D), dtype=out_dtype, device=v.device)
-    want_qk = (2, B, H, L, D) if differential else (B, H, L, D)
-    for name, t, shape in (("q", q, want_qk), ("k", k, want_qk), ("out", out, (B, H, L, D))):
-        if tuple(t.shape) != shape:
-            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
-    for name, t in (("q", q), ("k", k), ("v", v), ("cos", cos), ("sin", sin), ("out", out)):
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor")
-    for name, t in (("cos", cos), ("sin", sin)):
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
-        if t.stride(-1) != 1:
-            raise ValueError(f"{name} must have a contiguous last dimension")
-    if q.dtype != v.dtype or k.dtype != v.dtype:
-        raise TypeError("q, k and v must share one dtype")
-    if cos.dtype != torch.float32 or sin.dtype != torch.float32:
-        raise TypeError("cos and sin must be float32")
+    want_qk = (2, B, H, L, D) if differential else vshape
+    if q.shape != want_qk or k.shape != want_qk or out.shape != vshape:
+        for name, t, shape in (("q", q, want_qk), ("k", k, want_qk), ("out", out, vshape)):
+            _check(tuple(t.shape) == tuple(shape), ValueError,
+                   f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda and cos.is_cuda and sin.is_cuda and out.is_cuda):
+        for name, t in (("q", q), ("k", k), ("v", v), ("cos", cos), ("sin", sin), ("out", out)):
+            _check(t.is_cuda, ValueError, f"{name} must be a GPU tensor")
+    _check(cos.is_contiguous() and sin.is_contiguous(), ValueError, "cos and sin must be contiguous")
+    qs, ks, vs, os_ = q.stride(), k.stride(), v.stride(), out.stride()
+    if qs[-1] != 1 or ks[-1] != 1 or vs[-1] != 1 or os_[-1] != 1:
+        raise ValueError("q, k, v and out must have a contiguous last dimension")
+    dt = v.dtype
+    _check(q.dtype == dt and k.dtype == dt, TypeError, "q, k and v must share one dtype")
+    _check(cos.dtype == torch.float32 and sin.dtype == torch.float32, TypeError, "cos and sin must be float32")
     R = D if rotary_dim is None else int(rotary_dim)
-    if pairing not in ROPE_PAIRINGS:
-        raise ValueError(f"pairing must be one of {tuple(ROPE_PAIRINGS)}")
-    if cos.dim() != 2 or cos.shape[0] < L or cos.shape[1] != R // 2 or tuple(sin.shape) != tuple(cos.shape):
-        raise ValueError(f"cos/sin must be [>= {L}, {R // 2}]")
-    if out.dtype != out_dtype:
-        raise TypeError("out dtype does not match out_dtype")
-    # for a differential q / k, the data pointer is branch 1; branch 2 is one stride on
-    qq, kk = (q[0], k[0]) if differential else (q, k)
-    d = _Desc(_ptr(qq), _ptr(kk), _ptr(v), _ptr(cos), _ptr(sin), _ptr(out),
-              B, H, L, D, int(window), float(lam), float(scale),
-              _dt_code(v.dtype), _dt_code(out.dtype), 1 if differential else 0,
-              _stream_handle(stream, v.device))
+    _check(pairing in ROPE_PAIRINGS, ValueError, f"pairing must be one of {tuple(ROPE_PAIRINGS)}")
+    cshape = cos.shape
+    _check(len(cshape) == 2 and cshape[0] >= L and cshape[1] == R // 2 and sin.shape == cshape, ValueError,
+           f"cos/sin must be [>= {L}, {R // 2}]")
+    _check(out.dtype == out_dtype, TypeError, "out dtype does not match out_dtype")
+    _check(prep in PREP_POLICIES, ValueError, f"prep must be one of {tuple(PREP_POLICIES)}")
+    io, odt = _dt_of(dt), _dt_of(out.dtype)
+    global _raw_stream
+    if _raw_stream is False:
+        _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if stream is not None:
+        sh = stream.cuda_stream
+    elif _raw_stream is not None:
+        sh = _raw_stream(v.get_device())
+    else:
+        sh = torch.cuda.current_stream(v.device).cuda_stream
+    # for a differential q / k the data pointer is branch 1 (q[0]); branch 2 is one
+    # stride of the leading dimension on
+    d = _Desc(q.data_ptr(), k.data_ptr(), v.data_ptr(), cos.data_ptr(), sin.data_ptr(), out.data_ptr(),
+              B, H, L, D, int(window), float(lam), float(scale), io, odt, 1 if differential else 0, sh)
     lib = load_library()
-    contiguous = all(t.is_contiguous() for t in (q, k, v, out))
-    default_rope = pairing == "adjacent" and R == D
-    if prep not in PREP_POLICIES:
-        raise ValueError(f"prep must be one of {tuple(PREP_POLICIES)}")
     st = None
-    if not contiguous:
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous() and out.is_contiguous()):
         st = _Strides()
-        st.q[:] = qq.stride()[:3]
-        st.k[:] = kk.stride()[:3]
-        st.v[:] = v.stride()[:3]
-        st.out[:] = out.stride()[:3]
-        st.q_branch = q.stride(0) if differential else 0
-        st.k_branch = k.stride(0) if differential else 0
-    rope = None if default_rope else _Rope(ROPE_PAIRINGS[pairing], R)
+        st.q[:] = qs[1:4] if differential else qs[:3]
+        st.k[:] = ks[1:4] if differential else ks[:3]
+        st.v[:] = vs[:3]
+        st.out[:] = os_[:3]
+        st.q_branch = qs[0] if differential else 0
+        st.k_branch = ks[0] if differential else 0
+    rope = None if (pairing == "adjacent" and R == D) else _Rope(ROPE_PAIRINGS[pairing], R)
     st_p = ctypes.byref(st) if st is not None else None
     rope_p = ctypes.byref(rope) if rope is not None else None
-    need = workspace_bytes(B, H, L, D, window=window, differential=differential, dtype=d.dtype,
-                           out_dtype=d.out_dtype, prep=prep)
-    if need > 0:
-        if workspace is None:
+    need = workspace_bytes(B, H, L, D, window=window, differential=differential, dtype=io, out_dtype=odt,
+                           prep=prep)
+    if need > 0 or prep in ("only", "reuse"):
+        if workspace is None and need > 0:
             workspace = torch.empty(need, dtype=torch.uint8, device=v.device)
-        elif not workspace.is_cuda or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
-            raise ValueError("workspace must be a contiguous uint8 GPU tensor")
-        rc = lib.sa3attn_forward_ws(ctypes.byref(d), st_p, rope_p, _ptr(workspace), workspace.numel(),
-                                    PREP_POLICIES[prep])
+        if workspace is not None:
+            _check(workspace.is_cuda and workspace.dtype == torch.uint8 and workspace.is_contiguous(), ValueError,
+                   "workspace must be a contiguous uint8 GPU tensor")
+        rc = lib.sa3attn_forward_ws(ctypes.byref(d), st_p, rope_p,
+                                    workspace.data_ptr() if workspace is not None else None,
+                                    workspace.numel() if workspace is not None else 0, PREP_POLICIES[prep])
         what = "sa3attn_forward_ws"
     elif st is None and rope is None:
         rc = lib.sa3attn_forward_ex(ctypes.byref(d))

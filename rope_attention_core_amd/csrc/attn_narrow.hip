@@ -13,7 +13,13 @@
 // so there is no running rescale), and P.V, and stores. Small workgroups and a small
 // LDS footprint keep several of them resident per CU so that their loads overlap.
 //
-//  * Plain: 4 waves x 32 query rows (BM = 128); windowed span 192 keys.
+//  * Plain, windowed: 4 waves x 32 query rows (BM = 128); span 192 keys.
+//  * Plain, short sequence: the waves split the span instead of the rows (KSPLIT = 4,
+//    or 2 for a 64-key span), BM = 32 (64): each wave takes its share of the keys for
+//    the same 32 rows with its own exact maximum, row sum and O, and the shares are
+//    merged through LDS at the end (O = sum of 2^(m_w - M) O_w, l likewise, M the
+//    largest m_w). A 256-key sequence then runs 8 query tiles per head instead of 2,
+//    which fills 4x more CUs.
 //  * Differential: waves w and w + 2 share 32 rows, one softmax branch each (BM = 64),
 //    windowed span 128 keys; the second branch hands O2 / l2 to the first through LDS.
 //  * Arithmetic per element is the long-span kernel's: RoPE in FP32 with separate
@@ -37,7 +43,8 @@ template <bool DIFF, int NKF>
 struct NarrowShape {
     static constexpr int NT = 256;                    // threads (4 waves)
     static constexpr int NBS = DIFF ? 2 : 1;          // branches staged
-    static constexpr int WPB = DIFF ? 2 : 4;          // query blocks (waves) per branch
+    static constexpr int KSPLIT = (DIFF || !NKF) ? 1 : NKF == 64 ? 2 : 4;   // waves per query block
+    static constexpr int WPB = DIFF ? 2 : 4 / KSPLIT; // query blocks per branch
     static constexpr int BM = WPB * 32;               // query rows per workgroup
     static constexpr int NK = NKF ? NKF : BM + 64;    // keys staged
     static constexpr int NKB = NK / 32;               // 32-key blocks
@@ -57,18 +64,25 @@ template <int IO, bool DIFF, int NKF, bool CONTIG>
 __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTIG && !NKF) ? 3 : 2) void attn_narrow_kernel(Params P) {
     using S = NarrowShape<DIFF, NKF>;
     constexpr int NT = S::NT, NBS = S::NBS, WPB = S::WPB, BM = S::BM, NK = S::NK, NKB = S::NKB;
+    constexpr int KSPLIT = S::KSPLIT;
+    constexpr int NKBW = NKB / KSPLIT;       // 32-key blocks of this wave's share
+    static_assert(NKB % KSPLIT == 0, "key split");
+    // the merge of the key shares reuses the staging area: NT / 64 waves x 34 rows of 64 floats
+    constexpr int MERGE_ELEMS = KSPLIT > 1 ? (NT / 64) * 34 * 64 * 2 : 0;
+    constexpr int SMEM_ELEMS = S::LDS_ELEMS > MERGE_ELEMS ? S::LDS_ELEMS : MERGE_ELEMS;
     constexpr int KC = NK * 8 / NT;          // K chunks (8 elements) per thread per branch
     constexpr int VC = NK * 4 / NT;          // V items (2 keys x 8 d) per thread
     static_assert(NK * 8 % NT == 0 && NK * 4 % NT == 0, "staging split");
     static_assert(!DIFF || S::LDS_ELEMS * 2 >= WPB * 32 * 64 * 4, "LDS too small for the O2 exchange");
-    __shared__ __attribute__((aligned(16))) uint16_t smem[S::LDS_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_ELEMS];
 
     const float NEG_INF = -__builtin_inff();
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wbr = DIFF ? wave / WPB : 0;
-    const int wq = DIFF ? wave % WPB : wave;
+    const int wq = DIFF ? wave % WPB : wave / KSPLIT;
+    const int kq = DIFF ? 0 : wave % KSPLIT;  // this wave's share of the span
     const int r = lane & 31;
     const int g = lane >> 5;
     const int L = P.L;
@@ -217,16 +231,19 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
 
     // ---- scores of this wave's 32 rows over the span: S^T blocks of 32 keys ----------
     const uint16_t *Ks = smem + wbr * S::K_ELEMS;
-    f32x16 s[NKB];
+    // s[j]: keys of 32-key block kb = kq * NKBW + j of the span
+    const int kb0 = kq * NKBW;
+    f32x16 s[NKBW];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+    for (int j = 0; j < NKBW; ++j) {
+        const int kb = kb0 + j;
         u32x4 ka[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) ka[ks] = lds16(Ks + (kb * 32 + r) * S::KS + 16 * ks + 8 * g);
         f32x16 acc = {};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) acc = mfma_qk<IO>(ka[ks], qreg[ks], acc);
-        s[kb] = acc;
+        s[j] = acc;
     }
 
     // valid keys of this lane's query: [max(0, qi - w), min(L - 1, qi + w)], as offsets o
@@ -242,12 +259,12 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
         return (uint32_t)(o - lo) <= span;
     };
 
-    // exact maximum over the span (log2 units), then P = 2^(s c - m) in fp16
+    // exact maximum over this wave's share of the span, then P = 2^(s c - m) in fp16
     float mx = NEG_INF;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int j = 0; j < NKBW; ++j)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, valid(kb, i) ? s[kb][i] : NEG_INF);
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, valid(kb0 + j, i) ? s[j][i] : NEG_INF);
     mx = pair_max(mx);
     const float nb = (mx == NEG_INF) ? 0.0f : -(mx * c);
 
@@ -255,11 +272,12 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
     f32x16 o[2] = {f32x16{}, f32x16{}};
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+    for (int j = 0; j < NKBW; ++j) {
+        const int kb = kb0 + j;
         float e[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const float t = __builtin_fmaf(s[kb][i], c, nb);
+            const float t = __builtin_fmaf(s[j][i], c, nb);
             e[i] = __builtin_amdgcn_exp2f(valid(kb, i) ? t : NEG_INF);
         }
 #pragma unroll
@@ -269,8 +287,8 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
             for (int j = 0; j < 4; ++j) {
                 const f16x2 h = {(_Float16)e[8 * tt + 2 * j], (_Float16)e[8 * tt + 2 * j + 1]};
                 pk[j] = __builtin_bit_cast(uint32_t, h);
-                acc[(kb & 1) * 2 + tt] = __builtin_amdgcn_fdot2(h, f16x2{(_Float16)1.0f, (_Float16)1.0f},
-                                                                acc[(kb & 1) * 2 + tt], false);
+                acc[(j & 1) * 2 + tt] = __builtin_amdgcn_fdot2(h, f16x2{(_Float16)1.0f, (_Float16)1.0f},
+                                                               acc[(j & 1) * 2 + tt], false);
             }
 #pragma unroll
             for (int db = 0; db < 2; ++db) {
@@ -279,7 +297,49 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
             }
         }
     }
-    const float l = pair_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
+    float l = pair_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
+
+    if constexpr (KSPLIT > 1) {
+        // merge the shares of one query block: wave wq * KSPLIT (kq = 0) takes
+        // O = sum_w 2^(b_w - B) O_w and l = sum_w 2^(b_w - B) l_w with b_w = m_w c its
+        // base (log2 units, -inf for a share with no valid key) and B the largest b_w.
+        // Partial of wave v in rows of 64 floats (one per lane): O element e in row
+        // v * 32 + e, b in row NW * 32 + v, l in row NW * 33 + v (NW * 34 rows).
+        constexpr int NW = NT / 64;
+        float *pb = reinterpret_cast<float *>(smem);
+        const float base = (mx == NEG_INF) ? NEG_INF : mx * c;
+        __syncthreads();   // every wave is done with the staged span
+        if (kq != 0) {
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) pb[(wave * 32 + db * 16 + i) * 64 + lane] = o[db][i];
+            pb[(NW * 32 + wave) * 64 + lane] = base;
+            pb[(NW * 33 + wave) * 64 + lane] = l;
+        }
+        __syncthreads();
+        if (kq != 0) return;
+        float bmax = base;
+#pragma unroll
+        for (int v = 1; v < KSPLIT; ++v) bmax = fmaxf(bmax, pb[(NW * 32 + wave + v) * 64 + lane]);
+        // rows past L have no valid key in any share (bmax = -inf); they are not stored
+        const float w0 = __builtin_amdgcn_exp2f(base - bmax);
+        l *= w0;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[db][i] *= w0;
+#pragma unroll
+        for (int v = 1; v < KSPLIT; ++v) {
+            const float wv = __builtin_amdgcn_exp2f(pb[(NW * 32 + wave + v) * 64 + lane] - bmax);
+            l = __builtin_fmaf(wv, pb[(NW * 33 + wave + v) * 64 + lane], l);
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    o[db][i] = __builtin_fmaf(wv, pb[((wave + v) * 32 + db * 16 + i) * 64 + lane], o[db][i]);
+        }
+    }
 
     // ---- epilogue: normalise, subtract, cast, store rows < L -------------------------
     const float inv = 1.0f / l;
@@ -352,7 +412,17 @@ int span_keys(const LaunchArgs &a) { return a.L <= 64 ? 64 : a.L <= 128 ? 128 : 
 
 bool narrow_applies(const LaunchArgs &a) { return span_keys(a) > 0 || (a.window >= 0 && a.window <= 32); }
 
-int narrow_tile_rows(const LaunchArgs &a) { return a.diff ? NarrowShape<true, 0>::BM : NarrowShape<false, 0>::BM; }
+template <int NKF>
+int rows_of(const LaunchArgs &a) { return a.diff ? NarrowShape<true, NKF>::BM : NarrowShape<false, NKF>::BM; }
+
+int narrow_tile_rows(const LaunchArgs &a) {
+    switch (span_keys(a)) {
+        case 64: return rows_of<64>(a);
+        case 128: return rows_of<128>(a);
+        case 256: return rows_of<256>(a);
+        default: return rows_of<0>(a);
+    }
+}
 
 int launch_narrow(const LaunchArgs &a) {
     switch (span_keys(a)) {
