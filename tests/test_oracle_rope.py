@@ -109,10 +109,11 @@ def test_rotate_def_matches_brute():
         np.testing.assert_allclose(got, want, rtol=0, atol=1e-13)
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("io,fmt", [("f16", FMT_F16), ("bf16", FMT_BF16)])
-def test_rotate_method_bit_exact_vs_rational(io, fmt):
-    rng = np.random.default_rng(5)
-    L, D = 40, 64
+def test_rotate_method_bit_exact_vs_rational(io, fmt, D):
+    rng = np.random.default_rng(5 + D)
+    L = 40
     # large positions too, where fp32 table values are irregular
     pos = np.concatenate([np.arange(20), rng.integers(20, 8192, 20)])
     c32, s32 = P.rope_table_f32(8192, D)
@@ -220,11 +221,16 @@ def test_partial_rotary_leaves_the_tail_and_rotates_the_head(rd, pairing):
     np.testing.assert_array_equal(got[:, :rd], head)
 
 
-@pytest.mark.parametrize("rd,pairing", ROTARY + [(64, "adjacent")])
+# head dim 128: rotary widths past 64, and the full width
+ROTARY_128 = [(96, "adjacent"), (96, "half"), (112, "half"), (128, "half"), (128, "adjacent")]
+
+
+@pytest.mark.parametrize("rd,pairing,D", [(r, p, 64) for r, p in ROTARY + [(64, "adjacent")]] +
+                         [(r, p, 128) for r, p in ROTARY_128] + [(32, "half", 128)])
 @pytest.mark.parametrize("io,fmt", [("f16", FMT_F16), ("bf16", FMT_BF16)])
-def test_rotation_options_bit_exact_vs_rational(rd, pairing, io, fmt):
-    rng = np.random.default_rng(40 + rd)
-    L, D = 24, 64
+def test_rotation_options_bit_exact_vs_rational(rd, pairing, D, io, fmt):
+    rng = np.random.default_rng(40 + rd + D)
+    L = 24
     pos = np.concatenate([np.arange(8), rng.integers(8, 8192, 16)])
     c32, s32 = P.rope_table_f32(8192, rd)
     c32, s32 = c32[pos], s32[pos]
@@ -235,10 +241,10 @@ def test_rotation_options_bit_exact_vs_rational(rd, pairing, io, fmt):
     np.testing.assert_array_equal(got, want)
 
 
-@pytest.mark.parametrize("rd,pairing", ROTARY)
-def test_rotate_def_options_match_brute(rd, pairing):
-    rng = np.random.default_rng(50 + rd)
-    L, D = 12, 64
+@pytest.mark.parametrize("rd,pairing,D", [(r, p, 64) for r, p in ROTARY] + [(r, p, 128) for r, p in ROTARY_128])
+def test_rotate_def_options_match_brute(rd, pairing, D):
+    rng = np.random.default_rng(50 + rd + D)
+    L = 12
     x = rng.standard_normal((L, D))
     phi = P.rope_angles(L, rd)
     got = P.rotate_def(x, np.cos(phi), np.sin(phi), pairing=pairing, rotary_dim=rd)
