@@ -123,7 +123,7 @@ def test_method_rotation_mistakes_are_caught(monkeypatch, mut, io):
     monkeypatch.setattr(A, "rotate_method", mut)
     from oracle.brute import FMT_BF16, FMT_F16
     fmt = FMT_F16 if io == "f16" else FMT_BF16
-    assert _any_fails([(TP.test_rotate_method_bit_exact_vs_rational, io, fmt),
+    assert _any_fails([(TP.test_rotate_method_bit_exact_vs_rational, io, fmt, 64),
                        (TA.test_method_mode_matches_brute, io, fmt, False)])
 
 
@@ -236,6 +236,6 @@ def test_rotation_option_mistakes_are_caught(monkeypatch, mut):
               (TP.test_partial_rotary_leaves_the_tail_and_rotates_the_head, 32, "adjacent"),
               (TP.test_partial_rotary_leaves_the_tail_and_rotates_the_head, 32, "half")]
     from oracle.brute import FMT_F16
-    checks += [(TP.test_rotation_options_bit_exact_vs_rational, r, p, "f16", FMT_F16)
-               for r, p in ((32, "half"), (64, "half"), (32, "adjacent"))]
+    checks += [(TP.test_rotation_options_bit_exact_vs_rational, r, p, D, "f16", FMT_F16)
+               for r, p, D in ((32, "half", 64), (64, "half", 64), (32, "adjacent", 64), (96, "half", 128))]
     assert _any_fails(checks)
