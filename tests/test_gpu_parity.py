@@ -180,3 +180,38 @@ def test_scale_values(scale):
                       c, s, scale=scale)
     torch.cuda.synchronize()
     G.assert_parity(out.float().cpu().numpy().astype(np.float64), want, what=f"scale {scale}", out="f16")
+
+
+def _sampled_rows(L, seed, extra=()):
+    rng = np.random.default_rng(seed)
+    edges = [0, 1, 2, 17, 63, 64, 255, 256, L // 2, L - 257, L - 65, L - 18, L - 2, L - 1]
+    picks = np.concatenate([np.asarray(edges, dtype=np.int64), np.asarray(list(extra), dtype=np.int64),
+                            rng.integers(0, L, 24)])
+    return np.unique(np.clip(picks, 0, L - 1))
+
+
+@pytest.mark.parametrize("w", [17, 256])
+def test_long_sequence_windowed_sampled(w):
+    """L = 131072 (16x the SAME-L shape; 32-bit row offsets well above 2^24 bytes) in
+    the differential windowed form: the single-span kernel (w = 17) and the long-span
+    kernel with its pre-pass (w = 256), sampled rows against the oracle."""
+    L = 1 << 17
+    cfg = synth.config("samel_swa", H=1, L=L, window=w, seed=8100 + w)
+    inp = synth.make_inputs(cfg)
+    got = G.run_gpu(cfg, inp)
+    rows = _sampled_rows(L, 8150 + w)
+    want = G.run_oracle_rows(cfg, inp, 0, 0, rows)
+    G.assert_parity(got[0, 0, rows], want, what=f"L=2^17 w={w}", out=cfg.out_dtype)
+
+
+def test_long_sequence_full_sampled():
+    """Full attention at L = 16384 (4x the long latent; 64 query tiles per head, the
+    pre-pass on), bf16 with spiked keys, sampled rows against the oracle."""
+    L = 1 << 14
+    cfg = synth.config("dit_long", B=1, H=2, L=L, seed=8200)
+    inp = synth.make_inputs(cfg)
+    got = G.run_gpu(cfg, inp)
+    for h in range(cfg.H):
+        rows = _sampled_rows(L, 8250 + h)
+        want = G.run_oracle_rows(cfg, inp, 0, h, rows)
+        G.assert_parity(got[0, h, rows], want, what=f"L=2^14 full h{h}", out=cfg.out_dtype)
