@@ -14,8 +14,8 @@
 // LDS footprint keep several of them resident per CU so that their loads overlap.
 //
 //  * Plain, windowed: 4 waves x 32 query rows (BM = 128); span 192 keys.
-//  * Plain, short sequence: the waves split the span instead of the rows (KSPLIT = 4,
-//    or 2 for a 64-key span), BM = 32 (64): each wave takes its share of the keys for
+//  * Plain, short sequence of 65..256 keys: the waves split the span instead of the
+//    rows (KSPLIT = 4), BM = 32: each wave takes its share of the keys for
 //    the same 32 rows with its own exact maximum, row sum and O, and the shares are
 //    merged through LDS at the end (O = sum of 2^(m_w - M) O_w, l likewise, M the
 //    largest m_w). A 256-key sequence then runs 8 query tiles per head instead of 2,
@@ -43,7 +43,9 @@ template <bool DIFF, int NKF>
 struct NarrowShape {
     static constexpr int NT = 256;                    // threads (4 waves)
     static constexpr int NBS = DIFF ? 2 : 1;          // branches staged
-    static constexpr int KSPLIT = (DIFF || !NKF) ? 1 : NKF == 64 ? 2 : 4;   // waves per query block
+    // waves per query block: a 64-key span (L <= 64) is one query tile either way, so
+    // splitting it would only add the merge
+    static constexpr int KSPLIT = (DIFF || NKF == 0 || NKF == 64) ? 1 : 4;
     static constexpr int WPB = DIFF ? 2 : 4 / KSPLIT; // query blocks per branch
     static constexpr int BM = WPB * 32;               // query rows per workgroup
     static constexpr int NK = NKF ? NKF : BM + 64;    // keys staged
