@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cfloat>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -219,6 +220,10 @@ int forward_impl(const sa3attn_desc *d, const sa3attn_strides *sp, const sa3attn
     shape_args(d, a);
     a.lam = d->lambda;
     a.scale_log2 = (float)(std::fabs((double)d->scale) * 1.4426950408889634074);
+    // masked keys carry -inf scores into s * c: with scale 0 use the smallest normal
+    // float instead (-inf * c stays -inf, and every finite s * c still rounds 2^(s c - m)
+    // to exactly 1, the value scale 0 gives)
+    if (a.scale_log2 == 0.0f) a.scale_log2 = FLT_MIN;
     a.neg_scale = d->scale < 0.0f ? 1 : 0;
     a.stream = d->stream;
     a.ws = nullptr;

@@ -358,7 +358,9 @@ __device__ __forceinline__ float max32(const float (&v)[32]) {
 
 // exact maximum of c * s over the valid keys of this lane pair (log2 units)
 template <bool MASK>
-__device__ __forceinline__ float tile_max(const f32x16 (&s)[2], float c, TileMask mk) {
+// With MASK the masked scores are also written back as -inf, so the softmax that follows
+// needs no mask of its own (c > 0: -inf * c + b = -inf, and 2^-inf = 0).
+__device__ __forceinline__ float tile_max(f32x16 (&s)[2], float c, TileMask mk) {
     const float NEG_INF = -__builtin_inff();
     float v[32];
 #pragma unroll
@@ -369,6 +371,7 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[2], float c, TileMas
             if constexpr (MASK) {
                 const int o = kb * 32 + (i >> 2) * 8 + (i & 3);
                 x = ((uint32_t)(o - mk.lo) <= mk.span) ? x : NEG_INF;
+                s[kb][i] = x;
             }
             v[kb * 16 + i] = x;
         }

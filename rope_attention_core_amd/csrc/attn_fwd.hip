@@ -401,7 +401,7 @@ __global__ __launch_bounds__(waves_for<D>() * 64, waves_for<D>() / 4) void attn_
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             u32x4 p[2];
-            softmax_half<MASK>(sb[PC][kb], kb, c, nb, mk, p, part[kb]);
+            softmax_half<false>(sb[PC][kb], kb, c, nb, mk, p, part[kb]);   // masked by tile_max
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
