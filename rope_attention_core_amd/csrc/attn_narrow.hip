@@ -286,9 +286,10 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
         for (int tt = 0; tt < 2; ++tt) {
             u32x4 pk;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const f16x2 h = {(_Float16)e[8 * tt + 2 * j], (_Float16)e[8 * tt + 2 * j + 1]};
-                pk[j] = __builtin_bit_cast(uint32_t, h);
+            for (int jj = 0; jj < 4; ++jj) {
+                const f16x2 h = {(_Float16)e[8 * tt + 2 * jj], (_Float16)e[8 * tt + 2 * jj + 1]};
+                pk[jj] = __builtin_bit_cast(uint32_t, h);
+                // partial sums by block parity and half (summed in a fixed order below)
                 acc[(j & 1) * 2 + tt] = __builtin_amdgcn_fdot2(h, f16x2{(_Float16)1.0f, (_Float16)1.0f},
                                                                acc[(j & 1) * 2 + tt], false);
             }
