@@ -102,7 +102,8 @@ def test_dit_medium_diff_one_head_full():
     G.assert_parity(G.run_gpu(cfg, inp), G.run_oracle(cfg, inp), what="dit_medium_diff H1 L2048")
 
 
-TAILS = [1, 2, 3, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 511, 513, 1291, 1292]
+TAILS = [1, 2, 3, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 511, 513, 1291, 1292,
+         2047, 4093, 4095]
 
 
 @pytest.mark.parametrize("L", TAILS)

@@ -71,6 +71,37 @@ def test_length_one_returns_v_exactly(io):
     assert torch.equal(got.view(torch.int16), v.view(torch.int16))
 
 
+@pytest.mark.parametrize("name,kw", [
+    ("dit_2min", dict(H=2, L=700)),                 # long-span kernel, full attention
+    ("dit_2min", dict(H=2, L=1000, window=100)),    # long-span kernel, masked edge tiles
+    ("dit_2min", dict(H=2, L=2100)),                # long-span kernel with the pre-pass
+    ("samel_w17", dict(H=2, L=500)),                # single-span kernel, differential window
+    ("dit_short", dict(H=2, L=200)),                # single-span kernel, key-split short mode
+])
+@pytest.mark.parametrize("io", ["f16", "bf16"])
+def test_zero_queries_give_window_mean(name, kw, io):
+    """Q = 0: every valid key scores exactly 0, so P = 1 and each output row is the mean
+    of the V rows in its window ((1 - lambda) times it for the differential form), up to
+    the FP32 accumulation of the sums."""
+    import oracle
+    torch = G.torch_mod()
+    cfg = synth.config(name, io=io, out="f32", seed=9400 + kw["L"], **kw)
+    inp, q, k, v = _dev_inputs(cfg)
+    got = _fwd(cfg, torch.zeros_like(q), k, v).double().cpu().numpy()
+    V = oracle.widen_io(inp["v"], io)
+    L, w = cfg.L, cfg.window
+    cs = np.concatenate([np.zeros(V.shape[:2] + (1, V.shape[3])), np.cumsum(V, axis=2)], axis=2)
+    i = np.arange(L)
+    lo = np.maximum(0, i - w) if w >= 0 else np.zeros(L, dtype=np.int64)
+    hi = np.minimum(L - 1, i + w) if w >= 0 else np.full(L, L - 1)
+    want = (cs[:, :, hi + 1, :] - cs[:, :, lo, :]) / (hi - lo + 1)[:, None]
+    if cfg.diff:
+        want = want * (1.0 - cfg.lam)
+    err = np.abs(got - want).max()
+    G.note(f"  q=0 {name} {kw} {io}: max-abs vs window mean {err:.2e}")
+    assert err <= 1e-5 * (1.0 + np.abs(want).max())
+
+
 @pytest.mark.parametrize("w", [-1, 40])
 def test_differential_lambda_zero_equals_plain_bitwise(w):
     cfg = synth.config("samel_swa", H=2, L=900, window=w, lam=0.0)
