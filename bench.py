@@ -22,6 +22,10 @@ its own event pair; its median, min and max are reported as the spread. In that 
 call with the pre-pass is issued as its two kernels (policies "only" then "reuse") with
 an event between them: the roofline uses the attention kernel's own mean duration.
 
+After the timed region, 0.5 s more of headline calls run while a thread reads the
+shader clock (pp_dpm_sclk of the one card) every 10 ms: its median gives the peak at the
+clock the kernel actually ran at, next to the 2400 MHz figure.
+
 Short latents: per-call time inside one captured graph of 96 and of 40 calls (the
 number of fused attention calls in a medium / small DiT forward) at L = 1, 16, 64, 256,
 next to the same figure for a trivial one-element kernel (the launch floor).
@@ -70,6 +74,64 @@ def compulsory_bytes(cfg):
     out = n * (4 if cfg.out_dtype == "f32" else 2)
     table = 2 * cfg.L * (cfg.D // 2) * 4
     return qk + v + out + table
+
+
+def exps(cfg):
+    """Softmax exponentials of the definition: one per in-window pair and branch."""
+    return pairs(cfg) * (2 if cfg.diff else 1)
+
+
+def sclk_file():
+    """The shader-clock file of the one visible card (None unless exactly one exists)."""
+    import glob
+    files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    return files[0] if len(files) == 1 else None
+
+
+def read_sclk_mhz(path):
+    """Current shader clock: the line of pp_dpm_sclk marked with '*'."""
+    with open(path) as f:
+        for ln in f:
+            if "*" in ln:
+                tok = ln.split(":", 1)[1].strip().split()[0].lower()
+                return float(tok.replace("mhz", ""))
+    return None
+
+
+def sample_clock(torch, bench, seconds=0.5):
+    """Median shader clock while the headline call runs back to back for `seconds`
+    (after the timed region, so the sampling thread does not touch it)."""
+    import statistics
+    import threading
+    path = sclk_file()
+    if path is None:
+        return None
+    vals, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                v = read_sclk_mhz(path)
+            except OSError:
+                v = None
+            if v is not None:
+                vals.append(v)
+            stop.wait(0.01)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    t_end = time.perf_counter() + seconds
+    th.start()
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            bench.call()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    if not vals:
+        return None
+    return {"sclk_mhz_median": statistics.median(vals), "sclk_mhz_min": min(vals), "sclk_mhz_max": max(vals),
+            "samples": len(vals), "source": os.path.basename(os.path.dirname(os.path.dirname(path))) +
+            "/device/pp_dpm_sclk, sampled every 10 ms during 0.5 s of headline calls after the timed region"}
 
 
 def kernel_source_sha():
@@ -349,6 +411,12 @@ def main():
     tflops = fl / (ms * 1e-3) / 1e12
     k_tflops = fl / (t["ms_attn_kernel"] * 1e-3) / 1e12   # the attention kernel alone
     traffic = load_traffic()
+    clock = sample_clock(torch, bench)
+    if clock is not None:
+        # the peak scales with the clock: 2516.6 TFLOP/s is quoted at 2400 MHz
+        at_clk = PEAK_BF16_TFLOPS * clock["sclk_mhz_median"] / 2400.0
+        clock["peak_tflops_at_clock"] = round(at_clk, 1)
+        clock["attn_kernel_frac_at_clock"] = round(k_tflops / at_clk, 4) if at_clk > 0 else None
 
     per_config = {}
     if not args.no_configs:
@@ -366,6 +434,7 @@ def main():
                 "tflops": round(f / (r["ms_mean"] * 1e-3) / 1e12, 2),
                 "frac_mfma_peak": round(f / (r["ms_mean"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                 "gbs_compulsory": round(compulsory_bytes(c) / (r["ms_mean"] * 1e-3) / 1e9, 1),
+                "gexp_per_s": round(exps(c) / (r["ms_mean"] * 1e-3) / 1e9, 1),
             }
             if name in COLD_CONFIGS:
                 cm = cold_ms(torch, b)
@@ -403,6 +472,8 @@ def main():
         "ms_min": round(t["ms_min"], 5),
         "ms_max": round(t["ms_max"], 5),
         "frac_of_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "gexp_per_s": round(exps(cfg) / (ms * 1e-3) / 1e9, 1),
+        "clock": clock,
         "kernels_per_step": {
             "attn_prep_kernel_ms": None if t["ms_prep_kernel"] is None else round(t["ms_prep_kernel"], 5),
             "attn_fwd_kernel_ms": round(t["ms_attn_kernel"], 5),
