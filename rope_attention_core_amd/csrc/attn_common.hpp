@@ -356,6 +356,13 @@ __device__ __forceinline__ float max32(const float (&v)[32]) {
     return max3f(max3f(b0, b1, b2), b3, b3);
 }
 
+// exact maximum of c * s over one 32-key half of a tile for this lane pair (log2 units)
+__device__ __forceinline__ float half_max(const f32x16 &s, float c) {
+    const float a0 = max3f(s[0], s[1], s[2]), a1 = max3f(s[3], s[4], s[5]), a2 = max3f(s[6], s[7], s[8]);
+    const float a3 = max3f(s[9], s[10], s[11]), a4 = max3f(s[12], s[13], s[14]);
+    return pair_max(max3f(max3f(a0, a1, a2), max3f(a3, a4, s[15]), a4)) * c;
+}
+
 // exact maximum of c * s over the valid keys of this lane pair (log2 units)
 template <bool MASK>
 // With MASK the masked scores are also written back as -inf, so the softmax that follows

@@ -103,24 +103,33 @@ def test_zero_queries_give_window_mean(name, kw, io):
 
 
 @pytest.mark.parametrize("w", [-1, 40])
-def test_differential_lambda_zero_equals_plain_bitwise(w):
+def test_differential_lambda_zero_equals_plain(w):
+    """Differential at lambda = 0 is the plain core of its first branch. The two paths
+    may pick different exponent bases for a tile (the differential one moves its base
+    only when a P would overflow fp16), so their P round differently: they agree to
+    the same bar as against the oracle, and window-edge rows (masked tiles, where both
+    paths take the exact tile maximum) are covered by w = 40."""
     cfg = synth.config("samel_swa", H=2, L=900, window=w, lam=0.0)
     inp, q, k, v = _dev_inputs(cfg)
     diff = _fwd(cfg, q, k, v)
     plain_cfg = cfg.with_(diff=False)
     plain = _fwd(plain_cfg, q[0].contiguous(), k[0].contiguous(), v)
-    torch = G.torch_mod()
-    assert torch.equal(diff, plain)
+    G.torch_mod().cuda.synchronize()
+    G.assert_parity(diff.float().cpu().numpy().astype(np.float64), plain.float().cpu().numpy().astype(np.float64),
+                    what=f"lambda 0 vs plain, w={w}", out=cfg.out_dtype)
 
 
 def test_identical_branches_give_one_minus_lambda():
+    """With Q2 = Q1 and K2 = K1 both branches compute the same bits, so the output is
+    x - lambda * x for x the first branch's normalised output (lambda = 0), up to the
+    FP32 rounding of the subtraction."""
     cfg = synth.config("samel_swa", H=2, L=600, window=30, lam=0.8)
     inp, q, k, v = _dev_inputs(cfg)
     q2 = G.torch_mod().stack([q[0], q[0]]).contiguous()
     k2 = G.torch_mod().stack([k[0], k[0]]).contiguous()
     d = _fwd(cfg, q2, k2, v).double()
-    plain = _fwd(cfg.with_(diff=False), q[0].contiguous(), k[0].contiguous(), v).double()
-    assert (d - 0.2 * plain).abs().max().item() < 1e-6
+    x = _fwd(cfg.with_(lam=0.0), q2, k2, v).double()
+    assert (d - 0.2 * x).abs().max().item() < 1e-6
 
 
 def _embed(t, pad_elems):
