@@ -184,10 +184,13 @@ int sa3attn_forward_general(const sa3attn_desc *desc, const sa3attn_strides *str
  * library first runs a pre-pass kernel that rotates K (each branch) and converts and
  * transposes V once, into the workspace, and the attention kernel then copies its
  * key tiles from there. Outputs are bitwise identical to sa3attn_forward_general's.
- *   policy: SA3_PREP_AUTO runs the pre-pass when a key tile is visited by at least
- *     8 query tiles of a plain call or 6 of a differential one (full attention:
- *     L > 1792 plain, L > 640 differential; query tiles of 256 and 128 rows; a window
- *     of half-width w: about (2w + 64) / tile rows + 1 visits); SA3_PREP_ALWAYS whenever the call
+ *   policy: SA3_PREP_AUTO runs the pre-pass when the grid has more workgroups than
+ *     the current device has compute units (workgroups = B x H x ceil(L / tile rows);
+ *     256 compute units are assumed when no device is current) and a key tile is
+ *     visited by at least 12 query tiles of a plain call or 9 of a differential one
+ *     (full attention: L > 2816 plain, L > 1024 differential; query tiles of 256 and
+ *     128 rows; a window of half-width w: about (2w + 64) / tile rows + 1 visits), the
+ *     shapes where it measured faster; SA3_PREP_ALWAYS whenever the call
  *     takes the long-span kernel; SA3_PREP_NEVER never. SA3_PREP_ONLY enqueues the
  *     pre-pass alone (out is not written) and SA3_PREP_REUSE the attention kernel
  *     alone, reading a workspace that an earlier ALWAYS or ONLY call filled from the

@@ -214,8 +214,9 @@ def forward(q, k, v, cos, sin, *, window=-1, lam=0.0, scale=None, out=None, out_
     long sequences, "always"), else through sa3attn_forward_ex, or
     sa3attn_forward_general when a tensor is a strided view or a RoPE option is set.
 
-    prep: the pre-pass policy ("auto": when each key tile is visited by >= 8 query
-    tiles, 6 for a differential call; "always"; "never"; "only": the pre-pass alone,
+    prep: the pre-pass policy ("auto": when the grid has more workgroups than the
+    device has compute units and each key tile is visited by >= 12 query tiles, 9 for
+    a differential call; "always"; "never"; "only": the pre-pass alone,
     out not written; "reuse": the attention kernel alone on a workspace an "always" /
     "only" call filled from the same k, v, cos, sin); workspace: a uint8 GPU tensor of
     at least workspace_bytes(...) bytes, allocated here (torch's caching allocator) when

@@ -44,6 +44,28 @@ int check_device() {
     return s == 1 ? SA3_OK : SA3_ERR_DEVICE;
 }
 
+// Compute units of the current device, cached per device; 256 (an MI355X) when there is
+// no usable device, so that host-only queries answer the same as calls on that part.
+constexpr int kDefaultCUs = 256;
+std::atomic<int> g_dev_cus[kMaxDevices];
+
+int device_cus() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return kDefaultCUs;
+    }
+    int n = g_dev_cus[dev].load(std::memory_order_acquire);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+            (void)hipGetLastError();
+            return kDefaultCUs;
+        }
+        g_dev_cus[dev].store(n, std::memory_order_release);
+    }
+    return n;
+}
+
 bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
     const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
     return x < y + nb && y < x + na;
@@ -119,6 +141,7 @@ int check_shape(const sa3attn_desc *d) {
 
 // The launch fields that decide which kernel runs (and so the workspace size).
 void shape_args(const sa3attn_desc *d, sa3::LaunchArgs &a) {
+    a.n_cu = device_cus();
     a.B = d->B;
     a.H = d->H;
     a.L = d->L;

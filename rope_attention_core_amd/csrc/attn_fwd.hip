@@ -569,16 +569,22 @@ unsigned long long prep_bytes(const LaunchArgs &a) {
 }
 
 // The fused staging rotates and transposes a key tile once per query tile that visits
-// it; the pre-pass costs about one extra read and write of K and V. Measured: at L = 4096
-// (16 / 32 visits) 5-17% faster; a differential window of half-width 256 (6 visits,
-// two K tiles staged per key tile) 2.5% faster; plain full attention at L = 1292 (6
-// visits) 2% slower. So: 6 or more visits for differential calls, 8 for plain ones.
+// it; the pre-pass does that once but adds a pass over K and V (about one more read and
+// write of each) before the attention kernel can start. Measured over 18 shapes (plain
+// and differential, full and windowed, L 768-8192): it pays only when the grid has more
+// workgroups than the device has compute units (a single round of workgroups pays the
+// pass in full: 1-4% slower even at 12-16 visits) and each key tile is visited by at
+// least 12 query tiles (plain; 10 visits break even) or 9 (differential; 8 break
+// even): then 1-10% faster, e.g. 6% at L = 4096 and 6% for a differential window of
+// half-width 768; a differential window of half-width 256 (6 visits) runs 3% faster
+// without it.
 bool prep_pays(const LaunchArgs &a) {
     if (use_narrow(a)) return false;
     const int bm = tile_rows(a);
     const long long n_qtiles = ((long long)a.L + bm - 1) / bm;
     const long long visits = a.window < 0 ? n_qtiles : std::min(n_qtiles, (2ll * a.window + BN + bm - 1) / bm + 1);
-    return visits >= (a.diff ? 6 : 8);
+    const long long wgs = n_qtiles * a.B * a.H;
+    return wgs > a.n_cu && visits >= (a.diff ? 9 : 12);
 }
 
 int launch_forward(const LaunchArgs &a) {

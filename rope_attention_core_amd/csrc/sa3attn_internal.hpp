@@ -32,6 +32,7 @@ struct LaunchArgs {
     int prep;               // the long-span kernel reads K and V from the pre-pass workspace
     int run_prep;           // with prep: enqueue the pre-pass (0: ws already holds its result)
     int run_main;           // enqueue the attention kernel (0: only the pre-pass)
+    int n_cu;               // compute units of the current device (256 when there is none)
     void *stream;           // hipStream_t
 };
 

@@ -304,22 +304,29 @@ def _lp(L):
 
 
 @pytest.mark.parametrize("kw,policy,want", [
-    # full attention: AUTO from 8 query tiles of 256 rows (plain) / 6 of 128 (differential)
+    # AUTO: more workgroups than the 256 compute units assumed without a device, and at
+    # least 12 query tiles of 256 rows (plain) / 9 of 128 (differential) per key tile
     (dict(B=2, H=24, L=4096), AUTO, 2 * 2 * 24 * 4096 * 64 * 2),
-    (dict(B=1, H=3, L=1792), AUTO, 0),
-    (dict(B=1, H=3, L=1793), AUTO, 2 * 3 * _lp(1793) * 64 * 2),
-    (dict(B=1, H=3, L=640, differential=1), AUTO, 0),
-    (dict(B=1, H=3, L=641, differential=1), AUTO, 3 * 3 * _lp(641) * 64 * 2),
+    (dict(B=1, H=24, L=2816), AUTO, 0),                                  # 11 visits
+    (dict(B=1, H=24, L=2817), AUTO, 2 * 24 * _lp(2817) * 64 * 2),        # 12 visits, 288 WGs
+    (dict(B=1, H=16, L=3072), AUTO, 0),                                  # 12 visits, 192 WGs
+    (dict(B=1, H=32, L=1024, differential=1), AUTO, 0),                  # 8 visits
+    (dict(B=1, H=32, L=1025, differential=1), AUTO, 3 * 32 * _lp(1025) * 64 * 2),   # 9, 288 WGs
+    (dict(B=1, H=16, L=2048, differential=1), AUTO, 0),                  # 16 visits, 256 WGs
+    (dict(B=1, H=16, L=2049, differential=1), AUTO, 3 * 16 * _lp(2049) * 64 * 2),   # 17, 272 WGs
     # D = 128: the same 256 / 128 rows per query tile
-    (dict(B=1, H=2, L=1792, D=128), AUTO, 0),
-    (dict(B=1, H=2, L=1793, D=128), AUTO, 2 * 2 * _lp(1793) * 128 * 2),
-    (dict(B=1, H=2, L=640, D=128, differential=1), AUTO, 0),
-    (dict(B=1, H=2, L=641, D=128, differential=1), AUTO, 3 * 2 * _lp(641) * 128 * 2),
-    # windows: a key tile of a half-width-256 window is visited by 6 query tiles of 128,
-    # of half-width 128 by 4
-    (dict(B=1, H=16, L=8192, window=256, differential=1), AUTO, 3 * 16 * 8192 * 64 * 2),
-    (dict(B=1, H=16, L=8192, window=128, differential=1), AUTO, 0),
-    (dict(B=1, H=16, L=8192, window=256), AUTO, 0),
+    (dict(B=1, H=24, L=2816, D=128), AUTO, 0),
+    (dict(B=1, H=24, L=2817, D=128), AUTO, 2 * 24 * _lp(2817) * 128 * 2),
+    (dict(B=1, H=32, L=1024, D=128, differential=1), AUTO, 0),
+    (dict(B=1, H=32, L=1025, D=128, differential=1), AUTO, 3 * 32 * _lp(1025) * 128 * 2),
+    # windows: a key tile of a half-width-w window is visited by about (2w + 64) / rows + 1
+    # query tiles: 6 at w = 256, 8 at w = 384, 9 at w = 448 (128 rows); 10 at w = 1024,
+    # 12 at w = 1280 (256 rows)
+    (dict(B=1, H=16, L=8192, window=256, differential=1), AUTO, 0),
+    (dict(B=1, H=16, L=8192, window=384, differential=1), AUTO, 0),
+    (dict(B=1, H=16, L=8192, window=448, differential=1), AUTO, 3 * 16 * 8192 * 64 * 2),
+    (dict(B=1, H=16, L=8192, window=1024), AUTO, 0),
+    (dict(B=1, H=16, L=8192, window=1280), AUTO, 2 * 16 * 8192 * 64 * 2),
     (dict(B=1, H=16, L=8192, window=256, differential=1), ALWAYS, 3 * 16 * 8192 * 64 * 2),
     (dict(B=1, H=16, L=8192, window=1024, differential=1), AUTO, 3 * 16 * 8192 * 64 * 2),
     # the single-span kernel (w <= 32, or L <= 256 at D = 64) has no pre-pass
