@@ -447,6 +447,8 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, bench.inputs_host)
+        # the whole GPU step's rate over the oracle's, on the same workload
+        cpu["gpu_over_oracle"] = round(tflops / cpu["value"], 1) if cpu["value"] > 0 else None
 
     line = {
         "metric": "attention-core TFLOP/s at L=4096 (DiT long latent, fused RoPE attention)",
