@@ -167,10 +167,21 @@ def _shape_desc(B, H, L, D, window, dtype, out_dtype, differential):
 _ws_sizes = {}
 
 
+def _current_device():
+    """torch's current GPU index, or -1 without one (host-only size queries)."""
+    torch = _torch()
+    try:
+        return torch.cuda.current_device() if torch.cuda.is_available() else -1
+    except RuntimeError:
+        return -1
+
+
 def workspace_bytes(B, H, L, D, *, window=-1, differential=False, dtype=F16, out_dtype=None, prep="auto"):
     """Bytes of device workspace the pre-pass of this call shape takes under the
-    policy `prep` (0: it does not run). Answers are cached per shape."""
-    key = (B, H, L, D, window, bool(differential), dtype, dtype if out_dtype is None else out_dtype, prep)
+    policy `prep` (0: it does not run) on the current device (the AUTO decision
+    depends on its compute-unit count). Answers are cached per shape and device."""
+    key = (B, H, L, D, window, bool(differential), dtype, dtype if out_dtype is None else out_dtype, prep,
+           _current_device())
     n = _ws_sizes.get(key)
     if n is not None:
         return n
@@ -255,6 +266,17 @@ def forward(q, k, v, cos, sin, *, window=-1, lam=0.0, scale=None, out=None, out_
     if not (q.is_cuda and k.is_cuda and v.is_cuda and cos.is_cuda and sin.is_cuda and out.is_cuda):
         for name, t in (("q", q), ("k", k), ("v", v), ("cos", cos), ("sin", sin), ("out", out)):
             _check(t.is_cuda, ValueError, f"{name} must be a GPU tensor")
+    # the library launches on the current device: every tensor must live there
+    dev = v.get_device()
+    if not (q.get_device() == dev and k.get_device() == dev and cos.get_device() == dev and
+            sin.get_device() == dev and out.get_device() == dev and
+            (workspace is None or workspace.get_device() == dev)):
+        raise ValueError("q, k, v, cos, sin, out (and workspace) must be on one GPU")
+    if dev != torch.cuda.current_device():
+        with torch.cuda.device(dev):
+            return forward(q, k, v, cos, sin, window=window, lam=lam, scale=scale, out=out, out_dtype=out_dtype,
+                           differential=differential, stream=stream, pairing=pairing, rotary_dim=rotary_dim,
+                           prep=prep, workspace=workspace)
     _check(cos.is_contiguous() and sin.is_contiguous(), ValueError, "cos and sin must be contiguous")
     qs, ks, vs, os_ = q.stride(), k.stride(), v.stride(), out.stride()
     if qs[-1] != 1 or ks[-1] != 1 or vs[-1] != 1 or os_[-1] != 1:
@@ -325,6 +347,12 @@ def forward_short(q, k, v, cos, sin, out, *, window=-1, lam=0.0, scale=None, str
     Output dtype equals the IO dtype; differential exactly when lam != 0.
     """
     torch = _torch()
+    dev = v.get_device()
+    _check(dev >= 0 and all(t.get_device() == dev for t in (q, k, cos, sin, out)), ValueError,
+           "q, k, v, cos, sin and out must be on one GPU")
+    if dev != torch.cuda.current_device():
+        with torch.cuda.device(dev):
+            return forward_short(q, k, v, cos, sin, out, window=window, lam=lam, scale=scale, stream=stream)
     B, H, L, D = v.shape
     if scale is None:
         scale = 1.0 / float(D) ** 0.5
