@@ -54,6 +54,8 @@ struct Params {
     // [B*H][Lp/64][D][64] fp16, each 64-key tile transposed (Lp = L rounded up to 64)
     uint16_t *kw, *vw;
     int ws_tiles;                 // Lp / 64
+    int n_items;                  // query tiles x B x H (the long-span kernel's work items)
+    int cp;                       // every item spans >= 3 key tiles (its pipeline may run on)
 };
 
 // Kernel parameters common to every instance (n_qtiles and window are set by the caller).
@@ -83,6 +85,8 @@ inline Params make_params(const LaunchArgs &a) {
     P.L = a.L;
     P.window = a.window;
     P.n_qtiles = 1;
+    P.n_items = 0;
+    P.cp = 0;
     P.out_dtype = a.out_dtype;
     P.neg_scale = a.neg_scale;
     P.lam = a.lam;
