@@ -85,6 +85,8 @@ constexpr int waves_for() { return 8; }
 // registers free. D: head dim, 64 or 128. PRE: K and V come from the pre-pass
 // workspace (attn_prep.hip), already rotated / converted and in the LDS layout, so
 // staging a tile is a copy (CONTIG then concerns only q, out and the table of q).
+// PERS: persistent grid (each workgroup takes several query tiles in turn, see the file
+// header); the one-round instances (false) take one query tile per workgroup.
 template <int IO, bool DIFF, bool CONTIG, int D, bool PRE, bool PERS>
 __global__ __launch_bounds__(waves_for<D>() * 64, waves_for<D>() / 4) void attn_fwd_kernel(Params P) {
     constexpr int NW = waves_for<D>();
