@@ -38,7 +38,12 @@ namespace {
 // windowed mode, the span [q0 - w, q0 + BM - 1 + w] of a window of half-width w <= 32
 // (BM + 64 keys). NKF > 0: short-sequence mode, the whole sequence [0, L) with L <= NKF
 // and any window. The V^T stride keeps the 16-byte operand reads of 16 consecutive
-// rows on distinct banks.
+// rows on distinct banks. The K rows are padded to 72 elements for the same purpose,
+// except in the differential windowed mode, whose 53 KB would then miss three
+// workgroups per CU (LDS is granted in 2 KB units): there the rows are 64 elements
+// and the 16-byte chunk c of row k is stored at chunk c ^ (k & 7), which puts any 8
+// consecutive rows' reads of one chunk, and one row's 8 chunk writes, on distinct
+// banks without the padding.
 template <bool DIFF, int NKF>
 struct NarrowShape {
     static constexpr int NT = 256;                    // threads (4 waves)
@@ -50,7 +55,8 @@ struct NarrowShape {
     static constexpr int BM = WPB * 32;               // query rows per workgroup
     static constexpr int NK = NKF ? NKF : BM + 64;    // keys staged
     static constexpr int NKB = NK / 32;               // 32-key blocks
-    static constexpr int KS = 72;                     // K row stride
+    static constexpr bool SWZ = DIFF && NKF == 0;     // swizzled, unpadded K rows
+    static constexpr int KS = SWZ ? 64 : 72;          // K row stride
     static constexpr int VS = NK + 8;                 // V^T row stride
     static constexpr int K_ELEMS = NK * KS;
     static constexpr int V_ELEMS = HD * VS;
@@ -196,7 +202,7 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
 #pragma unroll
     for (int i = 0; i < KC; ++i) {
         const int it = tid + NT * i;
-        const int at = (it >> 3) * S::KS + (it & 7) * 8;
+        const int at = (it >> 3) * S::KS + ((it & 7) ^ (S::SWZ ? (it >> 3) & 7 : 0)) * 8;
 #pragma unroll
         for (int br = 0; br < NBS; ++br) {
             u32x4 rot;
@@ -241,7 +247,8 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
         const int kb = kb0 + j;
         u32x4 ka[4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) ka[ks] = lds16(Ks + (kb * 32 + r) * S::KS + 16 * ks + 8 * g);
+        for (int ks = 0; ks < 4; ++ks)
+            ka[ks] = lds16(Ks + (kb * 32 + r) * S::KS + ((2 * ks + g) ^ (S::SWZ ? r & 7 : 0)) * 8);
         f32x16 acc = {};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) acc = mfma_qk<IO>(ka[ks], qreg[ks], acc);
