@@ -65,3 +65,32 @@ def test_persistent_grid_sampled_parity(name, kw):
         got = outs["never"][b, h, rows].float().cpu().numpy().astype(np.float64)
         assert np.isfinite(got).all()
         G.assert_parity(got, want, what=f"{name} {kw} (b,h)=({b},{h})", out=cfg.out_dtype)
+
+
+def test_persistent_grid_in_a_graph():
+    """A persistent call captured in a graph: every replay gives the eager bits."""
+    torch = G.torch_mod()
+    cfg = synth.config("samel_swa", B=1, H=16, L=4096, window=300, seed=13200)
+    inp = synth.make_inputs(cfg)
+    q, k, v = (G.to_device(inp[n], cfg.io) for n in ("q", "k", "v"))
+    c, s = G.device_table(cfg.L, cfg.D, cfg.base)
+    call = dict(window=cfg.window, lam=cfg.lam, scale=cfg.scale, differential=True,
+                out_dtype=G.out_torch_dtype(cfg.out_dtype))
+    eager = G.sa3.forward(q, k, v, c, s, **call)
+    out = torch.empty_like(eager)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            G.sa3.forward(q, k, v, c, s, out=out, **call)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        G.sa3.forward(q, k, v, c, s, out=out, **call)
+    for i in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i} differs from eager"
