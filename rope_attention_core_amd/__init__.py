@@ -230,8 +230,10 @@ def forward(q, k, v, cos, sin, *, window=-1, lam=0.0, scale=None, out=None, out_
     a differential call; "always"; "never"; "only": the pre-pass alone,
     out not written; "reuse": the attention kernel alone on a workspace an "always" /
     "only" call filled from the same k, v, cos, sin); workspace: a uint8 GPU tensor of
-    at least workspace_bytes(...) bytes, allocated here (torch's caching allocator) when
-    not given and the pre-pass runs. All policies give bitwise identical outputs.
+    at least workspace_bytes(...) bytes, allocated here (torch's caching allocator, on
+    the current stream and recorded on `stream` when one is given) when not given and
+    the pre-pass runs; a caller's workspace used on several streams is the caller's to
+    order. All policies give bitwise identical outputs.
 
     pairing: "adjacent" (default) or "half" (pairs x[i], x[i + R/2]); rotary_dim: R,
     the leading dims rotated (default D; a multiple of 16), cos/sin then [>=L, R/2].
@@ -323,6 +325,11 @@ def forward(q, k, v, cos, sin, *, window=-1, lam=0.0, scale=None, out=None, out_
     if need > 0 or prep in ("only", "reuse"):
         if workspace is None and need > 0:
             workspace = torch.empty(need, dtype=torch.uint8, device=v.device)
+            if stream is not None:
+                # allocated on the current stream and released when this call returns:
+                # the allocator must not hand the block to other work before the
+                # kernels queued on `stream` have read it
+                workspace.record_stream(stream)
         if workspace is not None:
             _check(workspace.is_cuda and workspace.dtype == torch.uint8 and workspace.is_contiguous(), ValueError,
                    "workspace must be a contiguous uint8 GPU tensor")

@@ -6,8 +6,8 @@ every case must give the same bits as the fused path (prep="never"), and the res
 also compared with the oracle element by element on a subset. Cases cover plain and
 differential attention, full and wide windows, both IO dtypes, ragged lengths (the
 workspace's tail rows), strided views, the RoPE options, head dim 128, a workspace
-full of NaN bits on entry, reuse of one workspace by calls of different shapes, and
-graph capture.
+full of NaN bits on entry, reuse of one workspace by calls of different shapes, graph
+capture, and a workspace the binding allocates for a call queued on another stream.
 """
 
 import numpy as np
@@ -176,3 +176,26 @@ def test_prepare_once_then_reuse_for_several_queries():
         got = _call(cfg, qq, k, v, prep="reuse", workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(got, want)
+
+
+def test_internal_workspace_on_a_side_stream():
+    """The binding allocates the workspace (on torch's current stream) for a call queued
+    on another stream: it stays reserved until that stream has run the call, so
+    same-sized blocks allocated and filled on the current stream meanwhile leave the
+    results equal to the fused path's."""
+    torch = G.torch_mod()
+    cfg = synth.config("dit_2min", H=4, L=2000, seed=9880)
+    _, q, k, v = _inputs(cfg)
+    fused = _call(cfg, q, k, v, prep="never")
+    nb = G.sa3.workspace_bytes(cfg.B, cfg.H, cfg.L, cfg.D, prep="always")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs, fills = [], []
+    for i in range(3):
+        out = torch.empty_like(fused)
+        _call(cfg, q, k, v, prep="always", out=out, stream=side)
+        fills.append(torch.full((nb,), 0xFF, dtype=torch.uint8, device="cuda"))
+        outs.append(out)
+    torch.cuda.synchronize()
+    for i, out in enumerate(outs):
+        assert torch.equal(out, fused), f"call {i} on the side stream differs"
