@@ -17,8 +17,9 @@
  *    sized to a maximum length (sa3_trt README, section "DiT precision").
  *  - M is a sliding window of half-width w, "+-WINDOW" around each query
  *    (Stable Audio 3 TensorRT engines README, section "Building your own").
- *  - The differential variant shares V between two softmax branches and subtracts
- *    in FP32 on FP32 accumulators (same README, section "How the kernels differ").
+ *  - The differential variant shares V between two softmax branches; the two
+ *    branch results are subtracted after accumulation, in FP32 (same README,
+ *    section "How the kernels differ").
  *  - The forward must be capturable into a stream graph with no host callbacks
  *    (same README, section "Why JIT breaks on sm_120").
  *
@@ -55,8 +56,12 @@
  *  - Numerics: QK^T and P.V run on MFMA with FP32 accumulation; the running
  *    softmax max and sum are FP32. P is rounded to fp16 before P.V for both IO
  *    dtypes; with bf16 inputs V is converted to fp16 as it is staged, which is
- *    exact for |v| in [2^-14, 65504]; a bf16 |v| above 65504 overflows to inf and
- *    makes the affected outputs non-finite.
+ *    exact for |v| in [2^-14, 65504]. A bf16 V beyond fp16's range (|v| >= 65536,
+ *    up to bf16's largest finite value) is handled on the device: a workgroup whose
+ *    accumulators come out non-finite finds the largest finite |v| of the keys it
+ *    visited and redoes its work with V scaled by an exact power of two, undone in
+ *    the output (so large finite V gives finite, accurate results; that workgroup
+ *    takes about twice as long). Non-finite inputs give non-finite outputs.
  */
 #ifndef SA3ATTN_H
 #define SA3ATTN_H

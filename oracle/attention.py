@@ -9,15 +9,15 @@ the RoPE cast-back is fp64 and unrounded, so the oracle is the exact result that
 FP32-accumulating kernel approximates.
 
 Sliding window: key j is masked for query i when |i - j| > w, w being a half-width
-(TensorRT engines README, section "Building your own": a block of BLOCK_N queries
-with window WINDOW needs BLOCK_N + 2*WINDOW keys, "+-17"). w < 0 means full
-attention. There is no causal mask on this path.
+(TensorRT engines README, section "Building your own": the window reaches WINDOW keys
+to either side of a query, and a block of queries needs its own rows plus twice
+WINDOW keys). w < 0 means full attention. There is no causal mask on this path.
 
 Differential attention: out = softmax(S1) V - lambda * softmax(S2) V with the same
-mask on both branches and RoPE applied to Q1, K1, Q2, K2; the subtraction happens on
-the accumulated results (TensorRT engines README, section "How the kernels differ":
-the subtraction stays in FP32 on FP32 accumulators). No per-head norm or extra
-factor is applied (none is described as part of the core).
+mask on both branches and RoPE applied to Q1, K1, Q2, K2; the two branch results are
+subtracted after accumulation, in FP32 (TensorRT engines README, section "How the
+kernels differ"). No per-head norm or extra factor is applied (none is described as
+part of the core).
 
 Evaluation order is the definition's. Rows are computed in chunks because each
 output row depends only on its own row of scores; for a window only the keys with

@@ -20,7 +20,9 @@ __all__ = [
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libsa3attn.so")
+# SA3ATTN_LIB may name another build of the same library (for instance the copy whose
+# host code runs under sanitizers, see build.py); it must exist
+_LIB_PATH = os.environ.get("SA3ATTN_LIB") or os.path.join(_HERE, "libsa3attn.so")
 
 F16, BF16, F32 = 0, 1, 2
 EXPORTS = (
@@ -231,9 +233,10 @@ def forward(q, k, v, cos, sin, *, window=-1, lam=0.0, scale=None, out=None, out_
     out not written; "reuse": the attention kernel alone on a workspace an "always" /
     "only" call filled from the same k, v, cos, sin); workspace: a uint8 GPU tensor of
     at least workspace_bytes(...) bytes, allocated here (torch's caching allocator, on
-    the current stream and recorded on `stream` when one is given) when not given and
-    the pre-pass runs; a caller's workspace used on several streams is the caller's to
-    order. All policies give bitwise identical outputs.
+    `stream` when one is given, else on the current stream) when not given and the
+    pre-pass runs; a caller's workspace used on several streams is the caller's to
+    order; "only" and "reuse" need the caller's workspace (ValueError without one).
+    All policies give bitwise identical outputs.
 
     pairing: "adjacent" (default) or "half" (pairs x[i], x[i + R/2]); rotary_dim: R,
     the leading dims rotated (default D; a multiple of 16), cos/sin then [>=L, R/2].
@@ -324,12 +327,17 @@ def forward(q, k, v, cos, sin, *, window=-1, lam=0.0, scale=None, out=None, out_
                            prep=prep)
     if need > 0 or prep in ("only", "reuse"):
         if workspace is None and need > 0:
-            workspace = torch.empty(need, dtype=torch.uint8, device=v.device)
+            # "reuse" reads a workspace an earlier call filled, and "only" fills one for
+            # later calls: a workspace made here would be uninitialised, or dropped
+            _check(prep not in ("only", "reuse"), ValueError,
+                   f'prep="{prep}" needs the caller\'s workspace (workspace_bytes(...) bytes)')
             if stream is not None:
-                # allocated on the current stream and released when this call returns:
-                # the allocator must not hand the block to other work before the
-                # kernels queued on `stream` have read it
-                workspace.record_stream(stream)
+                # the block belongs to the stream that uses it, so the caching allocator
+                # hands it to other work only in that stream's order
+                with torch.cuda.stream(stream):
+                    workspace = torch.empty(need, dtype=torch.uint8, device=v.device)
+            else:
+                workspace = torch.empty(need, dtype=torch.uint8, device=v.device)
         if workspace is not None:
             _check(workspace.is_cuda and workspace.dtype == torch.uint8 and workspace.is_contiguous(), ValueError,
                    "workspace must be a contiguous uint8 GPU tensor")

@@ -336,6 +336,76 @@ __device__ __forceinline__ void softmax_half(const f32x16 &s, int kb, float c, f
     rowsum = acc[0] + acc[1];
 }
 
+// ---- range guard of the bf16 -> fp16 V conversion -------------------------------
+// P.V runs on fp16 operands for both IO types, and a bf16 V with |v| >= 65536 has no
+// fp16 value (it would become inf). The kernels stage V unscaled; when an accumulator
+// of a workgroup turns out non-finite they look up the largest finite |v| of the keys
+// that workgroup visited and, if it lies beyond fp16's range, redo the work with V
+// multiplied by 2^-shift while it is staged (exact: a power of two, the scaled values
+// keep their 8 significant bits inside fp16's normal range) and the output multiplied
+// by 2^shift. Finite inputs within fp16's range never take that path.
+
+// Largest finite |x| among the 8 bf16 values of a 16-byte chunk, as its bit pattern
+// without the sign (infinities and NaNs count as 0).
+__device__ __forceinline__ uint32_t bf16_finite_absmax(u32x4 w) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = w[j] & 0x7fffu, hi = (w[j] >> 16) & 0x7fffu;
+        m = max(m, lo < 0x7f80u ? lo : 0u);
+        m = max(m, hi < 0x7f80u ? hi : 0u);
+    }
+    return m;
+}
+
+// The shift that brings the bf16 magnitude with bits `absbits` below 2^16: the values
+// of its binade then scale to at most 65280, an fp16 value (0 when it already fits).
+__device__ __forceinline__ int vshift_of(uint32_t absbits) {
+    const int e = (int)(absbits >> 7);   // biased exponent
+    return e >= 143 ? e - 142 : 0;
+}
+
+// 2^e as a float, -126 <= e <= 127.
+__device__ __forceinline__ float exp2i(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+
+// Whether p holds on any lane of the workgroup's NW waves (all threads call it; one
+// barrier; `words` = NW words of LDS no other code uses between two calls).
+template <int NW>
+__device__ __forceinline__ bool wg_any(bool p, uint32_t *words) {
+    const unsigned long long b = __ballot(p);
+    if ((threadIdx.x & 63) == 0) words[threadIdx.x >> 6] = b != 0ull ? 1u : 0u;
+    __syncthreads();
+    uint32_t a = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) a |= words[i];
+    return __builtin_amdgcn_readfirstlane(a) != 0;
+}
+
+// Maximum of x over the workgroup's NW waves (same rules as wg_any).
+template <int NW>
+__device__ __forceinline__ uint32_t wg_max(uint32_t x, uint32_t *words) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, off, 64));
+    if ((threadIdx.x & 63) == 0) words[threadIdx.x >> 6] = x;
+    __syncthreads();
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) m = max(m, words[i]);
+    return __builtin_amdgcn_readfirstlane(m);
+}
+
+// A sum of the accumulators that is finite exactly when all of them are (with V within
+// fp16's range their sizes stay far below the float range: |O| <= 65504 l).
+template <int N>
+__device__ __forceinline__ bool acc_finite(const f32x16 (&o)[N], float l) {
+    float s = l;
+#pragma unroll
+    for (int n = 0; n < N; ++n)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s += o[n][i];
+    return __builtin_fabsf(s) <= 3.0e38f;
+}
+
 // max(a, b, c); the compiler emits one v_max3_f32 for it. MFMA results, selects between
 // them and -inf count as canonical floats, so no quieting instructions are added; and,
 // unlike inline assembly, the compiler sees the read of the MFMA result registers and

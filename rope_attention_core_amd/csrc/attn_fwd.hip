@@ -115,6 +115,7 @@ __global__ __launch_bounds__(waves_for<D>() * 64, waves_for<D>() / 4) void attn_
     constexpr int XB_ELEMS = (CP && DIFF) ? WPB * 32 * D * 2 : 0;
     static_assert(!DIFF || CP || NBUF * BUF_ELEMS * 2 >= WPB * 32 * D * 4, "LDS too small for the O2 exchange");
     __shared__ __attribute__((aligned(16))) uint16_t smem[NBUF * BUF_ELEMS + XB_ELEMS];
+    __shared__ uint32_t guard[2 * NW];       // words of the V range guard's reductions
 
     const float NEG_INF = -__builtin_inff();
     const int tid = threadIdx.x;
@@ -201,6 +202,18 @@ __global__ __launch_bounds__(waves_for<D>() * 64, waves_for<D>() / 4) void attn_
         kv_of(nxt.bh, nk, nv);
     }
 
+    // the input V rows of the current item (the range guard's redo reads them even when
+    // the staging copies V' from the pre-pass workspace)
+    rsrc_t rvr = rv;
+    auto raw_v_of = [&](int bh) __attribute__((always_inline)) {
+        if constexpr (PRE) {
+            const int bb = bh / P.H, hh = bh - bb * P.H;
+            return slab_rsrc(P.v, CONTIG ? (long long)bh * L * D : bb * P.vb + hh * P.vh, vrb, L, RB);
+        } else {
+            return rv;
+        }
+    };
+
     // per-item values the lambdas below read (set at the start of every item)
     int qw = 0, qhi_live = 0;
     u32x4 qreg[NKS];
@@ -209,8 +222,6 @@ __global__ __launch_bounds__(waves_for<D>() * 64, waves_for<D>() / 4) void attn_
     // K (each branch): 64 rows x CPR chunks of 8 elements; chunk item i of a thread is
     // row (tid / CPR) + i * NT / CPR, dims 8 (tid % CPR) .. +7.
     // V: thread -> keys 2p, 2p+1 (p = tid % 32) and VD values of d from VD * (tid / 32).
-    const int vp = tid & 31;
-    const int vd0 = (tid >> 5) * VD;
     u32x4 rawk[NBS][KC], rawc[KC], raws[KC];
     u32x4 rawp[NBS][KC], rawc1[KC], raws1[KC];   // general instances: partner chunks, table floats 4-7
     vraw_t rawv[2][NV];
@@ -224,8 +235,19 @@ __global__ __launch_bounds__(waves_for<D>() * 64, waves_for<D>() / 4) void attn_
     const uint32_t kpl = (uint32_t)(tid / CPR) * krb + (uint32_t)kch.partner * 16;
     const uint32_t cl = CONTIG ? (uint32_t)(tid / CPR) * RB + (uint32_t)(tid % CPR) * 16
                                : (uint32_t)(tid / CPR) * trb + kch.toff;
-    const uint32_t vl = (uint32_t)(2 * vp) * vrb + (uint32_t)vd0 * 2;
-    auto load_raw = [&](const rsrc_t (&kk)[NBS], const rsrc_t &vv, int t) __attribute__((always_inline)) {
+    // V staging: thread -> keys 2p, 2p+1 (p = tid % 32) and VD values of d from
+    // VD * (tid / 32); computed where used, so that the pre-pass instances (whose fast
+    // path copies V' tiles) keep no registers for them outside the guard's redo
+    auto v_lane = [&](int &vd0, int &vpos, uint32_t &vl) __attribute__((always_inline)) {
+        const int vp = tid & 31;
+        vd0 = (tid >> 5) * VD;
+        vpos = (2 * vp & ~12) | ((2 * vp & 4) << 1) | ((2 * vp & 8) >> 1);
+        vl = (uint32_t)(2 * vp) * vrb + (uint32_t)vd0 * 2;
+    };
+    // SAFE (the redo of the V range guard, bf16 only): V comes from the input rows even
+    // in the pre-pass instances and is scaled by vsc = 2^-shift as it is converted.
+    auto load_raw = [&](const rsrc_t (&kk)[NBS], const rsrc_t &vv, int t, auto safe_tag) __attribute__((always_inline)) {
+        constexpr bool VPRE = PRE && !decltype(safe_tag)::value;
         if constexpr (PRE) {
 #pragma unroll
             for (int i = 0; i < KC; ++i) {
@@ -233,49 +255,57 @@ __global__ __launch_bounds__(waves_for<D>() * 64, waves_for<D>() / 4) void attn_
 #pragma unroll
                 for (int br = 0; br < NBS; ++br) rawk[br][i] = bload(kk[br], kl + k0 * RB);
             }
+        } else {
+#pragma unroll
+            for (int i = 0; i < KC; ++i) {
+                const uint32_t k0 = (uint32_t)(t * BN + i * (NT / CPR));
+#pragma unroll
+                for (int br = 0; br < NBS; ++br) rawk[br][i] = bload(kk[br], kl + k0 * krb);
+                if constexpr (CONTIG) {
+                    rawc[i] = bload(rc, cl + k0 * RB);
+                    raws[i] = bload(rs, cl + k0 * RB);
+                } else {
+                    const uint32_t to = kch.mode ? cl + k0 * trb : NOWHERE;
+                    const uint32_t t1 = kch.mode >= 2 ? to + 16 : NOWHERE;
+                    const uint32_t po = kch.mode >= 2 ? kpl + k0 * krb : NOWHERE;
+#pragma unroll
+                    for (int br = 0; br < NBS; ++br) rawp[br][i] = bload(kk[br], po);
+                    rawc[i] = bload(rc, to);
+                    raws[i] = bload(rs, to);
+                    rawc1[i] = bload(rc, t1);
+                    raws1[i] = bload(rs, t1);
+                }
+            }
+        }
+        if constexpr (VPRE) {
             // tiles past the last one lie past the buffer's range and read zeros
 #pragma unroll
             for (int j = 0; j < VC; ++j) rawvp[j] = bload(vv, (uint32_t)t * (D * BN * 2) + (uint32_t)(tid + j * NT) * 16);
-            return;
-        }
-#pragma unroll
-        for (int i = 0; i < KC; ++i) {
-            const uint32_t k0 = (uint32_t)(t * BN + i * (NT / CPR));
-#pragma unroll
-            for (int br = 0; br < NBS; ++br) rawk[br][i] = bload(kk[br], kl + k0 * krb);
-            if constexpr (CONTIG) {
-                rawc[i] = bload(rc, cl + k0 * RB);
-                raws[i] = bload(rs, cl + k0 * RB);
-            } else {
-                const uint32_t to = kch.mode ? cl + k0 * trb : NOWHERE;
-                const uint32_t t1 = kch.mode >= 2 ? to + 16 : NOWHERE;
-                const uint32_t po = kch.mode >= 2 ? kpl + k0 * krb : NOWHERE;
-#pragma unroll
-                for (int br = 0; br < NBS; ++br) rawp[br][i] = bload(kk[br], po);
-                rawc[i] = bload(rc, to);
-                raws[i] = bload(rs, to);
-                rawc1[i] = bload(rc, t1);
-                raws1[i] = bload(rs, t1);
-            }
-        }
-        const uint32_t k0 = (uint32_t)(t * BN);
-        if constexpr (VD >= 8) {
-#pragma unroll
-            for (int n = 0; n < NV; ++n) {
-                rawv[0][n] = bload(vv, vl + k0 * vrb + 16 * n);
-                rawv[1][n] = bload(vv, vl + k0 * vrb + vrb + 16 * n);
-            }
         } else {
-            rawv[0][0] = bload8(vv, vl + k0 * vrb);
-            rawv[1][0] = bload8(vv, vl + k0 * vrb + vrb);
+            int vd0, vpos;
+            uint32_t vl;
+            v_lane(vd0, vpos, vl);
+            const uint32_t k0 = (uint32_t)(t * BN);
+            if constexpr (VD >= 8) {
+#pragma unroll
+                for (int n = 0; n < NV; ++n) {
+                    rawv[0][n] = bload(vv, vl + k0 * vrb + 16 * n);
+                    rawv[1][n] = bload(vv, vl + k0 * vrb + vrb + 16 * n);
+                }
+            } else {
+                rawv[0][0] = bload8(vv, vl + k0 * vrb);
+                rawv[1][0] = bload8(vv, vl + k0 * vrb + vrb);
+            }
         }
     };
 
     // V^T key positions: bits 2 and 3 of the key index swapped, so that the 8 keys one
     // lane multiplies in a P.V step (see load_v_operands) are contiguous.
-    const int vpos = (2 * vp & ~12) | ((2 * vp & 4) << 1) | ((2 * vp & 8) >> 1);
     const int kat = (tid / CPR) * KSTR + (tid % CPR) * 8;
-    auto stage = [&](int buf) __attribute__((always_inline)) {
+    float vsc = 1.0f;   // 2^-shift of the V range guard's redo (SAFE staging only)
+    auto stage = [&](int buf, auto safe_tag) __attribute__((always_inline)) {
+        constexpr bool SAFE = decltype(safe_tag)::value;
+        constexpr bool VPRE = PRE && !SAFE;
         uint16_t *Ks = smem + buf * BUF_ELEMS;
         uint16_t *Vt = Ks + NBS * KS_ELEMS;
 #pragma unroll
@@ -291,7 +321,7 @@ __global__ __launch_bounds__(waves_for<D>() * 64, waves_for<D>() / 4) void attn_
                     rot = rope8_general<IO>(rawk[br][i], rawp[br][i], rawc[i], rawc1[i], raws[i], raws1[i], kch.mode);
                 *reinterpret_cast<u32x4 *>(Ks + br * KS_ELEMS + kat + i * (NT / CPR) * KSTR) = rot;
             }
-        if constexpr (PRE) {
+        if constexpr (VPRE) {
 #pragma unroll
             for (int j = 0; j < VC; ++j) {
                 const int cv = tid + j * NT;
@@ -299,13 +329,20 @@ __global__ __launch_bounds__(waves_for<D>() * 64, waves_for<D>() / 4) void attn_
             }
             return;
         }
+        int vd0, vpos;
+        uint32_t vl;
+        v_lane(vd0, vpos, vl);
 #pragma unroll
         for (int j = 0; j < VD; ++j) {
             const uint32_t wa = rawv[0][j >> 3][(j >> 1) & 3], wb = rawv[1][j >> 3][(j >> 1) & 3];
             uint32_t w;
             if constexpr (IO == IO_BF16) {
-                const float fa = __uint_as_float((j & 1) ? (wa & 0xffff0000u) : (wa << 16));
-                const float fb = __uint_as_float((j & 1) ? (wb & 0xffff0000u) : (wb << 16));
+                float fa = __uint_as_float((j & 1) ? (wa & 0xffff0000u) : (wa << 16));
+                float fb = __uint_as_float((j & 1) ? (wb & 0xffff0000u) : (wb << 16));
+                if constexpr (SAFE) {
+                    fa *= vsc;
+                    fb *= vsc;
+                }
                 w = pack2<IO_F16>(fa, fb);
             } else {
                 w = (j & 1) ? __builtin_amdgcn_perm(wb, wa, 0x07060302u) : __builtin_amdgcn_perm(wb, wa, 0x05040100u);
@@ -384,23 +421,28 @@ __global__ __launch_bounds__(waves_for<D>() * 64, waves_for<D>() / 4) void attn_
     auto slot = [&](int t) __attribute__((always_inline)) { return PERS ? (sq0 + t - cur.tb) % NBUF : t % NBUF; };
     // loads of the tile 3 positions after t: past the item's last tile, CP takes the
     // next item's first tiles (when every item has at least 3 key tiles: P.cp)
-    auto load_next = [&](int t) __attribute__((always_inline)) {
+    // (the SAFE redo never runs on: the next item then starts cold)
+    auto load_next = [&](int t, auto safe_tag) __attribute__((always_inline)) {
         const int u = t + 3;
+        if constexpr (decltype(safe_tag)::value) {
+            load_raw(rk, rvr, u, safe_tag);
+            return;
+        }
         if constexpr (CP) {
             if (P.cp && has_nxt && u >= cur.te) {
-                load_raw(nk, nv, nxt.tb + (u - cur.te));
+                load_raw(nk, nv, nxt.tb + (u - cur.te), safe_tag);
                 return;
             }
         }
-        load_raw(rk, rv, u);
+        load_raw(rk, rv, u, safe_tag);
     };
-    auto block = [&](int t, auto mask_tag, auto par_tag) __attribute__((always_inline)) {
+    auto block = [&](int t, auto mask_tag, auto par_tag, auto safe_tag) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_tag)::value;
         constexpr int PC = PIPE2 ? decltype(par_tag)::value : 0;
         constexpr int PN = PIPE2 ? PC ^ 1 : 0;
         if constexpr (EARLY) {
-            stage(slot(t + 2));
-            load_next(t);
+            stage(slot(t + 2), safe_tag);
+            load_next(t, safe_tag);
         }
         if constexpr (PIPE2)
             qk(slot(t + 1), sb[PN]);   // past the item's last tile: computed and unused
@@ -440,8 +482,8 @@ __global__ __launch_bounds__(waves_for<D>() * 64, waves_for<D>() / 4) void attn_
                                            st.o[db]);
             }
             if constexpr (!EARLY) {
-                stage(slot(t + 2));
-                load_next(t);
+                stage(slot(t + 2), safe_tag);
+                load_next(t, safe_tag);
             }
             __syncthreads();
             return;
@@ -474,32 +516,30 @@ __global__ __launch_bounds__(waves_for<D>() * 64, waves_for<D>() / 4) void attn_
         }
         st.l = __builtin_fmaf(st.l, a, part[0] + part[1]);
         if constexpr (!EARLY) {
-            stage(slot(t + 2));
-            load_next(t);
+            stage(slot(t + 2), safe_tag);
+            load_next(t, safe_tag);
         }
         __syncthreads();
     };
 
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
-    auto step = [&](int t, auto par_tag) __attribute__((always_inline)) {
+    auto step = [&](int t, auto par_tag, auto safe_tag) __attribute__((always_inline)) {
         if (tile_needs_mask(t))
-            block(t, std::true_type{}, par_tag);
+            block(t, std::true_type{}, par_tag, safe_tag);
         else
-            block(t, std::false_type{}, par_tag);
+            block(t, std::false_type{}, par_tag, safe_tag);
     };
-    bool first = true;
-    for (;;) {
-        // ---- item setup: Q rotated into registers (MFMA B-operand layout) -----------
+    // One pass over the current item: Q rotated into registers (MFMA B-operand layout),
+    // O, l, m reset, the prologue when the item starts cold, then the key tiles.
+    auto run_item = [&](auto safe_tag, bool cold, bool wait) __attribute__((always_inline)) {
+        constexpr bool SAFE = decltype(safe_tag)::value;
         const int bb = cur.bh / P.H, hh = cur.bh - bb * P.H;
         const long long slab = (long long)cur.bh * L * D;   // contiguous offset of this (b, h)
-        const int q0 = cur.qt * BM;
-        qw = q0 + wq * 32;
-        qhi_live = min(qw + 31, L - 1);
         const rsrc_t rq = slab_rsrc(P.q, wbr * qbr + (CONTIG ? slab : bb * P.qb + hh * P.qh), qrb, L, RB);
         {
             const uint32_t row = (uint32_t)(qw + r);
-    #pragma unroll
+#pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 const uint32_t col = (uint32_t)(16 * ks + 8 * g) * 2;
                 if constexpr (CONTIG) {
@@ -522,26 +562,61 @@ __global__ __launch_bounds__(waves_for<D>() * 64, waves_for<D>() / 4) void attn_
         st.a = 1.0f;
 
         // ---- prologue: the first item, and every item without CP ------------------
-        if (first || !(CP && P.cp)) {
-            if (!first) __syncthreads();   // the previous epilogue's LDS reads are done
-            load_raw(rk, rv, cur.tb);
-            stage(slot(cur.tb));
-            load_raw(rk, rv, cur.tb + 1);
-            stage(slot(cur.tb + 1));
-            load_raw(rk, rv, cur.tb + 2);
+        if (cold) {
+            if (wait) __syncthreads();   // every wave is done with the LDS stages
+            const rsrc_t &vv = SAFE ? rvr : rv;
+            load_raw(rk, vv, cur.tb, safe_tag);
+            stage(slot(cur.tb), safe_tag);
+            load_raw(rk, vv, cur.tb + 1, safe_tag);
+            stage(slot(cur.tb + 1), safe_tag);
+            load_raw(rk, vv, cur.tb + 2, safe_tag);
             __syncthreads();
         }
-        first = false;
         if constexpr (PIPE2) qk(slot(cur.tb), sb[0]);
         int t = cur.tb;
         for (; t + 1 < cur.te; t += 2) {
-            step(t, P0{});
-            step(t + 1, P1{});
+            step(t, P0{}, safe_tag);
+            step(t + 1, P1{}, safe_tag);
         }
-        if (t < cur.te) step(t, P0{});
+        if (t < cur.te) step(t, P0{}, safe_tag);
+    };
+
+    bool first = true, cold_next = false;
+    for (;;) {
+        const int bb = cur.bh / P.H, hh = cur.bh - bb * P.H;
+        const long long slab = (long long)cur.bh * L * D;   // contiguous offset of this (b, h)
+        const int q0 = cur.qt * BM;
+        qw = q0 + wq * 32;
+        qhi_live = min(qw + 31, L - 1);
+        rvr = raw_v_of(cur.bh);
+        run_item(std::false_type{}, first || cold_next || !(CP && P.cp), !first);
+        first = false;
+        cold_next = false;
+
+        // ---- range guard of the bf16 -> fp16 V conversion (see attn_common.hpp) ------
+        int vshift = 0;
+        if constexpr (IO == IO_BF16) {
+            if (wg_any<NW>(!acc_finite(st.o, st.l), guard)) {
+                // largest finite |v| over the key tiles this item visited
+                uint32_t mx = 0;
+                const int k_lo = cur.tb * BN, k_hi = min(cur.te * BN, L);
+                for (int c = k_lo * CPR + tid; c < k_hi * CPR; c += NT)
+                    mx = max(mx, bf16_finite_absmax(bload(rvr, (uint32_t)(c / CPR) * vrb + (uint32_t)(c % CPR) * 16)));
+                vshift = vshift_of(wg_max<NW>(mx, guard + NW));
+                if (vshift > 0) {
+                    // redo the item with V scaled by 2^-vshift; the LDS stages and the
+                    // registers CP filled for the next item are overwritten, so that one
+                    // starts cold
+                    vsc = exp2i(-vshift);
+                    run_item(std::true_type{}, true, true);
+                    cold_next = true;
+                }
+            }
+        }
 
         // ---- epilogue: normalise, subtract, cast, store rows < L -------------------------
-        const float inv = 1.0f / pair_sum(st.l);
+        // (2^vshift undoes the guard's scaling of V; l >= 1, so inv * 2^vshift stays finite)
+        const float inv = (1.0f / pair_sum(st.l)) * exp2i(vshift);
         const int qi = qw + r;
         if constexpr (DIFF) {
             // The second branch hands x2 = O2 / l2 to the first through LDS (the stages

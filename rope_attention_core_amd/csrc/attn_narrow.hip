@@ -83,6 +83,7 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
     static_assert(NK * 8 % NT == 0 && NK * 4 % NT == 0, "staging split");
     static_assert(!DIFF || S::LDS_ELEMS * 2 >= WPB * 32 * 64 * 4, "LDS too small for the O2 exchange");
     __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_ELEMS];
+    __shared__ uint32_t guard[2 * (NT / 64)];   // words of the V range guard's reductions
 
     const float NEG_INF = -__builtin_inff();
     const int tid = threadIdx.x;
@@ -129,185 +130,225 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
     const int qw = q0 + wq * 32;
     const int ks0 = NKF ? 0 : q0 - w;        // first staged key (may be negative)
 
-    // ---- issue every load: Q rows of this wave, then the K / cos / sin / V span ------
-    // Q: the rotated chunks go straight to registers; general instances also load the
-    // partner chunks and table floats 4-7 (half-split pairs)
-    u32x4 qreg[4];
-    const uint32_t qsign = P.neg_scale ? 0x80008000u : 0u;
-    u32x4 rq_raw[4], rqc[4], rqs[4];
-    {
-        const uint32_t row = (uint32_t)(qw + r);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const uint32_t col = (uint32_t)(16 * ks + 8 * g) * 2;
-            rq_raw[ks] = bload(rq, row * qrb + col);
-            if constexpr (CONTIG) {
-                rqc[ks] = bload(rc, row * ROWB + col);
-                rqs[ks] = bload(rs, row * ROWB + col);
-            } else {
-                const RopeChunk rc8 = rope_chunk(2 * ks + g, rhalf, rdim);
-                const uint32_t to = rc8.mode ? row * trb + rc8.toff : NOWHERE;
-                const uint32_t t1 = rc8.mode >= 2 ? to + 16 : NOWHERE;
-                const uint32_t po = rc8.mode >= 2 ? row * qrb + (uint32_t)rc8.partner * 16 : NOWHERE;
-                qreg[ks] = rope8_general<IO>(rq_raw[ks], bload(rq, po), bload(rc, to), bload(rc, t1), bload(rs, to),
-                                             bload(rs, t1), rc8.mode) ^ qsign;
-            }
-        }
-    }
-    // K item i: span row (tid >> 3) + i * NT / 8, chunk tid & 7. The per-lane part of
-    // the offset is one multiply here; the per-item part is wave-uniform (scalar unit).
-    u32x4 rawk[NBS][KC], rawc[KC], raws[KC];
-    u32x4 rawp[CONTIG ? 1 : NBS][CONTIG ? 1 : KC], rawc1[CONTIG ? 1 : KC], raws1[CONTIG ? 1 : KC];
-    const RopeChunk kch = rope_chunk(tid & 7, rhalf, rdim);
-    const uint32_t kl = (uint32_t)(tid >> 3) * krb + (uint32_t)(tid & 7) * 16;
-    const uint32_t kpl = (uint32_t)(tid >> 3) * krb + (uint32_t)kch.partner * 16;
-    const uint32_t cl = CONTIG ? (uint32_t)(tid >> 3) * ROWB + (uint32_t)(tid & 7) * 16
-                               : (uint32_t)(tid >> 3) * trb + kch.toff;
-#pragma unroll
-    for (int i = 0; i < KC; ++i) {
-        const uint32_t r0 = (uint32_t)(ks0 + i * (NT / 8));
-#pragma unroll
-        for (int br = 0; br < NBS; ++br) rawk[br][i] = bload(rk[br], kl + r0 * krb);
-        if constexpr (CONTIG) {
-            rawc[i] = bload(rc, cl + r0 * ROWB);
-            raws[i] = bload(rs, cl + r0 * ROWB);
-        } else {
-            const uint32_t to = kch.mode ? cl + r0 * trb : NOWHERE;
-            const uint32_t t1 = kch.mode >= 2 ? to + 16 : NOWHERE;
-            const uint32_t po = kch.mode >= 2 ? kpl + r0 * krb : NOWHERE;
-#pragma unroll
-            for (int br = 0; br < NBS; ++br) rawp[br][i] = bload(rk[br], po);
-            rawc[i] = bload(rc, to);
-            raws[i] = bload(rs, to);
-            rawc1[i] = bload(rc, t1);
-            raws1[i] = bload(rs, t1);
-        }
-    }
-    // V item: keys 2p, 2p + 1 of the span and 8 values of d from 8 * ch
-    u32x4 rawv[VC][2];
-#pragma unroll
-    for (int i = 0; i < VC; ++i) {
-        const int it = tid + NT * i;
-        const int p = it % (NK / 2), ch = it / (NK / 2);
-        const uint32_t off = (uint32_t)(ks0 + 2 * p) * vrb + (uint32_t)ch * 16;
-        rawv[i][0] = bload(rv, off);
-        rawv[i][1] = bload(rv, off + vrb);
-    }
-
-    // ---- rotate Q into registers; rotate / transpose the span into LDS ---------------
-    if constexpr (CONTIG) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) qreg[ks] = rope8<IO>(rq_raw[ks], rqc[ks], rqs[ks]) ^ qsign;
-    }
-#pragma unroll
-    for (int i = 0; i < KC; ++i) {
-        const int it = tid + NT * i;
-        const int at = (it >> 3) * S::KS + ((it & 7) ^ (S::SWZ ? (it >> 3) & 7 : 0)) * 8;
-#pragma unroll
-        for (int br = 0; br < NBS; ++br) {
-            u32x4 rot;
-            if constexpr (CONTIG)
-                rot = rope8<IO>(rawk[br][i], rawc[i], raws[i]);
-            else
-                rot = rope8_general<IO>(rawk[br][i], rawp[br][i], rawc[i], rawc1[i], raws[i], raws1[i], kch.mode);
-            *reinterpret_cast<u32x4 *>(smem + br * S::K_ELEMS + at) = rot;
-        }
-    }
-    uint16_t *Vt = smem + NBS * S::K_ELEMS;
-#pragma unroll
-    for (int i = 0; i < VC; ++i) {
-        const int it = tid + NT * i;
-        const int p = it % (NK / 2), ch = it / (NK / 2);
-        // key positions inside each 16 carry bits 2 and 3 swapped (the P.V operand order)
-        const int k2 = 2 * p;
-        const int pos = (k2 & ~12) | ((k2 & 4) << 1) | ((k2 & 8) >> 1);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t wa = rawv[i][0][j >> 1], wb = rawv[i][1][j >> 1];
-            uint32_t wv;
-            if constexpr (IO == IO_BF16) {
-                const float fa = __uint_as_float((j & 1) ? (wa & 0xffff0000u) : (wa << 16));
-                const float fb = __uint_as_float((j & 1) ? (wb & 0xffff0000u) : (wb << 16));
-                wv = pack2<IO_F16>(fa, fb);
-            } else {
-                wv = (j & 1) ? __builtin_amdgcn_perm(wb, wa, 0x07060302u) : __builtin_amdgcn_perm(wb, wa, 0x05040100u);
-            }
-            *reinterpret_cast<uint32_t *>(Vt + (8 * ch + j) * S::VS + pos) = wv;
-        }
-    }
-    __syncthreads();
-
-    // ---- scores of this wave's 32 rows over the span: S^T blocks of 32 keys ----------
-    const uint16_t *Ks = smem + wbr * S::K_ELEMS;
-    // s[j]: keys of 32-key block kb = kq * NKBW + j of the span
-    const int kb0 = kq * NKBW;
-    f32x16 s[NKBW];
-#pragma unroll
-    for (int j = 0; j < NKBW; ++j) {
-        const int kb = kb0 + j;
-        u32x4 ka[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            ka[ks] = lds16(Ks + (kb * 32 + r) * S::KS + ((2 * ks + g) ^ (S::SWZ ? r & 7 : 0)) * 8);
-        f32x16 acc = {};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc = mfma_qk<IO>(ka[ks], qreg[ks], acc);
-        s[j] = acc;
-    }
-
-    // valid keys of this lane's query: [max(0, qi - w), min(L - 1, qi + w)], as offsets o
-    // inside the span relative to 4g (the accumulator layout), lo <= o <= lo + span
+    // One pass: issue every load (Q rows of this wave, then the K / cos / sin / V span),
+    // stage, and compute this wave's O, l and maximum. SAFE: the redo of the V range
+    // guard (bf16 only), which scales V by vsc = 2^-shift as it converts it.
     const int qi = qw + r;
-    int lo = max(0, qi - w) - (ks0 + 4 * g);
-    int hi = min(L - 1, qi + w) - (ks0 + 4 * g);
-    const bool any = hi >= lo;
-    const uint32_t span = any ? (uint32_t)(hi - lo) : 0u;
-    if (!any) lo = 1 << 20;
-    auto valid = [&](int kb, int i) __attribute__((always_inline)) {
-        const int o = kb * 32 + (i >> 2) * 8 + (i & 3);
-        return (uint32_t)(o - lo) <= span;
-    };
+    f32x16 o[2];
+    float l, mx;
+    float vsc = 1.0f;
+    auto compute = [&](auto safe_tag) __attribute__((always_inline)) {
+        constexpr bool SAFE = decltype(safe_tag)::value;
+        // The redo derives its lane values from an opaque copy of the thread id, so that the
+        // compiler cannot share address arithmetic between the two passes (which would keep
+        // it in registers through the first one).
+        int tid = (int)threadIdx.x;
+        if constexpr (SAFE) __asm__ volatile("" : "+v"(tid));
+        const int lane = tid & 63, r = lane & 31, g = lane >> 5;
+        const int qi = qw + r;
+        // Q: the rotated chunks go straight to registers; general instances also load the
+        // partner chunks and table floats 4-7 (half-split pairs)
+        u32x4 qreg[4];
+        const uint32_t qsign = P.neg_scale ? 0x80008000u : 0u;
+        u32x4 rq_raw[4], rqc[4], rqs[4];
+        {
+            const uint32_t row = (uint32_t)(qw + r);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const uint32_t col = (uint32_t)(16 * ks + 8 * g) * 2;
+                rq_raw[ks] = bload(rq, row * qrb + col);
+                if constexpr (CONTIG) {
+                    rqc[ks] = bload(rc, row * ROWB + col);
+                    rqs[ks] = bload(rs, row * ROWB + col);
+                } else {
+                    const RopeChunk rc8 = rope_chunk(2 * ks + g, rhalf, rdim);
+                    const uint32_t to = rc8.mode ? row * trb + rc8.toff : NOWHERE;
+                    const uint32_t t1 = rc8.mode >= 2 ? to + 16 : NOWHERE;
+                    const uint32_t po = rc8.mode >= 2 ? row * qrb + (uint32_t)rc8.partner * 16 : NOWHERE;
+                    qreg[ks] = rope8_general<IO>(rq_raw[ks], bload(rq, po), bload(rc, to), bload(rc, t1), bload(rs, to),
+                                                 bload(rs, t1), rc8.mode) ^ qsign;
+                }
+            }
+        }
+        // K item i: span row (tid >> 3) + i * NT / 8, chunk tid & 7. The per-lane part of
+        // the offset is one multiply here; the per-item part is wave-uniform (scalar unit).
+        u32x4 rawk[NBS][KC], rawc[KC], raws[KC];
+        u32x4 rawp[CONTIG ? 1 : NBS][CONTIG ? 1 : KC], rawc1[CONTIG ? 1 : KC], raws1[CONTIG ? 1 : KC];
+        const RopeChunk kch = rope_chunk(tid & 7, rhalf, rdim);
+        const uint32_t kl = (uint32_t)(tid >> 3) * krb + (uint32_t)(tid & 7) * 16;
+        const uint32_t kpl = (uint32_t)(tid >> 3) * krb + (uint32_t)kch.partner * 16;
+        const uint32_t cl = CONTIG ? (uint32_t)(tid >> 3) * ROWB + (uint32_t)(tid & 7) * 16
+                                   : (uint32_t)(tid >> 3) * trb + kch.toff;
+#pragma unroll
+        for (int i = 0; i < KC; ++i) {
+            const uint32_t r0 = (uint32_t)(ks0 + i * (NT / 8));
+#pragma unroll
+            for (int br = 0; br < NBS; ++br) rawk[br][i] = bload(rk[br], kl + r0 * krb);
+            if constexpr (CONTIG) {
+                rawc[i] = bload(rc, cl + r0 * ROWB);
+                raws[i] = bload(rs, cl + r0 * ROWB);
+            } else {
+                const uint32_t to = kch.mode ? cl + r0 * trb : NOWHERE;
+                const uint32_t t1 = kch.mode >= 2 ? to + 16 : NOWHERE;
+                const uint32_t po = kch.mode >= 2 ? kpl + r0 * krb : NOWHERE;
+#pragma unroll
+                for (int br = 0; br < NBS; ++br) rawp[br][i] = bload(rk[br], po);
+                rawc[i] = bload(rc, to);
+                raws[i] = bload(rs, to);
+                rawc1[i] = bload(rc, t1);
+                raws1[i] = bload(rs, t1);
+            }
+        }
+        // V item: keys 2p, 2p + 1 of the span and 8 values of d from 8 * ch
+        u32x4 rawv[VC][2];
+#pragma unroll
+        for (int i = 0; i < VC; ++i) {
+            const int it = tid + NT * i;
+            const int p = it % (NK / 2), ch = it / (NK / 2);
+            const uint32_t off = (uint32_t)(ks0 + 2 * p) * vrb + (uint32_t)ch * 16;
+            rawv[i][0] = bload(rv, off);
+            rawv[i][1] = bload(rv, off + vrb);
+        }
 
-    // exact maximum over this wave's share of the span, then P = 2^(s c - m) in fp16
-    float mx = NEG_INF;
+        // ---- rotate Q into registers; rotate / transpose the span into LDS ---------------
+        if constexpr (CONTIG) {
 #pragma unroll
-    for (int j = 0; j < NKBW; ++j)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, valid(kb0 + j, i) ? s[j][i] : NEG_INF);
-    mx = pair_max(mx);
-    const float nb = (mx == NEG_INF) ? 0.0f : -(mx * c);
-
-    // P of each 32-key block, its FP32 row sums, and O^T += V^T P^T right away
-    f32x16 o[2] = {f32x16{}, f32x16{}};
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int j = 0; j < NKBW; ++j) {
-        const int kb = kb0 + j;
-        float e[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float t = __builtin_fmaf(s[j][i], c, nb);
-            e[i] = __builtin_amdgcn_exp2f(valid(kb, i) ? t : NEG_INF);
+            for (int ks = 0; ks < 4; ++ks) qreg[ks] = rope8<IO>(rq_raw[ks], rqc[ks], rqs[ks]) ^ qsign;
         }
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            u32x4 pk;
+        for (int i = 0; i < KC; ++i) {
+            const int it = tid + NT * i;
+            const int at = (it >> 3) * S::KS + ((it & 7) ^ (S::SWZ ? (it >> 3) & 7 : 0)) * 8;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const f16x2 h = {(_Float16)e[8 * tt + 2 * jj], (_Float16)e[8 * tt + 2 * jj + 1]};
-                pk[jj] = __builtin_bit_cast(uint32_t, h);
-                // partial sums by block parity and half (summed in a fixed order below)
-                acc[(j & 1) * 2 + tt] = __builtin_amdgcn_fdot2(h, f16x2{(_Float16)1.0f, (_Float16)1.0f},
-                                                               acc[(j & 1) * 2 + tt], false);
+            for (int br = 0; br < NBS; ++br) {
+                u32x4 rot;
+                if constexpr (CONTIG)
+                    rot = rope8<IO>(rawk[br][i], rawc[i], raws[i]);
+                else
+                    rot = rope8_general<IO>(rawk[br][i], rawp[br][i], rawc[i], rawc1[i], raws[i], raws1[i], kch.mode);
+                *reinterpret_cast<u32x4 *>(smem + br * S::K_ELEMS + at) = rot;
+            }
+        }
+        uint16_t *Vt = smem + NBS * S::K_ELEMS;
+#pragma unroll
+        for (int i = 0; i < VC; ++i) {
+            const int it = tid + NT * i;
+            const int p = it % (NK / 2), ch = it / (NK / 2);
+            // key positions inside each 16 carry bits 2 and 3 swapped (the P.V operand order)
+            const int k2 = 2 * p;
+            const int pos = (k2 & ~12) | ((k2 & 4) << 1) | ((k2 & 8) >> 1);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t wa = rawv[i][0][j >> 1], wb = rawv[i][1][j >> 1];
+                uint32_t wv;
+                if constexpr (IO == IO_BF16) {
+                    float fa = __uint_as_float((j & 1) ? (wa & 0xffff0000u) : (wa << 16));
+                    float fb = __uint_as_float((j & 1) ? (wb & 0xffff0000u) : (wb << 16));
+                    if constexpr (SAFE) {
+                        fa *= vsc;
+                        fb *= vsc;
+                    }
+                    wv = pack2<IO_F16>(fa, fb);
+                } else {
+                    wv = (j & 1) ? __builtin_amdgcn_perm(wb, wa, 0x07060302u) : __builtin_amdgcn_perm(wb, wa, 0x05040100u);
+                }
+                *reinterpret_cast<uint32_t *>(Vt + (8 * ch + j) * S::VS + pos) = wv;
+            }
+        }
+        __syncthreads();
+
+        // ---- scores of this wave's 32 rows over the span: S^T blocks of 32 keys ----------
+        const uint16_t *Ks = smem + wbr * S::K_ELEMS;
+        // s[j]: keys of 32-key block kb = kq * NKBW + j of the span
+        const int kb0 = kq * NKBW;
+        f32x16 s[NKBW];
+#pragma unroll
+        for (int j = 0; j < NKBW; ++j) {
+            const int kb = kb0 + j;
+            u32x4 ka[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                ka[ks] = lds16(Ks + (kb * 32 + r) * S::KS + ((2 * ks + g) ^ (S::SWZ ? r & 7 : 0)) * 8);
+            f32x16 acc = {};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) acc = mfma_qk<IO>(ka[ks], qreg[ks], acc);
+            s[j] = acc;
+        }
+
+        // valid keys of this lane's query: [max(0, qi - w), min(L - 1, qi + w)], as offsets o
+        // inside the span relative to 4g (the accumulator layout), lo <= o <= lo + span
+        int lo = max(0, qi - w) - (ks0 + 4 * g);
+        int hi = min(L - 1, qi + w) - (ks0 + 4 * g);
+        const bool any = hi >= lo;
+        const uint32_t span = any ? (uint32_t)(hi - lo) : 0u;
+        if (!any) lo = 1 << 20;
+        auto valid = [&](int kb, int i) __attribute__((always_inline)) {
+            const int o = kb * 32 + (i >> 2) * 8 + (i & 3);
+            return (uint32_t)(o - lo) <= span;
+        };
+
+        // exact maximum over this wave's share of the span, then P = 2^(s c - m) in fp16
+        mx = NEG_INF;
+#pragma unroll
+        for (int j = 0; j < NKBW; ++j)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, valid(kb0 + j, i) ? s[j][i] : NEG_INF);
+        mx = pair_max(mx);
+        const float nb = (mx == NEG_INF) ? 0.0f : -(mx * c);
+
+        // P of each 32-key block, its FP32 row sums, and O^T += V^T P^T right away
+        o[0] = f32x16{};
+        o[1] = f32x16{};
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int j = 0; j < NKBW; ++j) {
+            const int kb = kb0 + j;
+            float e[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float t = __builtin_fmaf(s[j][i], c, nb);
+                e[i] = __builtin_amdgcn_exp2f(valid(kb, i) ? t : NEG_INF);
             }
 #pragma unroll
-            for (int db = 0; db < 2; ++db) {
-                const u32x4 va = lds16(Vt + (db * 32 + r) * S::VS + kb * 32 + 16 * tt + 8 * g);
-                o[db] = mfma_pv(va, pk, o[db]);
+            for (int tt = 0; tt < 2; ++tt) {
+                u32x4 pk;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const f16x2 h = {(_Float16)e[8 * tt + 2 * jj], (_Float16)e[8 * tt + 2 * jj + 1]};
+                    pk[jj] = __builtin_bit_cast(uint32_t, h);
+                    // partial sums by block parity and half (summed in a fixed order below)
+                    acc[(j & 1) * 2 + tt] = __builtin_amdgcn_fdot2(h, f16x2{(_Float16)1.0f, (_Float16)1.0f},
+                                                                   acc[(j & 1) * 2 + tt], false);
+                }
+#pragma unroll
+                for (int db = 0; db < 2; ++db) {
+                    const u32x4 va = lds16(Vt + (db * 32 + r) * S::VS + kb * 32 + 16 * tt + 8 * g);
+                    o[db] = mfma_pv(va, pk, o[db]);
+                }
+            }
+        }
+        l = pair_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
+    };
+    compute(std::false_type{});
+
+    // ---- range guard of the bf16 -> fp16 V conversion (see attn_common.hpp) ----------
+    int vshift = 0;
+    if constexpr (IO == IO_BF16) {
+        if (wg_any<NT / 64>(!acc_finite(o, l), guard)) {
+            // largest finite |v| over the staged span [ks0, ks0 + NK)
+            uint32_t vmax = 0;
+            for (int c = tid; c < NK * 8; c += NT) {
+                const int row = ks0 + (c >> 3);
+                if (row >= 0) vmax = max(vmax, bf16_finite_absmax(bload(rv, (uint32_t)row * vrb + (uint32_t)(c & 7) * 16)));
+            }
+            vshift = vshift_of(wg_max<NT / 64>(vmax, guard + NT / 64));
+            if (vshift > 0) {
+                vsc = exp2i(-vshift);
+                __syncthreads();   // every wave is done with the staged span
+                compute(std::true_type{});
             }
         }
     }
-    float l = pair_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
 
     if constexpr (KSPLIT > 1) {
         // merge the shares of one query block: wave wq * KSPLIT (kq = 0) takes
@@ -352,7 +393,8 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
     }
 
     // ---- epilogue: normalise, subtract, cast, store rows < L -------------------------
-    const float inv = 1.0f / l;
+    // (2^vshift undoes the guard's scaling of V; l >= 1, so inv * 2^vshift stays finite)
+    const float inv = (1.0f / l) * exp2i(vshift);
     if constexpr (DIFF) {
         float *xb = reinterpret_cast<float *>(smem);
         __syncthreads();   // every wave is done with the staged span

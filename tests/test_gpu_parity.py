@@ -19,11 +19,13 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("name", ["tiny", "dit_short", "dit_2min", "dit_2min_prime"])
 def test_config_full_parity(name):
+    """The fp16-output configurations, every element: the raw max-abs error (fp16
+    output rounding included) <= 2e-3 and row cosine >= 0.99995."""
     cfg = synth.config(name)
     inp = synth.make_inputs(cfg)
     got = G.run_gpu(cfg, inp)
     want = G.run_oracle(cfg, inp)
-    G.assert_parity(got, want, what=name, out=cfg.out_dtype)
+    G.assert_parity(got, want, what=name, out=cfg.out_dtype, raw=True)
 
 
 def test_dit_long_full_size_sampled():

@@ -199,3 +199,17 @@ def test_internal_workspace_on_a_side_stream():
     torch.cuda.synchronize()
     for i, out in enumerate(outs):
         assert torch.equal(out, fused), f"call {i} on the side stream differs"
+
+
+@pytest.mark.parametrize("prep", ["only", "reuse"])
+def test_only_and_reuse_need_a_workspace(prep):
+    """Without the caller's workspace, "reuse" would read an uninitialised one and
+    "only" would fill one that is dropped: both raise, and out is untouched."""
+    torch = G.torch_mod()
+    cfg = synth.config("dit_2min", H=2, L=700, seed=9890)
+    _, q, k, v = _inputs(cfg)
+    out = torch.full_like(v, 7.0)
+    with pytest.raises(ValueError):
+        _call(cfg, q, k, v, prep=prep, out=out)
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
