@@ -71,7 +71,7 @@ extern "C" {
 #endif
 
 #define SA3ATTN_VERSION_MAJOR 0
-#define SA3ATTN_VERSION_MINOR 5
+#define SA3ATTN_VERSION_MINOR 6
 
 /* Status codes. */
 enum {
@@ -82,7 +82,9 @@ enum {
     SA3_ERR_ARG = -4,          /* non-finite scale or lambda, out overlaps an input,
                                   a misaligned pointer, or unusable strides           */
     SA3_ERR_DEVICE = -5,       /* no HIP device, or the current device is not gfx950  */
-    SA3_ERR_LAUNCH = -6        /* the kernel launch failed (hipGetLastError)          */
+    SA3_ERR_LAUNCH = -6,       /* the kernel launch failed (hipGetLastError)          */
+    SA3_ERR_SCRATCH = -7       /* sa3attn_forward_noalloc: the pre-pass workspace the
+                                  policy asks for exceeds SA3ATTN_SCRATCH_BYTES        */
 };
 
 /* Element types. */
@@ -226,6 +228,33 @@ int sa3attn_workspace_bytes(const sa3attn_desc *desc, int policy, unsigned long 
 int sa3attn_forward_ws(const sa3attn_desc *desc, const sa3attn_strides *strides,
                        const sa3attn_rope *rope, void *workspace,
                        unsigned long long workspace_bytes, int policy);
+
+/*
+ * sa3attn_forward_noalloc -- sa3attn_forward_ws without a caller workspace, for
+ * callers that cannot allocate device memory (code under graph capture, serving
+ * loops or harnesses that forbid allocation): the pre-pass workspace is a static
+ * device array of the library, SA3ATTN_SCRATCH_BYTES (64 MiB) on each GPU the
+ * library runs on, held until the process ends. The call itself allocates nothing;
+ * its first call on a device looks up that device's copy of the array
+ * (hipGetSymbolAddress) and caches it.
+ *   desc, strides, rope: as for sa3attn_forward_general; the caller still provides
+ *     q, k, v, cos, sin and out.
+ *   policy: as for sa3attn_forward_ws. When the pre-pass would need more than
+ *     SA3ATTN_SCRATCH_BYTES (sa3attn_workspace_bytes gives the size): AUTO runs the
+ *     call without it (the same outputs, bitwise); ALWAYS, ONLY and REUSE return
+ *     SA3_ERR_SCRATCH before anything is enqueued.
+ *   Sharing: every call on one GPU uses the same array, whose contents persist from
+ *     call to call (REUSE reads what the last ALWAYS or ONLY call on that GPU wrote).
+ *     Calls that may overlap in time on one GPU (other streams, other threads) race
+ *     on it and give wrong outputs; order them, or use sa3attn_forward_ws with a
+ *     workspace per stream. Nothing in the array needs to start at zero.
+ *   Errors as for sa3attn_forward_ws, plus SA3_ERR_SCRATCH, and SA3_ERR_DEVICE when
+ *   the array's address cannot be looked up.
+ */
+#define SA3ATTN_SCRATCH_BYTES (64ull << 20)
+
+int sa3attn_forward_noalloc(const sa3attn_desc *desc, const sa3attn_strides *strides,
+                            const sa3attn_rope *rope, int policy);
 
 /*
  * sa3attn_rope_table -- fill a host FP32 cos/sin table [L][D/2].

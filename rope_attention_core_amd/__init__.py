@@ -15,7 +15,7 @@ import ctypes
 import os
 
 __all__ = [
-    "forward", "forward_short", "workspace_bytes", "rope_table", "status_string", "version", "library_path",
+    "forward", "forward_noalloc", "forward_short", "workspace_bytes", "SCRATCH_BYTES", "rope_table", "status_string", "version", "library_path",
     "load_library", "SA3Error", "F16", "BF16", "F32", "EXPORTS",
 ]
 
@@ -25,6 +25,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.environ.get("SA3ATTN_LIB") or os.path.join(_HERE, "libsa3attn.so")
 
 F16, BF16, F32 = 0, 1, 2
+SCRATCH_BYTES = 64 << 20   # SA3ATTN_SCRATCH_BYTES: the static workspace of sa3attn_forward_noalloc
 EXPORTS = (
     "sa3attn_forward",
     "sa3attn_forward_bf16",
@@ -33,6 +34,7 @@ EXPORTS = (
     "sa3attn_forward_general",
     "sa3attn_workspace_bytes",
     "sa3attn_forward_ws",
+    "sa3attn_forward_noalloc",
     "sa3attn_rope_table",
     "sa3attn_status_string",
     "sa3attn_version",
@@ -105,6 +107,8 @@ def load_library():
     lib.sa3attn_forward_ws.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_Strides), ctypes.POINTER(_Rope), vp,
                                        ctypes.c_ulonglong, i]
     lib.sa3attn_forward_ws.restype = i
+    lib.sa3attn_forward_noalloc.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_Strides), ctypes.POINTER(_Rope), i]
+    lib.sa3attn_forward_noalloc.restype = i
     lib.sa3attn_rope_table.argtypes = [vp, vp, i, i, ctypes.c_double]
     lib.sa3attn_rope_table.restype = i
     lib.sa3attn_status_string.argtypes = [i]
@@ -252,6 +256,26 @@ def forward(q, k, v, cos, sin, *, window=-1, lam=0.0, scale=None, out=None, out_
     Every shape, dtype, device and layout condition the library cannot see from raw
     pointers is checked here before the call.
     """
+    return _forward(q, k, v, cos, sin, window, lam, scale, out, out_dtype, differential, stream, pairing,
+                    rotary_dim, prep, workspace, False)
+
+
+def forward_noalloc(q, k, v, cos, sin, out, *, window=-1, lam=0.0, scale=None, differential=None, stream=None,
+                    pairing="adjacent", rotary_dim=None, prep="auto"):
+    """The same call through sa3attn_forward_noalloc: the pre-pass workspace is the
+    library's static device array (SCRATCH_BYTES per GPU) and nothing is allocated,
+    here or in the library; ``out`` must be given. Calls that overlap in time on one
+    GPU share that array and race; "reuse" reads what the last "always" / "only" call
+    on the GPU left in it. Raises SA3Error (SA3_ERR_SCRATCH) when "always", "only" or
+    "reuse" would need more than SCRATCH_BYTES; "auto" then runs without the pre-pass."""
+    _check(out is not None, ValueError, "forward_noalloc needs out")
+    return _forward(q, k, v, cos, sin, window, lam, scale, out, out.dtype, differential, stream, pairing,
+                    rotary_dim, prep, None, True)
+
+
+def _forward(q, k, v, cos, sin, window, lam, scale, out, out_dtype, differential, stream, pairing, rotary_dim,
+             prep, workspace, noalloc):
+    """forward() and forward_noalloc(): argument checks, then one C-ABI call."""
     torch = _torch()
     if differential is None:
         differential = q.dim() == 5
@@ -279,9 +303,8 @@ def forward(q, k, v, cos, sin, *, window=-1, lam=0.0, scale=None, out=None, out_
         raise ValueError("q, k, v, cos, sin, out (and workspace) must be on one GPU")
     if dev != torch.cuda.current_device():
         with torch.cuda.device(dev):
-            return forward(q, k, v, cos, sin, window=window, lam=lam, scale=scale, out=out, out_dtype=out_dtype,
-                           differential=differential, stream=stream, pairing=pairing, rotary_dim=rotary_dim,
-                           prep=prep, workspace=workspace)
+            return _forward(q, k, v, cos, sin, window, lam, scale, out, out_dtype, differential, stream, pairing,
+                            rotary_dim, prep, workspace, noalloc)
     _check(cos.is_contiguous() and sin.is_contiguous(), ValueError, "cos and sin must be contiguous")
     qs, ks, vs, os_ = q.stride(), k.stride(), v.stride(), out.stride()
     if qs[-1] != 1 or ks[-1] != 1 or vs[-1] != 1 or os_[-1] != 1:
@@ -323,6 +346,11 @@ def forward(q, k, v, cos, sin, *, window=-1, lam=0.0, scale=None, out=None, out_
     rope = None if (pairing == "adjacent" and R == D) else _Rope(ROPE_PAIRINGS[pairing], R)
     st_p = ctypes.byref(st) if st is not None else None
     rope_p = ctypes.byref(rope) if rope is not None else None
+    if noalloc:
+        rc = lib.sa3attn_forward_noalloc(ctypes.byref(d), st_p, rope_p, PREP_POLICIES[prep])
+        if rc != 0:
+            raise SA3Error(rc, "sa3attn_forward_noalloc")
+        return out
     need = workspace_bytes(B, H, L, D, window=window, differential=differential, dtype=io, out_dtype=odt,
                            prep=prep)
     if need > 0 or prep in ("only", "reuse"):

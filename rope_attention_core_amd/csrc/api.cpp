@@ -116,11 +116,13 @@ bool rows_distinct(const long long s[3], int B, int H, int L, int D) {
     return true;
 }
 
-// The workspace arguments of sa3attn_forward_ws (absent for the other entry points).
+// The workspace arguments of sa3attn_forward_ws (absent for the other entry points);
+// scratch: sa3attn_forward_noalloc, whose workspace is the library's static device array.
 struct Workspace {
     void *ptr;
     unsigned long long bytes;
     int policy;
+    bool scratch;
 };
 
 // Shape and type checks shared by every entry point.
@@ -256,17 +258,25 @@ int forward_impl(const sa3attn_desc *d, const sa3attn_strides *sp, const sa3attn
     if (!std::isfinite(a.scale_log2)) return SA3_ERR_ARG;
 
     // workspace of the pre-pass, when the policy runs it for this call: it must hold
-    // prep_bytes, be 16-byte aligned and overlap neither an input nor out
-    const unsigned long long need = ws ? prep_need(a, ws->policy) : 0;
+    // prep_bytes, be 16-byte aligned and overlap neither an input nor out (the static
+    // scratch is a separate allocation of fixed size: AUTO skips the pre-pass when the
+    // scratch is too small, the other policies are an error)
+    unsigned long long need = ws ? prep_need(a, ws->policy) : 0;
+    if (ws && ws->scratch && need > sa3::kScratchBytes) {
+        if (ws->policy != SA3_PREP_AUTO) return SA3_ERR_SCRATCH;
+        need = 0;
+    }
     if (ws && ws->policy == SA3_PREP_ONLY) a.run_main = 0;
     if (need > 0) {
-        if (!ws->ptr) return SA3_ERR_NULL;
-        if (ws->bytes < need || !aligned16(ws->ptr)) return SA3_ERR_ARG;
-        const size_t wb = (size_t)need;
-        if (overlaps(ws->ptr, wb, d->q, q_bytes) || overlaps(ws->ptr, wb, d->k, k_bytes) ||
-            overlaps(ws->ptr, wb, d->v, v_bytes) || overlaps(ws->ptr, wb, d->cos, tab_bytes) ||
-            overlaps(ws->ptr, wb, d->sin, tab_bytes) || overlaps(ws->ptr, wb, d->out, out_bytes))
-            return SA3_ERR_ARG;
+        if (!ws->scratch) {
+            if (!ws->ptr) return SA3_ERR_NULL;
+            if (ws->bytes < need || !aligned16(ws->ptr)) return SA3_ERR_ARG;
+            const size_t wb = (size_t)need;
+            if (overlaps(ws->ptr, wb, d->q, q_bytes) || overlaps(ws->ptr, wb, d->k, k_bytes) ||
+                overlaps(ws->ptr, wb, d->v, v_bytes) || overlaps(ws->ptr, wb, d->cos, tab_bytes) ||
+                overlaps(ws->ptr, wb, d->sin, tab_bytes) || overlaps(ws->ptr, wb, d->out, out_bytes))
+                return SA3_ERR_ARG;
+        }
         a.ws = ws->ptr;
         a.prep = 1;
         a.run_prep = ws->policy != SA3_PREP_REUSE;
@@ -279,6 +289,8 @@ int forward_impl(const sa3attn_desc *d, const sa3attn_strides *sp, const sa3attn
 
     const int dev = check_device();
     if (dev != SA3_OK) return dev;
+    // the static scratch: this device's address of the array (never its host-side name)
+    if (a.prep && ws->scratch && sa3::scratch_device_ptr(&a.ws) != 0) return SA3_ERR_DEVICE;
 
     const int e = sa3::launch_forward(a);
     return e == (int)hipSuccess ? SA3_OK : SA3_ERR_LAUNCH;
@@ -312,7 +324,13 @@ int sa3attn_workspace_bytes(const sa3attn_desc *desc, int policy, unsigned long 
 
 int sa3attn_forward_ws(const sa3attn_desc *desc, const sa3attn_strides *strides, const sa3attn_rope *rope,
                        void *workspace, unsigned long long workspace_bytes, int policy) {
-    const Workspace w{workspace, workspace_bytes, policy};
+    const Workspace w{workspace, workspace_bytes, policy, false};
+    return forward_impl(desc, strides, rope, &w);
+}
+
+int sa3attn_forward_noalloc(const sa3attn_desc *desc, const sa3attn_strides *strides, const sa3attn_rope *rope,
+                            int policy) {
+    const Workspace w{nullptr, sa3::kScratchBytes, policy, true};
     return forward_impl(desc, strides, rope, &w);
 }
 
@@ -362,6 +380,9 @@ const char *sa3attn_status_string(int status) {
                    "or unusable strides";
         case SA3_ERR_DEVICE: return "SA3_ERR_DEVICE: no HIP device, or the current device is not gfx950";
         case SA3_ERR_LAUNCH: return "SA3_ERR_LAUNCH: kernel launch failed";
+        case SA3_ERR_SCRATCH:
+            return "SA3_ERR_SCRATCH: the pre-pass workspace of this call exceeds the static scratch of "
+                   "sa3attn_forward_noalloc (SA3ATTN_SCRATCH_BYTES)";
         default: return "unknown sa3attn status";
     }
 }

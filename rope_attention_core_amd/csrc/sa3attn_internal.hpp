@@ -4,6 +4,8 @@
 
 #include <cstdint>
 
+#include "sa3attn.h"
+
 namespace sa3 {
 
 // Fully validated launch description. Pointers are device pointers.
@@ -58,5 +60,11 @@ int launch_prep(const LaunchArgs &a);
 bool narrow_applies(const LaunchArgs &a);
 int launch_narrow(const LaunchArgs &a);
 int narrow_tile_rows(const LaunchArgs &a);
+
+// The static device scratch (scratch.hip) that sa3attn_forward_noalloc uses as the
+// pre-pass workspace: its size, and the current device's address of it (looked up once
+// per device with hipGetSymbolAddress; returns 0, or -1 when there is no usable device).
+constexpr unsigned long long kScratchBytes = SA3ATTN_SCRATCH_BYTES;
+int scratch_device_ptr(void **ptr);
 
 }  // namespace sa3

@@ -19,6 +19,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sa3attn.h")
 
 SA3_OK, SA3_ERR_NULL, SA3_ERR_SHAPE, SA3_ERR_UNSUPPORTED, SA3_ERR_ARG, SA3_ERR_DEVICE = 0, -1, -2, -3, -4, -5
+SA3_ERR_SCRATCH = -7
 
 
 def _declared_functions():
@@ -42,11 +43,11 @@ def test_library_exports_every_declared_function(lib):
 
 def test_status_strings_and_version(lib):
     assert sa3.status_string(0) == "SA3_OK"
-    for code in range(-6, 0):
+    for code in range(-7, 0):
         s = sa3.status_string(code)
         assert s.startswith("SA3_ERR_"), s
     assert "unknown" in sa3.status_string(12345)
-    assert sa3.version() == (0, 5)
+    assert sa3.version() == (0, 6)
 
 
 @pytest.mark.parametrize("L,D", [(1, 2), (37, 8), (8192, 16), (8192, 64), (8192, 128)])
@@ -404,3 +405,48 @@ def test_valid_ws_calls_without_gpu_report_device_error(lib):
     assert _call_ws(lib, ws, need, out=ctypes.c_void_p(ws.value - 2 * 1000 * 64 * 2)) == SA3_ERR_DEVICE
     assert _call_ws(lib, ws, 3 * 2 * _lp(1000) * 64 * 2, differential=1, st=_strides(layout="blhd"),
                     rope=_rope(1, 32)) == SA3_ERR_DEVICE
+
+
+# ---- sa3attn_forward_noalloc: the static scratch as the pre-pass workspace -----------
+
+SCRATCH = 64 << 20
+
+
+def _call_na(lib, policy=ALWAYS, st=None, rope=None, **kw):
+    return lib.sa3attn_forward_noalloc(ctypes.byref(_desc(**kw)), ctypes.byref(st) if st is not None else None,
+                                       ctypes.byref(rope) if rope is not None else None, policy)
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    assert re.search(r"#define SA3ATTN_SCRATCH_BYTES \(64ull << 20\)", text)
+    assert sa3.SCRATCH_BYTES == SCRATCH
+
+
+def test_noalloc_validation(lib):
+    assert lib.sa3attn_forward_noalloc(None, None, None, ALWAYS) == SA3_ERR_NULL
+    assert _call_na(lib, policy=5) == SA3_ERR_ARG
+    assert _call_na(lib, D=96) == SA3_ERR_UNSUPPORTED
+    assert _call_na(lib, q=None) == SA3_ERR_NULL
+    assert _call_na(lib, scale=float("inf")) == SA3_ERR_ARG
+    assert _call_na(lib, rope=_rope(1, 80)) == SA3_ERR_ARG
+    # a pre-pass workspace beyond the scratch: the medium DiT's differential shape
+    # (3 x 2 x 24 x 4096 x 64 x 2 bytes = 72 MiB) under the policies that insist on it
+    big = dict(B=2, H=24, L=4096, differential=1, dtype=1, out_dtype=2)
+    rc, need = _ws_bytes(lib, ALWAYS, **big)
+    assert rc == SA3_OK and need > SCRATCH
+    for policy in (ALWAYS, ONLY, REUSE):
+        assert _call_na(lib, policy=policy, **big) == SA3_ERR_SCRATCH
+
+
+@pytest.mark.skipif(_gpu_present(), reason="placeholder pointers must never reach a real GPU")
+def test_valid_noalloc_calls_without_gpu_report_device_error(lib):
+    # within the scratch (the long latent's plain shape: 48 MiB), and AUTO beyond it
+    # (which then runs without the pre-pass)
+    long = dict(B=2, H=24, L=4096, dtype=1, out_dtype=2)
+    rc, need = _ws_bytes(lib, ALWAYS, **long)
+    assert rc == SA3_OK and 0 < need <= SCRATCH
+    for policy in (AUTO, ALWAYS, NEVER, ONLY, REUSE):
+        assert _call_na(lib, policy=policy, **long) == SA3_ERR_DEVICE
+    assert _call_na(lib, policy=AUTO, B=2, H=24, L=4096, differential=1, dtype=1, out_dtype=2) == SA3_ERR_DEVICE
+    assert _call_na(lib, policy=ALWAYS, window=17, L=5000) == SA3_ERR_DEVICE
