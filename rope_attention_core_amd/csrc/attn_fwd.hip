@@ -87,9 +87,11 @@ constexpr int waves_for() { return 8; }
 // staging a tile is a copy (CONTIG then concerns only q, out and the table of q).
 // PERS: persistent grid (each workgroup takes several query tiles in turn, see the file
 // header); the one-round instances (false) take one query tile per workgroup.
-template <int IO, bool DIFF, bool CONTIG, int D, bool PRE, bool PERS>
-__global__ __launch_bounds__(waves_for<D>() * 64, waves_for<D>() / 4) void attn_fwd_kernel(Params P) {
-    constexpr int NW = waves_for<D>();
+// NW: waves per workgroup (8; 2 for the 64-row tiles of under-filled grids, see
+// small_grid below); the 8-wave instances keep <= 256 registers (two waves per SIMD),
+// the 2-wave ones may use more (two of them share a CU, one wave per SIMD).
+template <int IO, bool DIFF, bool CONTIG, int D, bool PRE, bool PERS, int NW = waves_for<D>()>
+__global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(Params P) {
     constexpr int NT = NW * 64;
     constexpr int NBS = DIFF ? 2 : 1;        // K tiles staged per key tile (one per branch)
     constexpr int WPB = NW / NBS;            // waves (32-row query blocks) per branch
@@ -676,7 +678,7 @@ __global__ __launch_bounds__(waves_for<D>() * 64, waves_for<D>() / 4) void attn_
     }
 }
 
-template <int IO, bool DIFF, bool CONTIG, int D, bool PRE, bool PERS>
+template <int IO, bool DIFF, bool CONTIG, int D, bool PRE, bool PERS, int NW = waves_for<D>()>
 hipError_t launch(const LaunchArgs &a, int n_qtiles) {
     Params P = make_params(a);
     P.n_qtiles = n_qtiles;
@@ -687,7 +689,7 @@ hipError_t launch(const LaunchArgs &a, int n_qtiles) {
     const unsigned grid = (unsigned)(PERS ? std::min(P.n_items, ncu) : P.n_items);
     // an item's key span is >= min(L, rows + w) keys, and >= 129 keys cover >= 3 tiles
     P.cp = (a.L >= 129 && (a.window < 0 || a.window >= 128)) ? 1 : 0;
-    hipLaunchKernelGGL((attn_fwd_kernel<IO, DIFF, CONTIG, D, PRE, PERS>), dim3(grid), dim3(waves_for<D>() * 64), 0,
+    hipLaunchKernelGGL((attn_fwd_kernel<IO, DIFF, CONTIG, D, PRE, PERS, NW>), dim3(grid), dim3(NW * 64), 0,
                        static_cast<hipStream_t>(a.stream), P);
     return hipGetLastError();
 }
@@ -700,6 +702,8 @@ hipError_t launch(const LaunchArgs &a, int n_qtiles) {
 // bookkeeping costs ~30 scalar instructions per tile), so up to 32 key tiles.
 template <int IO, bool DIFF, int D, bool PRE>
 hipError_t launch_contig(const LaunchArgs &a, int n_qtiles) {
+    if constexpr (PRE && !DIFF && D == 64)
+        if (small_grid(a)) return launch<IO, false, true, 64, true, false, 2>(a, n_qtiles);
     const long long items = (long long)n_qtiles * a.B * a.H;
     const long long bm = tile_rows(a);   // query rows per tile
     const long long all = ((long long)a.L + BN - 1) / BN;
@@ -711,6 +715,8 @@ hipError_t launch_contig(const LaunchArgs &a, int n_qtiles) {
 template <int IO, int D, bool PRE>
 hipError_t launch_io(const LaunchArgs &a, int n_qtiles) {
     if (a.contig) return a.diff ? launch_contig<IO, true, D, PRE>(a, n_qtiles) : launch_contig<IO, false, D, PRE>(a, n_qtiles);
+    if constexpr (PRE && D == 64)
+        if (small_grid(a)) return launch<IO, false, false, 64, true, false, 2>(a, n_qtiles);
     return a.diff ? launch<IO, true, false, D, PRE, false>(a, n_qtiles) : launch<IO, false, false, D, PRE, false>(a, n_qtiles);
 }
 
@@ -727,9 +733,22 @@ hipError_t launch_d(const LaunchArgs &a, int n_qtiles) {
 // built for D = 64 only, so D = 128 always takes the long-span kernel.
 bool use_narrow(const LaunchArgs &a) { return a.D == 64 && narrow_applies(a); }
 
+// Plain calls at D = 64 whose grid of 256-row query tiles leaves compute units
+// idle (fewer workgroups than compute units, e.g. B=1 H=24 L=1292: 144 workgroups on
+// 256 CUs): with the pre-pass they run 2-wave workgroups of 64 rows instead, two per
+// compute unit (LDS allows two), so every SIMD holds one wave and every CU has work;
+// without it a 2-wave workgroup would rotate and transpose each key tile for only 64
+// rows, so such calls run the pre-pass (prep_pays).
+bool small_grid(const LaunchArgs &a) {
+    if (a.D != 64 || a.diff || use_narrow(a)) return false;
+    const long long wgs = ((long long)a.L + 255) / 256 * a.B * a.H;
+    return wgs < a.n_cu;
+}
+
 // Query rows per workgroup: 32 per wave plain, 32 per pair of waves differential.
 int tile_rows(const LaunchArgs &a) {
     if (use_narrow(a)) return narrow_tile_rows(a);
+    if (a.prep && small_grid(a)) return 64;
     const int nw = a.D == 128 ? waves_for<128>() : waves_for<64>();
     return a.diff ? nw * 16 : nw * 32;
 }
@@ -755,6 +774,7 @@ unsigned long long prep_bytes(const LaunchArgs &a) {
 // without it.
 bool prep_pays(const LaunchArgs &a) {
     if (use_narrow(a)) return false;
+    if (small_grid(a)) return true;
     const int bm = tile_rows(a);
     const long long n_qtiles = ((long long)a.L + bm - 1) / bm;
     const long long visits = a.window < 0 ? n_qtiles : std::min(n_qtiles, (2ll * a.window + BN + bm - 1) / bm + 1);

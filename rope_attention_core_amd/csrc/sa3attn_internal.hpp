@@ -45,6 +45,10 @@ int launch_forward(const LaunchArgs &a);
 // host can check the grid size before launching.
 int tile_rows(const LaunchArgs &a);
 
+// Plain D = 64 calls whose grid of 256-row tiles has fewer workgroups than
+// compute units: with the pre-pass they run 64-row tiles of 2-wave workgroups.
+bool small_grid(const LaunchArgs &a);
+
 // The pre-pass (attn_prep.hip): K of each branch rotated and V converted to fp16 and
 // transposed, once per key tile, into a workspace the long-span kernel then copies
 // from. prep_bytes: the workspace it needs (0 when the call takes the single-span

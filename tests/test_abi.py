@@ -310,7 +310,14 @@ def _lp(L):
     (dict(B=2, H=24, L=4096), AUTO, 2 * 2 * 24 * 4096 * 64 * 2),
     (dict(B=1, H=24, L=2816), AUTO, 0),                                  # 11 visits
     (dict(B=1, H=24, L=2817), AUTO, 2 * 24 * _lp(2817) * 64 * 2),        # 12 visits, 288 WGs
-    (dict(B=1, H=16, L=3072), AUTO, 0),                                  # 12 visits, 192 WGs
+    # plain D = 64 grids of fewer 256-row workgroups than compute units run 64-row tiles
+    # with the pre-pass
+    (dict(B=1, H=16, L=3072), AUTO, 2 * 16 * 3072 * 64 * 2),             # 192 WGs of 256 rows
+    (dict(B=1, H=24, L=1292), AUTO, 2 * 24 * _lp(1292) * 64 * 2),        # 144
+    (dict(B=1, H=1, L=257), AUTO, 2 * 1 * _lp(257) * 64 * 2),            # 2
+    (dict(B=1, H=24, L=2560), AUTO, 2 * 24 * 2560 * 64 * 2),             # 240
+    (dict(B=1, H=24, L=2561), AUTO, 0),                                  # 264 WGs, 11 visits
+    (dict(B=1, H=24, L=2560, D=128), AUTO, 0),                           # D = 128: 256-row tiles
     (dict(B=1, H=32, L=1024, differential=1), AUTO, 0),                  # 8 visits
     (dict(B=1, H=32, L=1025, differential=1), AUTO, 3 * 32 * _lp(1025) * 64 * 2),   # 9, 288 WGs
     (dict(B=1, H=16, L=2048, differential=1), AUTO, 0),                  # 16 visits, 256 WGs
@@ -395,7 +402,8 @@ def test_valid_ws_calls_without_gpu_report_device_error(lib):
     assert _call_ws(lib, ws, need + 4096) == SA3_ERR_DEVICE
     # no workspace needed: NEVER, AUTO below the threshold, the single-span kernel
     assert _call_ws(lib, None, 0, policy=NEVER) == SA3_ERR_DEVICE
-    assert _call_ws(lib, None, 0, policy=AUTO) == SA3_ERR_DEVICE
+    assert _call_ws(lib, None, 0, policy=AUTO, differential=1) == SA3_ERR_DEVICE
+    assert _call_ws(lib, None, 0, policy=AUTO) == SA3_ERR_NULL      # a small grid: the pre-pass runs
     assert _call_ws(lib, None, 0, policy=ALWAYS, window=17) == SA3_ERR_DEVICE
     assert _call_ws(lib, None, 0, policy=ALWAYS, L=200) == SA3_ERR_DEVICE
     assert _call_ws(lib, ws, need, policy=ONLY) == SA3_ERR_DEVICE
