@@ -273,10 +273,29 @@ def graph_per_call_us(torch, fn, n_calls, replays=20):
     return t0.elapsed_time(t1) * 1e3 / (replays * n_calls)
 
 
+def prepared_loop_us(torch, sa3, b, calls=200):
+    """us per call of back-to-back eager calls through a PreparedCall (sa3.prepare), whose
+    host cost is one C-ABI call: between two HIP events, after 20 warmup calls."""
+    c = b.cfg
+    call = sa3.prepare(b.q, b.k, b.v, b.cos, b.sin, window=c.window, lam=c.lam, scale=c.scale, out=b.out,
+                       differential=c.diff, workspace=b.ws)
+    for _ in range(20):
+        call()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(calls):
+        call()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) * 1e3 / calls
+
+
 def short_graphs(torch, sa3, synth):
     """Short-latent regime: per-call time of the fused core in a loop of 100 eager calls
-    and inside one captured graph of 96 / 40 calls, next to the per-launch floor of a
-    trivial kernel (a one-element add) captured the same way."""
+    (through forward(), and through a PreparedCall) and inside one captured graph of
+    96 / 40 calls, next to the per-launch floor of a trivial kernel (a one-element add)
+    captured the same way."""
     x = torch.zeros(1, device="cuda")
     res = {"launch_floor_graph_us": round(graph_per_call_us(torch, lambda: x.add_(1.0), 96), 3)}
     for L in GRAPH_LENGTHS:
@@ -284,7 +303,8 @@ def short_graphs(torch, sa3, synth):
         b = Bench(torch, sa3, synth, cfg)
         r = b.run(100, 5)
         ent = {"shape": f"B{cfg.B} H{cfg.H} L{L} D{cfg.D} {cfg.io}",
-               "eager_loop_us_per_call": round(r["ms_mean"] * 1e3, 3)}
+               "eager_loop_us_per_call": round(r["ms_mean"] * 1e3, 3),
+               "eager_prepared_us_per_call": round(prepared_loop_us(torch, sa3, b), 3)}
         for n in GRAPH_CALLS:
             ent[f"graph{n}_us_per_call"] = round(graph_per_call_us(torch, b.call, n), 3)
         ent["gbs_compulsory_graph96"] = round(compulsory_bytes(cfg) / (ent["graph96_us_per_call"] * 1e-6) / 1e9, 1)

@@ -15,7 +15,7 @@ import ctypes
 import os
 
 __all__ = [
-    "forward", "forward_noalloc", "forward_short", "workspace_bytes", "SCRATCH_BYTES", "rope_table", "status_string", "version", "library_path",
+    "forward", "forward_noalloc", "forward_short", "prepare", "PreparedCall", "workspace_bytes", "SCRATCH_BYTES", "rope_table", "status_string", "version", "library_path",
     "load_library", "SA3Error", "F16", "BF16", "F32", "EXPORTS",
 ]
 
@@ -273,8 +273,44 @@ def forward_noalloc(q, k, v, cos, sin, out, *, window=-1, lam=0.0, scale=None, d
                     rotary_dim, prep, None, True)
 
 
+def prepare(q, k, v, cos, sin, *, window=-1, lam=0.0, scale=None, out=None, out_dtype=None, differential=None,
+            stream=None, pairing="adjacent", rotary_dim=None, prep="auto", workspace=None, noalloc=False):
+    """forward() (forward_noalloc() with noalloc=True) with every check done now: returns
+    a PreparedCall whose call() enqueues that same call again with a single C-ABI call.
+
+    For short sequences an eager call is bound by the host: forward() checks shapes,
+    dtypes, devices and strides in Python on every call. A PreparedCall keeps the
+    checked descriptor (and the workspace it allocated, if any) and only reads the
+    current stream per call (unless `stream` was given). It holds references to the
+    tensors; their storage must stay where it is (fill them in place between calls)."""
+    return _forward(q, k, v, cos, sin, window, lam, scale, out, out_dtype if out is None else out.dtype,
+                    differential, stream, pairing, rotary_dim, prep, workspace, noalloc, True)
+
+
+class PreparedCall:
+    """One checked call of the core; see prepare()."""
+
+    __slots__ = ("out", "_fn", "_args", "_desc", "_what", "_keep", "_dev", "_fixed")
+
+    def __init__(self, out, fn, args, desc, what, keep, dev, fixed):
+        self.out, self._fn, self._args, self._desc, self._what = out, fn, args, desc, what
+        self._keep, self._dev, self._fixed = keep, dev, fixed
+
+    def __call__(self):
+        torch = _torch()
+        if torch._C._cuda_getDevice() != self._dev:
+            raise ValueError(f"prepared on GPU {self._dev}; make it the current device to call it")
+        if not self._fixed:
+            self._desc.stream = _raw_stream(self._dev) if _raw_stream else \
+                torch.cuda.current_stream(self._dev).cuda_stream
+        rc = self._fn(*self._args)
+        if rc != 0:
+            raise SA3Error(rc, self._what)
+        return self.out
+
+
 def _forward(q, k, v, cos, sin, window, lam, scale, out, out_dtype, differential, stream, pairing, rotary_dim,
-             prep, workspace, noalloc):
+             prep, workspace, noalloc, prepared=False):
     """forward() and forward_noalloc(): argument checks, then one C-ABI call."""
     torch = _torch()
     if differential is None:
@@ -304,7 +340,7 @@ def _forward(q, k, v, cos, sin, window, lam, scale, out, out_dtype, differential
     if dev != torch.cuda.current_device():
         with torch.cuda.device(dev):
             return _forward(q, k, v, cos, sin, window, lam, scale, out, out_dtype, differential, stream, pairing,
-                            rotary_dim, prep, workspace, noalloc)
+                            rotary_dim, prep, workspace, noalloc, prepared)
     _check(cos.is_contiguous() and sin.is_contiguous(), ValueError, "cos and sin must be contiguous")
     qs, ks, vs, os_ = q.stride(), k.stride(), v.stride(), out.stride()
     if qs[-1] != 1 or ks[-1] != 1 or vs[-1] != 1 or os_[-1] != 1:
@@ -347,38 +383,38 @@ def _forward(q, k, v, cos, sin, window, lam, scale, out, out_dtype, differential
     st_p = ctypes.byref(st) if st is not None else None
     rope_p = ctypes.byref(rope) if rope is not None else None
     if noalloc:
-        rc = lib.sa3attn_forward_noalloc(ctypes.byref(d), st_p, rope_p, PREP_POLICIES[prep])
-        if rc != 0:
-            raise SA3Error(rc, "sa3attn_forward_noalloc")
-        return out
-    need = workspace_bytes(B, H, L, D, window=window, differential=differential, dtype=io, out_dtype=odt,
-                           prep=prep)
-    if need > 0 or prep in ("only", "reuse"):
-        if workspace is None and need > 0:
-            # "reuse" reads a workspace an earlier call filled, and "only" fills one for
-            # later calls: a workspace made here would be uninitialised, or dropped
-            _check(prep not in ("only", "reuse"), ValueError,
-                   f'prep="{prep}" needs the caller\'s workspace (workspace_bytes(...) bytes)')
-            if stream is not None:
-                # the block belongs to the stream that uses it, so the caching allocator
-                # hands it to other work only in that stream's order
-                with torch.cuda.stream(stream):
-                    workspace = torch.empty(need, dtype=torch.uint8, device=v.device)
-            else:
-                workspace = torch.empty(need, dtype=torch.uint8, device=v.device)
-        if workspace is not None:
-            _check(workspace.is_cuda and workspace.dtype == torch.uint8 and workspace.is_contiguous(), ValueError,
-                   "workspace must be a contiguous uint8 GPU tensor")
-        rc = lib.sa3attn_forward_ws(ctypes.byref(d), st_p, rope_p,
-                                    workspace.data_ptr() if workspace is not None else None,
-                                    workspace.numel() if workspace is not None else 0, PREP_POLICIES[prep])
-        what = "sa3attn_forward_ws"
-    elif st is None and rope is None:
-        rc = lib.sa3attn_forward_ex(ctypes.byref(d))
-        what = "sa3attn_forward_ex"
+        fn, args, what = lib.sa3attn_forward_noalloc, [st_p, rope_p, PREP_POLICIES[prep]], "sa3attn_forward_noalloc"
     else:
-        rc = lib.sa3attn_forward_general(ctypes.byref(d), st_p, rope_p)
-        what = "sa3attn_forward_general"
+        need = workspace_bytes(B, H, L, D, window=window, differential=differential, dtype=io, out_dtype=odt,
+                               prep=prep)
+        if need > 0 or prep in ("only", "reuse"):
+            if workspace is None and need > 0:
+                # "reuse" reads a workspace an earlier call filled, and "only" fills one for
+                # later calls: a workspace made here would be uninitialised, or dropped
+                _check(prep not in ("only", "reuse"), ValueError,
+                       f'prep="{prep}" needs the caller\'s workspace (workspace_bytes(...) bytes)')
+                if stream is not None:
+                    # the block belongs to the stream that uses it, so the caching allocator
+                    # hands it to other work only in that stream's order
+                    with torch.cuda.stream(stream):
+                        workspace = torch.empty(need, dtype=torch.uint8, device=v.device)
+                else:
+                    workspace = torch.empty(need, dtype=torch.uint8, device=v.device)
+            if workspace is not None:
+                _check(workspace.is_cuda and workspace.dtype == torch.uint8 and workspace.is_contiguous(),
+                       ValueError, "workspace must be a contiguous uint8 GPU tensor")
+            fn, what = lib.sa3attn_forward_ws, "sa3attn_forward_ws"
+            args = [st_p, rope_p, workspace.data_ptr() if workspace is not None else None,
+                    workspace.numel() if workspace is not None else 0, PREP_POLICIES[prep]]
+        elif st is None and rope is None:
+            fn, args, what = lib.sa3attn_forward_ex, [], "sa3attn_forward_ex"
+        else:
+            fn, args, what = lib.sa3attn_forward_general, [st_p, rope_p], "sa3attn_forward_general"
+    args = [ctypes.byref(d)] + args
+    if prepared:
+        keep = (q, k, v, cos, sin, workspace, st, rope)
+        return PreparedCall(out, fn, tuple(args), d, what, keep, dev, stream is not None)
+    rc = fn(*args)
     if rc != 0:
         raise SA3Error(rc, what)
     return out
