@@ -238,13 +238,24 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(Para
     const uint32_t cl = CONTIG ? (uint32_t)(tid / CPR) * RB + (uint32_t)(tid % CPR) * 16
                                : (uint32_t)(tid / CPR) * trb + kch.toff;
     // V staging: thread -> keys 2p, 2p+1 (p = tid % 32) and VD values of d from
-    // VD * (tid / 32); computed where used, so that the pre-pass instances (whose fast
-    // path copies V' tiles) keep no registers for them outside the guard's redo
+    // VD * (tid / 32); computed once for the fused instances, and where used in the
+    // pre-pass instances (whose fast path copies V' tiles and needs them only in the
+    // guard's redo), so that those keep no registers for them
+    const int vp_ = tid & 31;
+    const int vd0_ = (tid >> 5) * VD;
+    const int vpos_ = (2 * vp_ & ~12) | ((2 * vp_ & 4) << 1) | ((2 * vp_ & 8) >> 1);
+    const uint32_t vl_ = (uint32_t)(2 * vp_) * vrb + (uint32_t)vd0_ * 2;
     auto v_lane = [&](int &vd0, int &vpos, uint32_t &vl) __attribute__((always_inline)) {
-        const int vp = tid & 31;
-        vd0 = (tid >> 5) * VD;
-        vpos = (2 * vp & ~12) | ((2 * vp & 4) << 1) | ((2 * vp & 8) >> 1);
-        vl = (uint32_t)(2 * vp) * vrb + (uint32_t)vd0 * 2;
+        if constexpr (PRE) {
+            const int vp = tid & 31;
+            vd0 = (tid >> 5) * VD;
+            vpos = (2 * vp & ~12) | ((2 * vp & 4) << 1) | ((2 * vp & 8) >> 1);
+            vl = (uint32_t)(2 * vp) * vrb + (uint32_t)vd0 * 2;
+        } else {
+            vd0 = vd0_;
+            vpos = vpos_;
+            vl = vl_;
+        }
     };
     // SAFE (the redo of the V range guard, bf16 only): V comes from the input rows even
     // in the pre-pass instances and is scaled by vsc = 2^-shift as it is converted.
@@ -598,7 +609,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(Para
         // ---- range guard of the bf16 -> fp16 V conversion (see attn_common.hpp) ------
         int vshift = 0;
         if constexpr (IO == IO_BF16) {
-            if (wg_any<NW>(!acc_finite(st.o, st.l), guard)) {
+            if (__builtin_expect(wg_any<NW>(!acc_finite(st.o, st.l), guard), 0)) {
                 // largest finite |v| over the key tiles this item visited
                 uint32_t mx = 0;
                 const int k_lo = cur.tb * BN, k_hi = min(cur.te * BN, L);
