@@ -190,8 +190,18 @@ int sa3attn_forward_general(const sa3attn_desc *desc, const sa3attn_strides *str
  * that visits the key: 16 to 32 times per key at L = 4096. With a workspace the
  * library first runs a pre-pass kernel that rotates K (each branch) and converts and
  * transposes V once, into the workspace, and the attention kernel then copies its
- * key tiles from there. Outputs are bitwise identical to sa3attn_forward_general's.
- *   policy: SA3_PREP_AUTO runs the pre-pass when the grid has more workgroups than
+ * key tiles from there. Outputs are bitwise identical to sa3attn_forward_general's,
+ *     except on the small grids below in plain full attention on contiguous tensors with
+ *     the default RoPE: there a key-split kernel takes each 64-row query tile, its two
+ *     halves of the keys on separate waves merged at the end, so sums over a row's keys
+ *     are taken in another order (the same bar against the exact result, other bits).
+ *   Small grids: plain calls (not differential) at D = 64 outside the single-span
+ *     kernel whose 256-row query tiles number fewer than the device's compute units
+ *     (B x H x ceil(L / 256) < CUs) and whose 64-row tiles fit two per compute unit
+ *     (B x H x ceil(L / 64) <= 2 x CUs). With the pre-pass they run 64-row tiles
+ *     (the key-split kernel, else 2-wave workgroups of the long-span kernel).
+ *   policy: SA3_PREP_AUTO runs the pre-pass on small grids, and otherwise when the grid
+ *     has more workgroups than
  *     the current device has compute units (workgroups = B x H x ceil(L / tile rows);
  *     256 compute units are assumed when no device is current) and a key tile is
  *     visited by at least 12 query tiles of a plain call or 9 of a differential one

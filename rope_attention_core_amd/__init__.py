@@ -231,7 +231,9 @@ def forward(q, k, v, cos, sin, *, window=-1, lam=0.0, scale=None, out=None, out_
     long sequences, "always"), else through sa3attn_forward_ex, or
     sa3attn_forward_general when a tensor is a strided view or a RoPE option is set.
 
-    prep: the pre-pass policy ("auto": when the grid has more workgroups than the
+    prep: the pre-pass policy ("auto": on small plain D = 64 grids, fewer 256-row
+    query tiles than compute units and at most two 64-row tiles per compute unit, and
+    when the grid has more workgroups than the
     device has compute units and each key tile is visited by >= 12 query tiles, 9 for
     a differential call; "always"; "never"; "only": the pre-pass alone,
     out not written; "reuse": the attention kernel alone on a workspace an "always" /
@@ -240,7 +242,10 @@ def forward(q, k, v, cos, sin, *, window=-1, lam=0.0, scale=None, out=None, out_
     `stream` when one is given, else on the current stream) when not given and the
     pre-pass runs; a caller's workspace used on several streams is the caller's to
     order; "only" and "reuse" need the caller's workspace (ValueError without one).
-    All policies give bitwise identical outputs.
+    All policies give bitwise identical outputs, except plain full attention on
+    contiguous tensors with the default RoPE on those small grids: with the pre-pass a
+    key-split kernel runs them, summing each row's keys in two halves (other last bits,
+    the same error bar).
 
     pairing: "adjacent" (default) or "half" (pairs x[i], x[i + R/2]); rotary_dim: R,
     the leading dims rotated (default D; a multiple of 16), cos/sin then [>=L, R/2].

@@ -34,7 +34,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsa3attn.so")
 
 ARCH = "gfx950"
-SOURCES = ["attn_fwd.hip", "attn_narrow.hip", "attn_prep.hip", "scratch.hip", "api.cpp", "rope_table.cpp"]
+SOURCES = ["attn_fwd.hip", "attn_narrow.hip", "attn_prep.hip", "attn_split.hip", "scratch.hip", "api.cpp",
+           "rope_table.cpp"]
 # Packed FP32 instructions are kept out of the device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]

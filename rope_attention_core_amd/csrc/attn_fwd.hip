@@ -746,14 +746,19 @@ bool use_narrow(const LaunchArgs &a) { return a.D == 64 && narrow_applies(a); }
 
 // Plain calls at D = 64 whose grid of 256-row query tiles leaves compute units
 // idle (fewer workgroups than compute units, e.g. B=1 H=24 L=1292: 144 workgroups on
-// 256 CUs): with the pre-pass they run 2-wave workgroups of 64 rows instead, two per
-// compute unit (LDS allows two), so every SIMD holds one wave and every CU has work;
-// without it a 2-wave workgroup would rotate and transpose each key tile for only 64
-// rows, so such calls run the pre-pass (prep_pays).
+// 256 CUs) run 64-row tiles on the pre-pass workspace (AUTO runs the pre-pass for
+// them, prep_pays): full attention on contiguous tensors in the key-split kernel
+// (attn_split.hip: 4 waves, each key half of a tile on its own pair of waves, so every
+// SIMD runs two waves), other such calls as 2-wave workgroups of this kernel, two per
+// compute unit (one wave per SIMD, every CU busy). Without the pre-pass either would
+// rotate and transpose each key tile for only 64 rows.
+// Only grids whose 64-row tiles fit in one round of two workgroups per compute unit:
+// measured on B=1 H=24, L = 2000 (768 workgroups of 64 rows, 1.5 rounds) the 256-row
+// tiles of the fused path are 10% faster.
 bool small_grid(const LaunchArgs &a) {
     if (a.D != 64 || a.diff || use_narrow(a)) return false;
-    const long long wgs = ((long long)a.L + 255) / 256 * a.B * a.H;
-    return wgs < a.n_cu;
+    const long long bh = (long long)a.B * a.H;
+    return ((long long)a.L + 255) / 256 * bh < a.n_cu && ((long long)a.L + 63) / 64 * bh <= 2ll * a.n_cu;
 }
 
 // Query rows per workgroup: 32 per wave plain, 32 per pair of waves differential.
@@ -802,6 +807,7 @@ int launch_forward(const LaunchArgs &a) {
     if (!a.run_main) return (int)hipSuccess;
     const int bm = tile_rows(a);
     const int n_qtiles = (a.L + bm - 1) / bm;
+    if (a.prep && small_grid(a) && split_applies(a)) return launch_split(a, n_qtiles);
     return (int)(a.D == 128 ? launch_d<128>(a, n_qtiles) : launch_d<64>(a, n_qtiles));
 }
 

@@ -1,0 +1,320 @@
+// Key-split attention for grids that leave the chip under-filled, on gfx950: plain full
+// attention at D = 64 on the pre-pass workspace (rotated K' and fp16 V^T tiles).
+//
+// The long-span kernel gives each wave 32 query rows and all their keys, so a call has
+// only as many waves as 32-row blocks: B=1 H=24 L=1292 has 984, under one per SIMD of
+// an MI355X (1024 SIMDs), and a SIMD needs two waves to overlap one wave's softmax with
+// the other's MFMAs. Here a workgroup of 4 waves takes a tile of 64 query rows and
+// splits its keys in two halves: waves 0 and 1 take the two 32-row blocks over the
+// first half of the key tiles, waves 2 and 3 the same rows over the second half. Each
+// wave runs the long-span kernel's online softmax over its half (the same arithmetic
+// per element: S^T = K Q^T on MFMA, base-2 softmax with a lazy rescale, P rounded to
+// fp16, O^T = V^T P^T on MFMA); at the end the second-half waves hand (O, m, l) to the
+// first-half waves through LDS, which combine them as O = 2^(m0 - M) O0 + 2^(m1 - M) O1
+// (l likewise, M the larger base) and store out = O / l. Two workgroups share a CU (73.7
+// KB of LDS each), so every SIMD runs two waves. The sums over a row's keys are taken in
+// a different order than in the long-span kernel, so the outputs differ from it in the
+// last bits (both are held to the oracle).
+//
+// Key tiles are staged in LDS two per block (one per half) from the pre-pass workspace
+// with two stages: block j stages step j + 1 (loaded during block j - 1) and loads step
+// j + 2, then computes step j. The attention core is the one described in the "Fixes
+// the medium DiT's FP16-mixed ONNX so the attention core runs FP16" discussion
+// (sections "The bug" and "The fix").
+
+#include "attn_common.hpp"
+
+namespace sa3 {
+namespace {
+
+template <int IO>
+__global__ __launch_bounds__(256, 2) void attn_split_kernel(Params P) {
+    constexpr int NT = 256;
+    constexpr int NW = 4;
+    constexpr int D = 64;
+    constexpr int RB = D * 2;
+    constexpr int NKS = D / 16;                  // MFMA k-steps of QK^T
+    constexpr int NDB = D / 32;                  // 32-wide d blocks of O
+    constexpr int KSTR = D + 8;                  // LDS row stride of a K tile (16-bit elements)
+    constexpr int KS_ELEMS = BN * KSTR;
+    constexpr int VT_ELEMS = D * VT_STRIDE;
+    constexpr int TILE = KS_ELEMS + VT_ELEMS;    // one key tile: K rows, then V^T
+    constexpr int STAGE = 2 * TILE;              // the two halves' tiles of one step
+    constexpr int KC = BN * (D / 8) / NT;        // K' chunks (16 bytes) per thread per tile
+    constexpr int VC = D * BN / (8 * NT);        // V' chunks per thread per tile
+    constexpr int VD = BN * D / (2 * NT);        // d values per thread in the redo's V staging
+    static_assert(KC == 2 && VC == 2 && VD == 8, "tile split");
+    static_assert(2 * STAGE * 2 >= 2 * 34 * 64 * 4, "LDS too small for the merge");
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+    __shared__ uint32_t guard[2 * NW];           // words of the V range guard's reductions
+
+    const float NEG_INF = -__builtin_inff();
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int qb = wave & 1;                     // query block of this wave
+    const int kh = wave >> 1;                    // key half of this wave
+    const int r = lane & 31;
+    const int g = lane >> 5;
+    const int L = P.L;
+    const float c = P.c;
+
+    // item -> (b*h, query tile of 64 rows), XCD-aware as in the long-span kernel
+    const int n_items = P.n_items;
+    const int it = blockIdx.x;
+    const int per = n_items >> 3, rem = n_items & 7, xcd = it & 7, idx = it >> 3;
+    const int lid = (xcd < rem) ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+    const int bh = lid / P.n_qtiles;
+    const int qt = lid - bh * P.n_qtiles;
+    const int qw = qt * 64 + qb * 32;
+    const long long slab = (long long)bh * L * D;
+
+    // key tiles: half 0 takes [0, T0), half 1 [T0, T); a step past T reads zeros (past
+    // the workspace's range) and its keys, all >= L, are masked
+    const int T = P.ws_tiles;
+    const int T0 = (T + 1) >> 1;
+    const long long lpd = (long long)T * BN * D;
+    const rsrc_t rkw = make_rsrc(P.kw + (long long)bh * lpd, (uint32_t)lpd * 2);
+    const rsrc_t rvw = make_rsrc(P.vw + (long long)bh * lpd, (uint32_t)lpd * 2);
+    const rsrc_t rv = slab_rsrc(P.v, slab, RB, L, RB);      // input V (the guard's redo)
+    const rsrc_t rq = slab_rsrc(P.q, slab, RB, L, RB);
+    const rsrc_t rc = make_rsrc(P.cos, (uint32_t)L * RB);
+    const rsrc_t rs = make_rsrc(P.sin, (uint32_t)L * RB);
+    const uint32_t qsign = P.neg_scale ? 0x80008000u : 0u;
+
+    // Q rotated into registers (MFMA B-operand layout)
+    u32x4 qreg[NKS];
+    {
+        const uint32_t row = (uint32_t)(qw + r);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const uint32_t off = row * RB + (uint32_t)(16 * ks + 8 * g) * 2;
+            qreg[ks] = rope8<IO>(bload(rq, off), bload(rc, off), bload(rs, off)) ^ qsign;
+        }
+    }
+
+    // ---- staging: both halves' tiles of one step --------------------------------------
+    u32x4 rawk[2][KC], rawv[2][VC];
+    float vsc = 1.0f;
+    auto tile_of = [&](int h, int j) __attribute__((always_inline)) { return h ? T0 + j : j; };
+    auto load = [&](int j, auto safe_tag) __attribute__((always_inline)) {
+        constexpr bool SAFE = decltype(safe_tag)::value;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t t = (uint32_t)tile_of(h, j);
+#pragma unroll
+            for (int i = 0; i < KC; ++i) {
+                const int cc = tid + i * NT;
+                rawk[h][i] = bload(rkw, (t * BN + (uint32_t)(cc >> 3)) * RB + (uint32_t)(cc & 7) * 16);
+            }
+            if constexpr (SAFE) {
+                // input V: keys 2p, 2p + 1 (p = tid % 32), VD values of d from VD * (tid / 32)
+                const uint32_t off = (t * BN + 2 * (uint32_t)(tid & 31)) * RB + (uint32_t)(tid >> 5) * VD * 2;
+                rawv[h][0] = bload(rv, off);
+                rawv[h][1] = bload(rv, off + RB);
+            } else {
+#pragma unroll
+                for (int i = 0; i < VC; ++i) rawv[h][i] = bload(rvw, t * (D * BN * 2) + (uint32_t)(tid + i * NT) * 16);
+            }
+        }
+    };
+    auto stage = [&](int slot, auto safe_tag) __attribute__((always_inline)) {
+        constexpr bool SAFE = decltype(safe_tag)::value;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint16_t *Ks = smem + slot * STAGE + h * TILE;
+            uint16_t *Vt = Ks + KS_ELEMS;
+#pragma unroll
+            for (int i = 0; i < KC; ++i) {
+                const int cc = tid + i * NT;
+                *reinterpret_cast<u32x4 *>(Ks + (cc >> 3) * KSTR + (cc & 7) * 8) = rawk[h][i];
+            }
+            if constexpr (SAFE) {
+                // convert (scaled by vsc) and transpose: keys 2p, 2p + 1 at their P.V
+                // operand positions (bits 2 and 3 of the key index swapped)
+                const int k2 = 2 * (tid & 31);
+                const int vpos = (k2 & ~12) | ((k2 & 4) << 1) | ((k2 & 8) >> 1);
+                const int vd0 = (tid >> 5) * VD;
+#pragma unroll
+                for (int j = 0; j < VD; ++j) {
+                    const uint32_t wa = rawv[h][0][j >> 1], wb = rawv[h][1][j >> 1];
+                    uint32_t w;
+                    if constexpr (IO == IO_BF16) {
+                        const float fa = __uint_as_float((j & 1) ? (wa & 0xffff0000u) : (wa << 16)) * vsc;
+                        const float fb = __uint_as_float((j & 1) ? (wb & 0xffff0000u) : (wb << 16)) * vsc;
+                        w = pack2<IO_F16>(fa, fb);
+                    } else {
+                        w = (j & 1) ? __builtin_amdgcn_perm(wb, wa, 0x07060302u)
+                                    : __builtin_amdgcn_perm(wb, wa, 0x05040100u);
+                    }
+                    *reinterpret_cast<uint32_t *>(Vt + (vd0 + j) * VT_STRIDE + vpos) = w;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < VC; ++i) {
+                    const int cv = tid + i * NT;
+                    *reinterpret_cast<u32x4 *>(Vt + (cv >> 3) * VT_STRIDE + (cv & 7) * 8) = rawv[h][i];
+                }
+            }
+        }
+    };
+
+    f32x16 o[NDB];
+    float l = 0.0f, m = NEG_INF;
+
+    // one pass over this wave's key half; SAFE: the V range guard's redo
+    const int steps = T0;
+    auto run = [&](auto safe_tag) __attribute__((always_inline)) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
+        l = 0.0f;
+        m = NEG_INF;
+        load(0, safe_tag);
+        stage(0, safe_tag);
+        if (steps > 1) load(1, safe_tag);
+        __syncthreads();
+        for (int j = 0; j < steps; ++j) {
+            if (j + 1 < steps) stage((j + 1) & 1, safe_tag);
+            if (j + 2 < steps) load(j + 2, safe_tag);
+            const uint16_t *Ks = smem + (j & 1) * STAGE + kh * TILE;
+            const uint16_t *Vt = Ks + KS_ELEMS;
+            f32x16 s[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                u32x4 ka[NKS];
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) ka[ks] = lds16(Ks + (kb * 32 + r) * KSTR + 16 * ks + 8 * g);
+                f32x16 acc = {};
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) acc = mfma_qk<IO>(ka[ks], qreg[ks], acc);
+                s[kb] = acc;
+            }
+            const int k0 = tile_of(kh, j) * BN;
+            auto softmax = [&](auto mask_tag) __attribute__((always_inline)) {
+                constexpr bool MASK = decltype(mask_tag)::value;
+                TileMask mk{0, 0};
+                if constexpr (MASK) {
+                    const int lo = -(k0 + 4 * g), hi = L - 1 - (k0 + 4 * g);
+                    mk = hi < lo ? TileMask{1 << 20, 0u} : TileMask{lo, (uint32_t)(hi - lo)};
+                }
+                const float mt = tile_max<MASK>(s, c, mk);
+                const float mn = (mt > m + TAU) ? mt : m;
+                const float ea = __builtin_amdgcn_exp2f(m - mn);
+                const float a = (mn == m) ? 1.0f : ea;
+                m = mn;
+                const float nb = (mn == NEG_INF) ? 0.0f : -mn;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) o[db][i] *= a;
+                float part[2];
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    u32x4 p[2];
+                    softmax_half<false>(s[kb], kb, c, nb, mk, p, part[kb]);   // masked by tile_max
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                        for (int db = 0; db < NDB; ++db)
+                            o[db] = mfma_pv(lds16(Vt + (db * 32 + r) * VT_STRIDE + kb * 32 + 16 * tt + 8 * g), p[tt],
+                                            o[db]);
+                }
+                l = __builtin_fmaf(l, a, part[0] + part[1]);
+            };
+            if (k0 + BN > L)
+                softmax(std::true_type{});
+            else
+                softmax(std::false_type{});
+            __syncthreads();
+        }
+    };
+    run(std::false_type{});
+
+    // ---- range guard of the bf16 -> fp16 V conversion (see attn_common.hpp) -------------
+    int vshift = 0;
+    if constexpr (IO == IO_BF16) {
+        if (__builtin_expect(wg_any<NW>(!acc_finite(o, l), guard), 0)) {
+            uint32_t mx = 0;
+            for (int cc = tid; cc < L * (D / 8); cc += NT)
+                mx = max(mx, bf16_finite_absmax(bload(rv, (uint32_t)(cc >> 3) * RB + (uint32_t)(cc & 7) * 16)));
+            vshift = vshift_of(wg_max<NW>(mx, guard + NW));
+            if (vshift > 0) {
+                vsc = exp2i(-vshift);
+                run(std::true_type{});
+            }
+        }
+    }
+
+    // ---- merge the halves, normalise, store rows < L -------------------------------------
+    // The second-half waves hand O, m and l to the first-half waves of the same rows: element
+    // e of lane x of query block qb at word (qb * 34 + e) * 64 + x (m at e = 32, l at 33).
+    float *xb = reinterpret_cast<float *>(smem);
+    __syncthreads();   // every wave is done with the staged tiles
+    if (kh == 1) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) xb[(qb * 34 + db * 16 + i) * 64 + lane] = o[db][i];
+        xb[(qb * 34 + 32) * 64 + lane] = m;
+        xb[(qb * 34 + 33) * 64 + lane] = l;
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    const int qi = qw + r;
+    if (qi >= L) return;
+    {
+        const float m1 = xb[(qb * 34 + 32) * 64 + lane];
+        const float mx = fmaxf(m, m1);
+        // a half with no valid key has m = -inf and contributes nothing (2^-inf = 0)
+        const float a0 = __builtin_amdgcn_exp2f(m - mx);
+        const float a1 = __builtin_amdgcn_exp2f(m1 - mx);
+        l = a0 * l + a1 * xb[(qb * 34 + 33) * 64 + lane];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[db][i] = a0 * o[db][i] + a1 * xb[(qb * 34 + db * 16 + i) * 64 + lane];
+    }
+    // (2^vshift undoes the guard's scaling of V; l >= 1, so inv * 2^vshift stays finite)
+    const float inv = (1.0f / pair_sum(l)) * exp2i(vshift);
+    const long long row = slab + (long long)qi * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) {
+            float y[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) y[j] = o[db][grp * 4 + j] * inv;
+            const int d = db * 32 + grp * 8 + g * 4;
+            if (P.out_dtype == OUT_F32) {
+                *reinterpret_cast<f32x4 *>(static_cast<float *>(P.out) + row + d) = f32x4{y[0], y[1], y[2], y[3]};
+            } else if (P.out_dtype == OUT_BF16) {
+                *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(P.out) + row + d) =
+                    u32x2{pack2<IO_BF16>(y[0], y[1]), pack2<IO_BF16>(y[2], y[3])};
+            } else {
+                *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(P.out) + row + d) =
+                    u32x2{pack2<IO_F16>(y[0], y[1]), pack2<IO_F16>(y[2], y[3])};
+            }
+        }
+}
+
+}  // namespace
+
+// Plain full attention at D = 64, contiguous, default RoPE, with the pre-pass workspace.
+bool split_applies(const LaunchArgs &a) {
+    return a.D == 64 && !a.diff && a.contig && a.window < 0 && a.prep;
+}
+
+int launch_split(const LaunchArgs &a, int n_qtiles) {
+    Params P = make_params(a);
+    P.n_qtiles = n_qtiles;
+    P.n_items = n_qtiles * a.B * a.H;
+    if (a.dtype == 1)
+        hipLaunchKernelGGL(attn_split_kernel<IO_BF16>, dim3((unsigned)P.n_items), dim3(256), 0,
+                           static_cast<hipStream_t>(a.stream), P);
+    else
+        hipLaunchKernelGGL(attn_split_kernel<IO_F16>, dim3((unsigned)P.n_items), dim3(256), 0,
+                           static_cast<hipStream_t>(a.stream), P);
+    return (int)hipGetLastError();
+}
+
+}  // namespace sa3

@@ -45,6 +45,11 @@ int launch_forward(const LaunchArgs &a);
 // host can check the grid size before launching.
 int tile_rows(const LaunchArgs &a);
 
+// The key-split kernel (attn_split.hip) for such grids under plain full attention with
+// the pre-pass (contiguous, default RoPE): whether it applies, and its launcher.
+bool split_applies(const LaunchArgs &a);
+int launch_split(const LaunchArgs &a, int n_qtiles);
+
 // Plain D = 64 calls whose grid of 256-row tiles has fewer workgroups than
 // compute units: with the pre-pass they run 64-row tiles of 2-wave workgroups.
 bool small_grid(const LaunchArgs &a);

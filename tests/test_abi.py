@@ -312,11 +312,13 @@ def _lp(L):
     (dict(B=1, H=24, L=2817), AUTO, 2 * 24 * _lp(2817) * 64 * 2),        # 12 visits, 288 WGs
     # plain D = 64 grids of fewer 256-row workgroups than compute units run 64-row tiles
     # with the pre-pass
-    (dict(B=1, H=16, L=3072), AUTO, 2 * 16 * 3072 * 64 * 2),             # 192 WGs of 256 rows
+    (dict(B=1, H=16, L=3072), AUTO, 0),                                  # 768 of 64 rows: 1.5 rounds
     (dict(B=1, H=24, L=1292), AUTO, 2 * 24 * _lp(1292) * 64 * 2),        # 144
     (dict(B=1, H=1, L=257), AUTO, 2 * 1 * _lp(257) * 64 * 2),            # 2
-    (dict(B=1, H=24, L=2560), AUTO, 2 * 24 * 2560 * 64 * 2),             # 240
-    (dict(B=1, H=24, L=2561), AUTO, 0),                                  # 264 WGs, 11 visits
+    (dict(B=1, H=12, L=2560), AUTO, 2 * 12 * 2560 * 64 * 2),             # 120 (480 of 64 rows)
+    (dict(B=1, H=24, L=2560), AUTO, 0),                                  # 240 (960 of 64 rows)
+    (dict(B=1, H=24, L=1344), AUTO, 2 * 24 * 1344 * 64 * 2),             # 144 (504 of 64 rows)
+    (dict(B=1, H=24, L=1345), AUTO, 0),                                  # 144 (528 of 64 rows)
     (dict(B=1, H=24, L=2560, D=128), AUTO, 0),                           # D = 128: 256-row tiles
     (dict(B=1, H=32, L=1024, differential=1), AUTO, 0),                  # 8 visits
     (dict(B=1, H=32, L=1025, differential=1), AUTO, 3 * 32 * _lp(1025) * 64 * 2),   # 9, 288 WGs

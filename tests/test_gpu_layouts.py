@@ -24,11 +24,11 @@ def _blhd_view(t):
     return t.transpose(-2, -3).contiguous().transpose(-2, -3)
 
 
-def _run(cfg, inp, q, k, v, out=None):
+def _run(cfg, inp, q, k, v, out=None, **kw):
     torch = G.torch_mod()
     c, s = G.device_table(cfg.L, cfg.D, cfg.base)
     res = G.sa3.forward(q, k, v, c, s, window=cfg.window, lam=cfg.lam, scale=cfg.scale, out=out,
-                        out_dtype=G.out_torch_dtype(cfg.out_dtype), differential=cfg.diff)
+                        out_dtype=G.out_torch_dtype(cfg.out_dtype), differential=cfg.diff, **kw)
     torch.cuda.synchronize()
     return res
 
@@ -54,7 +54,9 @@ def test_blhd_inputs(name, kw, strided_out):
     inp = synth.make_inputs(cfg)
     q, k, v = (G.to_device(inp[n], cfg.io) for n in ("q", "k", "v"))
     G.note(f"  strided: {cfg.name} {kw} out strided={strided_out}")
-    base = _run(cfg, inp, q, k, v)
+    # the contiguous call without the pre-pass: on small plain full-attention grids the
+    # pre-pass would send it to the key-split kernel, which views never take
+    base = _run(cfg, inp, q, k, v, prep="never")
     qs, ks, vs = _blhd_view(q), _blhd_view(k), _blhd_view(v)
     assert not qs.is_contiguous() and qs.stride(-1) == 1
     out = None
@@ -73,7 +75,7 @@ def test_heads_of_a_wider_buffer():
     cfg = synth.config("dit_2min", H=4, L=517, seed=9300)
     inp = synth.make_inputs(cfg)
     q, k, v = (G.to_device(inp[n], cfg.io) for n in ("q", "k", "v"))
-    base = _run(cfg, inp, q, k, v)
+    base = _run(cfg, inp, q, k, v, prep="never")
     B, H, L, D = v.shape
     qkv = torch.empty((B, L, 3 * H, D), dtype=q.dtype, device="cuda")
     qkv[:, :, 0:H] = q.transpose(1, 2)
