@@ -16,9 +16,11 @@
 // a different order than in the long-span kernel, so the outputs differ from it in the
 // last bits (both are held to the oracle).
 //
-// Key tiles are staged in LDS two per block (one per half) from the pre-pass workspace
-// with two stages: block j stages step j + 1 (loaded during block j - 1) and loads step
-// j + 2, then computes step j. The attention core is the one described in the "Fixes
+// Key tiles are copied into LDS from the pre-pass workspace, one per half and step, into
+// two buffers each for K and for V^T: step j stages K(j + 2) and V(j + 1) (loaded during
+// step j - 1), loads K(j + 3) and V(j + 2), issues QK^T(j + 1) into a second score set,
+// whose MFMAs run under the softmax of step j, then computes the softmax and P.V of
+// step j; one barrier per step. The attention core is the one described in the "Fixes
 // the medium DiT's FP16-mixed ONNX so the attention core runs FP16" discussion
 // (sections "The bug" and "The fix").
 
@@ -38,8 +40,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(Params P) {
     constexpr int KSTR = D + 8;                  // LDS row stride of a K tile (16-bit elements)
     constexpr int KS_ELEMS = BN * KSTR;
     constexpr int VT_ELEMS = D * VT_STRIDE;
-    constexpr int TILE = KS_ELEMS + VT_ELEMS;    // one key tile: K rows, then V^T
-    constexpr int STAGE = 2 * TILE;              // the two halves' tiles of one step
+    constexpr int STAGE = 2 * (KS_ELEMS + VT_ELEMS);   // one buffer of K and of V^T per half
     constexpr int KC = BN * (D / 8) / NT;        // K' chunks (16 bytes) per thread per tile
     constexpr int VC = D * BN / (8 * NT);        // V' chunks per thread per tile
     constexpr int VD = BN * D / (2 * NT);        // d values per thread in the redo's V staging
@@ -93,12 +94,17 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(Params P) {
         }
     }
 
-    // ---- staging: both halves' tiles of one step --------------------------------------
+    // ---- staging: both halves' tiles of one step ------------------------------------
+    // K tiles are staged two steps ahead of their use in P.V's step (QK^T(j + 1) runs in
+    // step j), V tiles one step ahead; each has two LDS buffers per half.
     u32x4 rawk[2][KC], rawv[2][VC];
     float vsc = 1.0f;
     auto tile_of = [&](int h, int j) __attribute__((always_inline)) { return h ? T0 + j : j; };
-    auto load = [&](int j, auto safe_tag) __attribute__((always_inline)) {
-        constexpr bool SAFE = decltype(safe_tag)::value;
+    auto kbuf = [&](int slot, int h) __attribute__((always_inline)) { return smem + (slot * 2 + h) * KS_ELEMS; };
+    auto vbuf = [&](int slot, int h) __attribute__((always_inline)) {
+        return smem + 4 * KS_ELEMS + (slot * 2 + h) * VT_ELEMS;
+    };
+    auto load_k = [&](int j) __attribute__((always_inline)) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const uint32_t t = (uint32_t)tile_of(h, j);
@@ -107,6 +113,13 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(Params P) {
                 const int cc = tid + i * NT;
                 rawk[h][i] = bload(rkw, (t * BN + (uint32_t)(cc >> 3)) * RB + (uint32_t)(cc & 7) * 16);
             }
+        }
+    };
+    auto load_v = [&](int j, auto safe_tag) __attribute__((always_inline)) {
+        constexpr bool SAFE = decltype(safe_tag)::value;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t t = (uint32_t)tile_of(h, j);
             if constexpr (SAFE) {
                 // input V: keys 2p, 2p + 1 (p = tid % 32), VD values of d from VD * (tid / 32)
                 const uint32_t off = (t * BN + 2 * (uint32_t)(tid & 31)) * RB + (uint32_t)(tid >> 5) * VD * 2;
@@ -118,17 +131,22 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(Params P) {
             }
         }
     };
-    auto stage = [&](int slot, auto safe_tag) __attribute__((always_inline)) {
-        constexpr bool SAFE = decltype(safe_tag)::value;
+    auto stage_k = [&](int slot) __attribute__((always_inline)) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            uint16_t *Ks = smem + slot * STAGE + h * TILE;
-            uint16_t *Vt = Ks + KS_ELEMS;
+            uint16_t *Ks = kbuf(slot, h);
 #pragma unroll
             for (int i = 0; i < KC; ++i) {
                 const int cc = tid + i * NT;
                 *reinterpret_cast<u32x4 *>(Ks + (cc >> 3) * KSTR + (cc & 7) * 8) = rawk[h][i];
             }
+        }
+    };
+    auto stage_v = [&](int slot, auto safe_tag) __attribute__((always_inline)) {
+        constexpr bool SAFE = decltype(safe_tag)::value;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint16_t *Vt = vbuf(slot, h);
             if constexpr (SAFE) {
                 // convert (scaled by vsc) and transpose: keys 2p, 2p + 1 at their P.V
                 // operand positions (bits 2 and 3 of the key index swapped)
@@ -159,73 +177,96 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(Params P) {
         }
     };
 
+    // S^T of this wave's 32 rows against key tile j of its half (K in buffer j & 1)
+    auto qk = [&](int j, f32x16 (&s)[2]) __attribute__((always_inline)) {
+        const uint16_t *Ks = kbuf(j & 1, kh);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            u32x4 ka[NKS];
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) ka[ks] = lds16(Ks + (kb * 32 + r) * KSTR + 16 * ks + 8 * g);
+            f32x16 acc = {};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) acc = mfma_qk<IO>(ka[ks], qreg[ks], acc);
+            s[kb] = acc;
+        }
+    };
+
     f32x16 o[NDB];
     float l = 0.0f, m = NEG_INF;
 
-    // one pass over this wave's key half; SAFE: the V range guard's redo
+    // one step: stage K(j + 2) and V(j + 1), load K(j + 3) and V(j + 2), issue QK^T(j + 1)
+    // into `nxt`, then the softmax and P.V of step j on `cur`. Past a half's last step the
+    // tiles are the other half's or lie past the workspace (read as zeros): staged,
+    // computed and never used, which keeps the step one block of straight-line code.
     const int steps = T0;
+    auto step = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2], auto safe_tag) __attribute__((always_inline)) {
+        stage_k(j & 1);
+        stage_v((j + 1) & 1, safe_tag);
+        load_k(j + 3);
+        load_v(j + 2, safe_tag);
+        qk(j + 1, nxt);
+        const uint16_t *Vt = vbuf(j & 1, kh);
+        const int k0 = tile_of(kh, j) * BN;
+        auto softmax = [&](auto mask_tag) __attribute__((always_inline)) {
+            constexpr bool MASK = decltype(mask_tag)::value;
+            TileMask mk{0, 0};
+            if constexpr (MASK) {
+                const int lo = -(k0 + 4 * g), hi = L - 1 - (k0 + 4 * g);
+                mk = hi < lo ? TileMask{1 << 20, 0u} : TileMask{lo, (uint32_t)(hi - lo)};
+            }
+            const float mt = tile_max<MASK>(cur, c, mk);
+            const float mn = (mt > m + TAU) ? mt : m;
+            const float ea = __builtin_amdgcn_exp2f(m - mn);
+            const float a = (mn == m) ? 1.0f : ea;
+            m = mn;
+            const float nb = (mn == NEG_INF) ? 0.0f : -mn;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) o[db][i] *= a;
+            float part[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                u32x4 p[2];
+                softmax_half<false>(cur[kb], kb, c, nb, mk, p, part[kb]);   // masked by tile_max
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+                        o[db] = mfma_pv(lds16(Vt + (db * 32 + r) * VT_STRIDE + kb * 32 + 16 * tt + 8 * g), p[tt],
+                                        o[db]);
+            }
+            l = __builtin_fmaf(l, a, part[0] + part[1]);
+        };
+        if (k0 + BN > L)
+            softmax(std::true_type{});
+        else
+            softmax(std::false_type{});
+        __syncthreads();
+    };
+
+    // one pass over this wave's key half; SAFE: the V range guard's redo
     auto run = [&](auto safe_tag) __attribute__((always_inline)) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
         l = 0.0f;
         m = NEG_INF;
-        load(0, safe_tag);
-        stage(0, safe_tag);
-        if (steps > 1) load(1, safe_tag);
+        load_k(0);
+        load_v(0, safe_tag);
+        stage_k(0);
+        stage_v(0, safe_tag);
+        load_k(1);
+        stage_k(1);
         __syncthreads();
-        for (int j = 0; j < steps; ++j) {
-            if (j + 1 < steps) stage((j + 1) & 1, safe_tag);
-            if (j + 2 < steps) load(j + 2, safe_tag);
-            const uint16_t *Ks = smem + (j & 1) * STAGE + kh * TILE;
-            const uint16_t *Vt = Ks + KS_ELEMS;
-            f32x16 s[2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                u32x4 ka[NKS];
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) ka[ks] = lds16(Ks + (kb * 32 + r) * KSTR + 16 * ks + 8 * g);
-                f32x16 acc = {};
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) acc = mfma_qk<IO>(ka[ks], qreg[ks], acc);
-                s[kb] = acc;
-            }
-            const int k0 = tile_of(kh, j) * BN;
-            auto softmax = [&](auto mask_tag) __attribute__((always_inline)) {
-                constexpr bool MASK = decltype(mask_tag)::value;
-                TileMask mk{0, 0};
-                if constexpr (MASK) {
-                    const int lo = -(k0 + 4 * g), hi = L - 1 - (k0 + 4 * g);
-                    mk = hi < lo ? TileMask{1 << 20, 0u} : TileMask{lo, (uint32_t)(hi - lo)};
-                }
-                const float mt = tile_max<MASK>(s, c, mk);
-                const float mn = (mt > m + TAU) ? mt : m;
-                const float ea = __builtin_amdgcn_exp2f(m - mn);
-                const float a = (mn == m) ? 1.0f : ea;
-                m = mn;
-                const float nb = (mn == NEG_INF) ? 0.0f : -mn;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) o[db][i] *= a;
-                float part[2];
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    u32x4 p[2];
-                    softmax_half<false>(s[kb], kb, c, nb, mk, p, part[kb]);   // masked by tile_max
-#pragma unroll
-                    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                        for (int db = 0; db < NDB; ++db)
-                            o[db] = mfma_pv(lds16(Vt + (db * 32 + r) * VT_STRIDE + kb * 32 + 16 * tt + 8 * g), p[tt],
-                                            o[db]);
-                }
-                l = __builtin_fmaf(l, a, part[0] + part[1]);
-            };
-            if (k0 + BN > L)
-                softmax(std::true_type{});
-            else
-                softmax(std::false_type{});
-            __syncthreads();
+        f32x16 sa[2], sb[2];
+        qk(0, sa);
+        load_k(2);
+        load_v(1, safe_tag);
+        __syncthreads();   // every wave has read K(0) before step 0 stages K(2) over it
+        for (int j = 0; j < steps; j += 2) {
+            step(j, sa, sb, safe_tag);
+            if (j + 1 < steps) step(j + 1, sb, sa, safe_tag);
         }
     };
     run(std::false_type{});
