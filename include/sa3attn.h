@@ -191,17 +191,26 @@ int sa3attn_forward_general(const sa3attn_desc *desc, const sa3attn_strides *str
  * library first runs a pre-pass kernel that rotates K (each branch) and converts and
  * transposes V once, into the workspace, and the attention kernel then copies its
  * key tiles from there. Outputs are bitwise identical to sa3attn_forward_general's,
- *     except on the small grids below in plain full attention on contiguous tensors with
- *     the default RoPE: there a key-split kernel takes each 64-row query tile, its two
- *     halves of the keys on separate waves merged at the end, so sums over a row's keys
- *     are taken in another order (the same bar against the exact result, other bits).
+ *     except on the two kinds of grid below, where the sums over a row's keys are taken
+ *     in another order (the same bar against the exact result, other last bits; calls
+ *     of the same shape and policy give the same bits run to run).
  *   Small grids: plain calls (not differential) at D = 64 outside the single-span
  *     kernel whose 256-row query tiles number fewer than the device's compute units
  *     (B x H x ceil(L / 256) < CUs) and whose 64-row tiles fit two per compute unit
- *     (B x H x ceil(L / 64) <= 2 x CUs). With the pre-pass they run 64-row tiles
- *     (the key-split kernel, else 2-wave workgroups of the long-span kernel).
- *   policy: SA3_PREP_AUTO runs the pre-pass on small grids, and otherwise when the grid
- *     has more workgroups than
+ *     (B x H x ceil(L / 64) <= 2 x CUs). With the pre-pass they run 64-row tiles:
+ *     full attention on contiguous tensors with the default RoPE in a key-split kernel
+ *     (each tile's keys in two halves on separate waves, merged at the end), other
+ *     calls in 2-wave workgroups of the long-span kernel (the same bits).
+ *   Split tail: other long-span calls whose grid of query tiles (256 rows, 128
+ *     differential; T = B x H x ceil(L / rows)) leaves a last round of r = T mod CUs
+ *     tiles with 0 < r <= CUs / 2, except grids of more tiles than CUs whose tiles span
+ *     at most 32 key tiles (which run persistent when contiguous). With the pre-pass
+ *     each of those r tiles is split into k = min(4, CUs / r) contiguous key ranges of
+ *     at least 4 key tiles (k >= 2), one workgroup each; the last range to finish a
+ *     tile merges the ranges' partial results, which the workspace holds after K' and
+ *     V' (r x k x 8 x 64 x (D / 32 x 16 + 4) floats, then r counters in 256-byte units).
+ *   policy: SA3_PREP_AUTO runs the pre-pass on small grids and split-tail grids, and
+ *     otherwise when the grid has more workgroups than
  *     the current device has compute units (workgroups = B x H x ceil(L / tile rows);
  *     256 compute units are assumed when no device is current) and a key tile is
  *     visited by at least 12 query tiles of a plain call or 9 of a differential one
@@ -218,9 +227,11 @@ int sa3attn_forward_general(const sa3attn_desc *desc, const sa3attn_strides *str
  *     any policy: ONLY then enqueues nothing and REUSE runs the call as usual.
  *   sa3attn_workspace_bytes: *bytes = the workspace the call shape takes under
  *     `policy`: (2 or 3, differential) x B x H x ceil(L/64)*64 x D x 2 bytes when
- *     the pre-pass runs, else 0. Reads only B, H, L, D, window, dtype, out_dtype
- *     and differential of desc; shape errors as sa3attn_forward_ex's, SA3_ERR_NULL
- *     for a NULL desc or bytes, SA3_ERR_ARG for an unknown policy.
+ *     the pre-pass runs, plus the split tail's partials and counters where it
+ *     applies, else 0 (the compute-unit count is the current device's). Reads only
+ *     B, H, L, D, window, dtype, out_dtype and differential of desc; shape errors as
+ *     sa3attn_forward_ex's, SA3_ERR_NULL for a NULL desc or bytes, SA3_ERR_ARG for an
+ *     unknown policy.
  *   sa3attn_forward_ws: sa3attn_forward_general plus
  *     workspace: device memory of workspace_bytes bytes (at least what
  *       sa3attn_workspace_bytes gives for the same shape and policy), 16-byte
@@ -249,9 +260,12 @@ int sa3attn_forward_ws(const sa3attn_desc *desc, const sa3attn_strides *strides,
  * (hipGetSymbolAddress) and caches it.
  *   desc, strides, rope: as for sa3attn_forward_general; the caller still provides
  *     q, k, v, cos, sin and out.
- *   policy: as for sa3attn_forward_ws. When the pre-pass would need more than
- *     SA3ATTN_SCRATCH_BYTES (sa3attn_workspace_bytes gives the size): AUTO runs the
- *     call without it (the same outputs, bitwise); ALWAYS, ONLY and REUSE return
+ *   policy: as for sa3attn_forward_ws. When the pre-pass with the split tail's
+ *     partials would need more than SA3ATTN_SCRATCH_BYTES (sa3attn_workspace_bytes
+ *     gives the size) but K' and V' alone fit, the call runs the pre-pass without the
+ *     split tail (as a workspace call would run the same grid without one: bitwise the
+ *     fused path's outputs). When K' and V' alone do not fit either: AUTO runs the
+ *     call without the pre-pass (bitwise as NEVER); ALWAYS, ONLY and REUSE return
  *     SA3_ERR_SCRATCH before anything is enqueued.
  *   Sharing: every call on one GPU uses the same array, whose contents persist from
  *     call to call (REUSE reads what the last ALWAYS or ONLY call on that GPU wrote).

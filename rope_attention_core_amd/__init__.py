@@ -232,7 +232,8 @@ def forward(q, k, v, cos, sin, *, window=-1, lam=0.0, scale=None, out=None, out_
     sa3attn_forward_general when a tensor is a strided view or a RoPE option is set.
 
     prep: the pre-pass policy ("auto": on small plain D = 64 grids, fewer 256-row
-    query tiles than compute units and at most two 64-row tiles per compute unit, and
+    query tiles than compute units and at most two 64-row tiles per compute unit; on
+    grids whose last round of query tiles fills at most half the compute units; and
     when the grid has more workgroups than the
     device has compute units and each key tile is visited by >= 12 query tiles, 9 for
     a differential call; "always"; "never"; "only": the pre-pass alone,
@@ -243,9 +244,11 @@ def forward(q, k, v, cos, sin, *, window=-1, lam=0.0, scale=None, out=None, out_
     pre-pass runs; a caller's workspace used on several streams is the caller's to
     order; "only" and "reuse" need the caller's workspace (ValueError without one).
     All policies give bitwise identical outputs, except plain full attention on
-    contiguous tensors with the default RoPE on those small grids: with the pre-pass a
-    key-split kernel runs them, summing each row's keys in two halves (other last bits,
-    the same error bar).
+    contiguous tensors with the default RoPE on those small grids (with the pre-pass a
+    key-split kernel runs them, summing each row's keys in two halves) and grids whose
+    last round of query tiles fills at most half the compute units (with the pre-pass
+    each of those tiles is split into key ranges merged at the end; "auto" runs the
+    pre-pass there): other last bits, the same error bar.
 
     pairing: "adjacent" (default) or "half" (pairs x[i], x[i + R/2]); rotary_dim: R,
     the leading dims rotated (default D; a multiple of 16), cos/sin then [>=L, R/2].

@@ -144,6 +144,7 @@ int check_shape(const sa3attn_desc *d) {
 // The launch fields that decide which kernel runs (and so the workspace size).
 void shape_args(const sa3attn_desc *d, sa3::LaunchArgs &a) {
     a.n_cu = device_cus();
+    a.tail_ok = 1;
     a.B = d->B;
     a.H = d->H;
     a.L = d->L;
@@ -262,6 +263,11 @@ int forward_impl(const sa3attn_desc *d, const sa3attn_strides *sp, const sa3attn
     // scratch is a separate allocation of fixed size: AUTO skips the pre-pass when the
     // scratch is too small, the other policies are an error)
     unsigned long long need = ws ? prep_need(a, ws->policy) : 0;
+    if (ws && ws->scratch && need > sa3::kScratchBytes) {
+        // without the split tail's partials the pre-pass may still fit
+        a.tail_ok = 0;
+        need = prep_need(a, ws->policy);
+    }
     if (ws && ws->scratch && need > sa3::kScratchBytes) {
         if (ws->policy != SA3_PREP_AUTO) return SA3_ERR_SCRATCH;
         need = 0;

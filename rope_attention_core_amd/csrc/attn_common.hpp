@@ -56,6 +56,13 @@ struct Params {
     int ws_tiles;                 // Lp / 64
     int n_items;                  // query tiles x B x H (the long-span kernel's work items)
     int cp;                       // every item spans >= 3 key tiles (its pipeline may run on)
+    // split tail (one-round-per-tile grids with the pre-pass): the last n_tail query tiles
+    // are each split into n_split key ranges, one workgroup per range, after n_full whole
+    // tiles; each range's (O, m, l) goes to `part`, and the workgroup that brings the
+    // tile's counter in `cnt` to n_split merges them (n_split = 0: no split)
+    int n_full, n_split, n_tail;
+    float *part;
+    uint32_t *cnt;
 };
 
 // Kernel parameters common to every instance (n_qtiles and window are set by the caller).
@@ -98,7 +105,23 @@ inline Params make_params(const LaunchArgs &a) {
     P.ws_tiles = (int)(lp / BN);
     P.kw = a.prep ? static_cast<uint16_t *>(a.ws) : nullptr;
     P.vw = a.prep ? P.kw + (a.diff ? 2 : 1) * (long long)a.B * a.H * lp * a.D : nullptr;
+    P.n_full = 0;
+    P.n_split = 0;
+    P.n_tail = 0;
+    P.part = nullptr;
+    P.cnt = nullptr;
     return P;
+}
+
+// The split tail's fields (tail_plan), for the long-span kernel and the pre-pass.
+inline void set_tail(Params &P, const LaunchArgs &a) {
+    const TailPlan t = tail_plan(a);
+    if (t.k == 0) return;
+    P.n_full = t.n_full;
+    P.n_split = t.k;
+    P.n_tail = t.n_tail;
+    P.part = reinterpret_cast<float *>(static_cast<char *>(a.ws) + t.part_off);
+    P.cnt = reinterpret_cast<uint32_t *>(static_cast<char *>(a.ws) + t.cnt_off);
 }
 
 // ---- element conversions -------------------------------------------------------

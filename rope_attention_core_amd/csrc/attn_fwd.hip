@@ -90,8 +90,9 @@ constexpr int waves_for() { return 8; }
 // NW: waves per workgroup (8; 2 for the 64-row tiles of under-filled grids, see
 // small_grid below); the 8-wave instances keep <= 256 registers (two waves per SIMD),
 // the 2-wave ones may use more (two of them share a CU, one wave per SIMD).
-template <int IO, bool DIFF, bool CONTIG, int D, bool PRE, bool PERS, int NW = waves_for<D>()>
+template <int IO, bool DIFF, bool CONTIG, int D, bool PRE, bool PERS, int NW = waves_for<D>(), bool TAIL = false>
 __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(Params P) {
+    static_assert(!TAIL || (!PERS && PRE && NW == waves_for<D>()), "the split tail is for one-round pre-pass grids");
     constexpr int NT = NW * 64;
     constexpr int NBS = DIFF ? 2 : 1;        // K tiles staged per key tile (one per branch)
     constexpr int WPB = NW / NBS;            // waves (32-row query blocks) per branch
@@ -155,9 +156,13 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(Para
     struct Item {
         int bh, qt, tb, te;
     };
-    auto item_at = [&](int it) __attribute__((always_inline)) {
-        const int per = n_items >> 3, rem = n_items & 7, xcd = it & 7, idx = it >> 3;
-        const int lid = (xcd < rem) ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+    // the XCD-aware remap of workgroup (or item) `it` of n
+    auto remap = [](int it, int n) __attribute__((always_inline)) {
+        const int per = n >> 3, rem = n & 7, xcd = it & 7, idx = it >> 3;
+        return (xcd < rem) ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+    };
+    // linear tile id -> (b*h, query tile, key-tile range)
+    auto tile_of_lid = [&](int lid) __attribute__((always_inline)) {
         Item x;
         x.bh = lid / P.n_qtiles;
         x.qt = lid - x.bh * P.n_qtiles;
@@ -172,6 +177,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(Para
         x.te = (k_hi + BN - 1) / BN;
         return x;
     };
+    auto item_at = [&](int it) __attribute__((always_inline)) { return tile_of_lid(remap(it, n_items)); };
     // K (each branch) and V of one (b, h): the pre-pass workspace or the inputs
     auto kv_of = [&](int bh, rsrc_t (&kk)[NBS], rsrc_t &vv) __attribute__((always_inline)) {
         if constexpr (PRE) {
@@ -192,6 +198,24 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(Para
 
     int item = blockIdx.x;
     Item cur = item_at(item);
+    // split tail (one-round instances): workgroups from n_full on take key range `part`
+    // of split tile `spl` (the tiles after the n_full whole ones), XCD-aware like the rest
+    int spl = -1, part = 0;
+    if constexpr (TAIL) {
+        if (P.n_split > 0) {
+            if (item < P.n_full) {
+                cur = tile_of_lid(remap(item, P.n_full));
+            } else {
+                const int ls = remap(item - P.n_full, P.n_tail * P.n_split);
+                spl = ls / P.n_split;
+                part = ls - spl * P.n_split;
+                cur = tile_of_lid(P.n_full + spl);
+                const int tb = cur.tb, nt = cur.te - cur.tb;
+                cur.tb = tb + nt * part / P.n_split;
+                cur.te = tb + nt * (part + 1) / P.n_split;
+            }
+        }
+    }
     rsrc_t rk[NBS], rv;
     kv_of(cur.bh, rk, rv);
     // the next item (persistent grids only)
@@ -627,6 +651,72 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(Para
             }
         }
 
+        // ---- split tail: hand this key range's (O, m, l) over, or merge them all --------
+        // Every range stores its partial state (per wave and lane: O, m, l and the guard's
+        // shift) and counts itself in; the workgroup that counts in last reads all the
+        // partials and finishes the tile. Nobody waits. The partials are stored and read
+        // as device-scope atomics, which the hardware keeps coherent across the XCDs'
+        // L2 caches (a store completes at the device's coherence point: the wait for the
+        // stores before the barrier orders them before the count); a device-scope fence
+        // instead would write back and invalidate the whole L2, measured at 20-70 us.
+        if constexpr (TAIL) {
+            if (spl >= 0) {
+                constexpr int ROWF = NDB * 16 + 4;   // floats per lane: O, m, l, shift, pad
+                const int ns = P.n_split;
+                auto slot_of = [&](int q) __attribute__((always_inline)) {
+                    return P.part + ((long long)(spl * ns + q) * NW + wave) * (ROWF * 64) + lane;
+                };
+                auto put = [](float *p, float x) __attribute__((always_inline)) {
+                    __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                };
+                auto get = [](const float *p) __attribute__((always_inline)) {
+                    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                };
+                float *mine = slot_of(part);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) put(mine + (db * 16 + i) * 64, st.o[db][i]);
+                put(mine + (NDB * 16) * 64, st.m);
+                put(mine + (NDB * 16 + 1) * 64, st.l);
+                put(mine + (NDB * 16 + 2) * 64, __int_as_float(vshift));
+                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores are complete
+                __syncthreads();
+                if (tid == 0) guard[0] = __hip_atomic_fetch_add(P.cnt + spl, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __syncthreads();
+                if (guard[0] != (uint32_t)(ns - 1)) return;   // another range finishes the tile
+                if (tid == 0) __hip_atomic_store(P.cnt + spl, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // next call
+                // the common base M and the common guard shift of all ranges, then their sum in
+                // range order from the stored copies (the same operations whichever range
+                // merges, so the result does not depend on which one finished last)
+                float mx = NEG_INF;
+                int vs = 0;
+                for (int q = 0; q < ns; ++q) {
+                    const float *th = slot_of(q);
+                    mx = fmaxf(mx, get(th + (NDB * 16) * 64));
+                    vs = max(vs, __float_as_int(get(th + (NDB * 16 + 2) * 64)));
+                }
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) st.o[db] = f32x16{};
+                st.l = 0.0f;
+                for (int q = 0; q < ns; ++q) {
+                    const float *th = slot_of(q);
+                    const float mq = get(th + (NDB * 16) * 64);
+                    // a range with no valid key for this row has m = -inf and weight 0
+                    const float wq = mq == NEG_INF ? 0.0f : __builtin_amdgcn_exp2f(mq - mx);
+                    const float vq = wq * exp2i(__float_as_int(get(th + (NDB * 16 + 2) * 64)) - vs);
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i)
+                            st.o[db][i] = __builtin_fmaf(get(th + (db * 16 + i) * 64), vq, st.o[db][i]);
+                    st.l = __builtin_fmaf(get(th + (NDB * 16 + 1) * 64), wq, st.l);
+                }
+                st.m = mx;
+                vshift = vs;
+            }
+        }
+
         // ---- epilogue: normalise, subtract, cast, store rows < L -------------------------
         // (2^vshift undoes the guard's scaling of V; l >= 1, so inv * 2^vshift stays finite)
         const float inv = (1.0f / pair_sum(st.l)) * exp2i(vshift);
@@ -689,6 +779,29 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(Para
     }
 }
 
+// Query rows per workgroup of the 8-wave long-span instances.
+int full_tile_rows(const LaunchArgs &a) {
+    const int nw = a.D == 128 ? waves_for<128>() : waves_for<64>();
+    return a.diff ? nw * 16 : nw * 32;
+}
+
+// Key tiles the widest query tile of `bm` rows spans.
+long long key_span(const LaunchArgs &a, long long bm) {
+    const long long all = ((long long)a.L + BN - 1) / BN;
+    return a.window < 0 ? all : std::min(all, (2ll * a.window + bm + BN - 1) / BN + 1);
+}
+
+// Grids of more query tiles than compute units whose tiles span at most 32 key tiles:
+// contiguous calls run them persistent (see launch_contig). A shape property, so that
+// the workspace size (the split tail below) does not depend on the strides.
+bool persistent_shape(const LaunchArgs &a) {
+    if (use_narrow(a) || (a.prep && small_grid(a))) return false;
+    const long long bm = full_tile_rows(a);
+    const long long items = ((long long)a.L + bm - 1) / bm * a.B * a.H;
+    return items > (a.n_cu > 0 ? a.n_cu : 256) && key_span(a, bm) <= 32;
+}
+bool runs_persistent(const LaunchArgs &a) { return a.contig && persistent_shape(a); }
+
 template <int IO, bool DIFF, bool CONTIG, int D, bool PRE, bool PERS, int NW = waves_for<D>()>
 hipError_t launch(const LaunchArgs &a, int n_qtiles) {
     Params P = make_params(a);
@@ -700,6 +813,16 @@ hipError_t launch(const LaunchArgs &a, int n_qtiles) {
     const unsigned grid = (unsigned)(PERS ? std::min(P.n_items, ncu) : P.n_items);
     // an item's key span is >= min(L, rows + w) keys, and >= 129 keys cover >= 3 tiles
     P.cp = (a.L >= 129 && (a.window < 0 || a.window >= 128)) ? 1 : 0;
+    // the split tail runs its own instances, so that the others keep their code unchanged
+    if constexpr (!PERS && PRE && NW == waves_for<D>()) {
+        set_tail(P, a);
+        if (P.n_split > 0) {
+            hipLaunchKernelGGL((attn_fwd_kernel<IO, DIFF, CONTIG, D, PRE, PERS, NW, true>),
+                               dim3((unsigned)(P.n_full + P.n_tail * P.n_split)), dim3(NW * 64), 0,
+                               static_cast<hipStream_t>(a.stream), P);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((attn_fwd_kernel<IO, DIFF, CONTIG, D, PRE, PERS, NW>), dim3(grid), dim3(NW * 64), 0,
                        static_cast<hipStream_t>(a.stream), P);
     return hipGetLastError();
@@ -715,11 +838,7 @@ template <int IO, bool DIFF, int D, bool PRE>
 hipError_t launch_contig(const LaunchArgs &a, int n_qtiles) {
     if constexpr (PRE && !DIFF && D == 64)
         if (small_grid(a)) return launch<IO, false, true, 64, true, false, 2>(a, n_qtiles);
-    const long long items = (long long)n_qtiles * a.B * a.H;
-    const long long bm = tile_rows(a);   // query rows per tile
-    const long long all = ((long long)a.L + BN - 1) / BN;
-    const long long tiles = a.window < 0 ? all : std::min(all, (2ll * a.window + bm + BN - 1) / BN + 1);
-    if (items > (a.n_cu > 0 ? a.n_cu : 256) && tiles <= 32) return launch<IO, DIFF, true, D, PRE, true>(a, n_qtiles);
+    if (runs_persistent(a)) return launch<IO, DIFF, true, D, PRE, true>(a, n_qtiles);
     return launch<IO, DIFF, true, D, PRE, false>(a, n_qtiles);
 }
 
@@ -769,13 +888,46 @@ int tile_rows(const LaunchArgs &a) {
     return a.diff ? nw * 16 : nw * 32;
 }
 
+// The split tail. A one-round-per-tile grid (8-wave workgroups, one per compute unit)
+// whose last round holds r <= CUs / 2 query tiles would run that round with most CUs
+// idle: instead each of those r tiles is split into k = min(4, CUs / r) contiguous key
+// ranges (at least 4 key tiles each), one workgroup per range, and the workgroup that
+// finishes a tile's last range merges the ranges' partial (O, m, l) from the workspace
+// (O = sum of 2^(m_i - M) O_i, l likewise, M the largest base), so the last round takes
+// about 1/k of a tile's time. Grids of fewer tiles than half the CUs split all of them.
+// Not for the shapes of the persistent and small-grid instances, which have their own
+// balance (strided calls of a persistent shape run one round per tile without a split).
+TailPlan tail_plan(const LaunchArgs &a) {
+    const unsigned long long lp = ((unsigned long long)a.L + BN - 1) / BN * BN;
+    const unsigned long long kv = (unsigned long long)(a.diff ? 3 : 2) * (unsigned long long)a.B *
+                                  (unsigned long long)a.H * lp * (unsigned long long)a.D * 2ull;
+    TailPlan t{0, 0, 0, kv, kv, kv};
+    if (!a.tail_ok || use_narrow(a) || small_grid(a) || persistent_shape(a)) return t;
+    const long long bm = full_tile_rows(a);
+    const long long items = ((long long)a.L + bm - 1) / bm * a.B * a.H;
+    const long long ncu = a.n_cu > 0 ? a.n_cu : 256;
+    const long long rem = items % ncu;
+    if (rem == 0 || 2 * rem > ncu) return t;
+    const long long span = key_span(a, bm);
+    long long k = std::min(4ll, ncu / rem);
+    while (k > 1 && span < 4 * k) --k;
+    if (k < 2) return t;
+    t.n_full = (int)(items - rem);
+    t.k = (int)k;
+    t.n_tail = (int)rem;
+    // per range: 8 waves x 64 lanes x (O, m, l, shift, pad) floats
+    const unsigned long long rowf = (unsigned long long)a.D / 32 * 16 + 4;
+    t.cnt_off = kv + (unsigned long long)rem * k * 8ull * rowf * 64ull * 4ull;
+    t.end = t.cnt_off + ((unsigned long long)rem * 4ull + 255ull) / 256ull * 256ull;
+    return t;
+}
+
 // Workspace of the pre-pass: K' of each branch and V', Lp x D 16-bit values per (b, h)
-// each (0 for calls that take the single-span kernel).
+// each, then the split tail's partials and counters when it applies (0 for calls that
+// take the single-span kernel).
 unsigned long long prep_bytes(const LaunchArgs &a) {
     if (use_narrow(a)) return 0;
-    const unsigned long long lp = ((unsigned long long)a.L + BN - 1) / BN * BN;
-    return (unsigned long long)(a.diff ? 3 : 2) * (unsigned long long)a.B * (unsigned long long)a.H * lp *
-           (unsigned long long)a.D * 2ull;
+    return tail_plan(a).end;
 }
 
 // The fused staging rotates and transposes a key tile once per query tile that visits
@@ -791,6 +943,10 @@ unsigned long long prep_bytes(const LaunchArgs &a) {
 bool prep_pays(const LaunchArgs &a) {
     if (use_narrow(a)) return false;
     if (small_grid(a)) return true;
+    // the split tail needs the workspace, and a last round of at most half the CUs split
+    // into k ranges measured 10-49% faster than that round whole (even at 4 key tiles
+    // per range: B=1 H=2 L=1000 differential, 0.0305 -> 0.0226 ms)
+    if (tail_plan(a).k > 0) return true;
     const int bm = tile_rows(a);
     const long long n_qtiles = ((long long)a.L + bm - 1) / bm;
     const long long visits = a.window < 0 ? n_qtiles : std::min(n_qtiles, (2ll * a.window + BN + bm - 1) / bm + 1);

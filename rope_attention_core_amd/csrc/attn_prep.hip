@@ -39,6 +39,9 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(Params P) {
 
     const int tid = threadIdx.x;
     const int ntiles = P.ws_tiles;
+    // the split tail's counters (long-span kernel) start each call at zero
+    if (blockIdx.x == 0)
+        for (int i = tid; i < P.n_tail; i += NT) P.cnt[i] = 0u;
     const int bh = blockIdx.x / ntiles;
     const int t = blockIdx.x - bh * ntiles;
     const int bb = bh / P.H, hh = bh - bb * P.H;
@@ -119,6 +122,7 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(Params P) {
 template <int IO, bool DIFF, bool CONTIG, int D>
 hipError_t launch(const LaunchArgs &a) {
     Params P = make_params(a);
+    set_tail(P, a);   // its counters are cleared here
     const unsigned grid = (unsigned)P.ws_tiles * (unsigned)a.B * (unsigned)a.H;
     hipLaunchKernelGGL((attn_prep_kernel<IO, DIFF, CONTIG, D>), dim3(grid), dim3(256), 0,
                        static_cast<hipStream_t>(a.stream), P);

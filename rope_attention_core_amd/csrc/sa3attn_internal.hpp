@@ -35,6 +35,7 @@ struct LaunchArgs {
     int run_prep;           // with prep: enqueue the pre-pass (0: ws already holds its result)
     int run_main;           // enqueue the attention kernel (0: only the pre-pass)
     int n_cu;               // compute units of the current device (256 when there is none)
+    int tail_ok;            // with prep: the workspace may also hold the split tail's partials
     void *stream;           // hipStream_t
 };
 
@@ -50,6 +51,9 @@ int tile_rows(const LaunchArgs &a);
 bool split_applies(const LaunchArgs &a);
 int launch_split(const LaunchArgs &a, int n_qtiles);
 
+// Whether the single-span kernel takes the call (D = 64 only).
+bool use_narrow(const LaunchArgs &a);
+
 // Plain D = 64 calls whose grid of 256-row tiles has fewer workgroups than
 // compute units: with the pre-pass they run 64-row tiles of 2-wave workgroups.
 bool small_grid(const LaunchArgs &a);
@@ -61,6 +65,18 @@ bool small_grid(const LaunchArgs &a);
 // kernel (each key tile is rotated by every query tile that visits it) outweighs the
 // extra pass; launch_prep: enqueues it (a.ws set).
 unsigned long long prep_bytes(const LaunchArgs &a);
+
+// The split tail of the long-span kernel: a grid of one workgroup per query tile whose
+// last round would leave at least half the compute units idle splits each of its last
+// n_tail tiles into k key ranges (n_full whole tiles before them). k = 0: no split.
+// Applies with the pre-pass when a.tail_ok: its workspace holds, after K' and V', the
+// partial results (from byte part_off) and one counter per split tile (from cnt_off),
+// which the pre-pass clears.
+struct TailPlan {
+    int n_full, k, n_tail;
+    unsigned long long part_off, cnt_off, end;   // byte offsets in the workspace; end: its size
+};
+TailPlan tail_plan(const LaunchArgs &a);
 bool prep_pays(const LaunchArgs &a);
 int launch_prep(const LaunchArgs &a);
 

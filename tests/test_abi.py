@@ -304,11 +304,38 @@ def _lp(L):
     return (L + 63) // 64 * 64
 
 
+def _tail_bytes(B, H, L, D=64, differential=0, window=-1, n_cu=256):
+    """The split tail's share of the workspace, by the rule the header states: a grid of
+    one 8-wave workgroup per query tile (256 rows, 128 differential; not the persistent
+    grids of contiguous calls with more tiles than CUs and key spans <= 32 tiles, not
+    the small plain D = 64 grids) whose last round holds r <= CUs / 2 tiles splits them
+    in k = min(4, CUs // r) key ranges of >= 4 key tiles: r x k x 8 waves x 64 lanes x
+    (D / 32 x 16 + 4) floats, then r counters in 256-byte units."""
+    bm = 128 if differential else 256
+    items = (L + bm - 1) // bm * B * H
+    n_tiles = (L + 63) // 64
+    span = n_tiles if window < 0 or window >= L - 1 else min(n_tiles, (2 * window + bm + 63) // 64 + 1)
+    if items > n_cu and span <= 32:
+        return 0                                   # persistent grid
+    if D == 64 and not differential and (L + 255) // 256 * B * H < n_cu and (L + 63) // 64 * B * H <= 2 * n_cu:
+        return 0                                   # small grid
+    r = items % n_cu
+    if r == 0 or 2 * r > n_cu:
+        return 0
+    k = min(4, n_cu // r)
+    while k > 1 and span < 4 * k:
+        k -= 1
+    if k < 2:
+        return 0
+    return r * k * 8 * 64 * (D // 32 * 16 + 4) * 4 + (r * 4 + 255) // 256 * 256
+
+
 @pytest.mark.parametrize("kw,policy,want", [
     # AUTO: more workgroups than the 256 compute units assumed without a device, and at
     # least 12 query tiles of 256 rows (plain) / 9 of 128 (differential) per key tile
     (dict(B=2, H=24, L=4096), AUTO, 2 * 2 * 24 * 4096 * 64 * 2),
-    (dict(B=1, H=24, L=2816), AUTO, 0),                                  # 11 visits
+    (dict(B=1, H=24, L=2816), AUTO, 2 * 24 * _lp(2816) * 64 * 2),        # 11 visits, but 264 WGs: split tail
+    (dict(B=1, H=20, L=2816), AUTO, 0),                                  # 11 visits, 220 WGs
     (dict(B=1, H=24, L=2817), AUTO, 2 * 24 * _lp(2817) * 64 * 2),        # 12 visits, 288 WGs
     # plain D = 64 grids of fewer 256-row workgroups than compute units run 64-row tiles
     # with the pre-pass
@@ -325,7 +352,8 @@ def _lp(L):
     (dict(B=1, H=16, L=2048, differential=1), AUTO, 0),                  # 16 visits, 256 WGs
     (dict(B=1, H=16, L=2049, differential=1), AUTO, 3 * 16 * _lp(2049) * 64 * 2),   # 17, 272 WGs
     # D = 128: the same 256 / 128 rows per query tile
-    (dict(B=1, H=24, L=2816, D=128), AUTO, 0),
+    (dict(B=1, H=24, L=2816, D=128), AUTO, 2 * 24 * _lp(2816) * 128 * 2),   # split tail
+    (dict(B=1, H=20, L=2816, D=128), AUTO, 0),
     (dict(B=1, H=24, L=2817, D=128), AUTO, 2 * 24 * _lp(2817) * 128 * 2),
     (dict(B=1, H=32, L=1024, D=128, differential=1), AUTO, 0),
     (dict(B=1, H=32, L=1025, D=128, differential=1), AUTO, 3 * 32 * _lp(1025) * 128 * 2),
@@ -350,6 +378,8 @@ def _lp(L):
     (dict(B=1, H=2, L=200), ONLY, 0),
 ])
 def test_workspace_bytes(lib, kw, policy, want):
+    if want:
+        want += _tail_bytes(**kw)
     assert _ws_bytes(lib, policy, **kw) == (SA3_OK, want)
     B, H, L, D = kw["B"], kw["H"], kw["L"], kw.get("D", 64)
     prep = {AUTO: "auto", ALWAYS: "always", NEVER: "never", ONLY: "only", REUSE: "reuse"}[policy]
@@ -404,7 +434,8 @@ def test_valid_ws_calls_without_gpu_report_device_error(lib):
     assert _call_ws(lib, ws, need + 4096) == SA3_ERR_DEVICE
     # no workspace needed: NEVER, AUTO below the threshold, the single-span kernel
     assert _call_ws(lib, None, 0, policy=NEVER) == SA3_ERR_DEVICE
-    assert _call_ws(lib, None, 0, policy=AUTO, differential=1) == SA3_ERR_DEVICE
+    assert _call_ws(lib, None, 0, policy=AUTO, differential=1) == SA3_ERR_NULL   # split tail: the pre-pass runs
+    assert _call_ws(lib, None, 0, policy=AUTO, differential=1, window=100) == SA3_ERR_DEVICE
     assert _call_ws(lib, None, 0, policy=AUTO) == SA3_ERR_NULL      # a small grid: the pre-pass runs
     assert _call_ws(lib, None, 0, policy=ALWAYS, window=17) == SA3_ERR_DEVICE
     assert _call_ws(lib, None, 0, policy=ALWAYS, L=200) == SA3_ERR_DEVICE
@@ -413,7 +444,8 @@ def test_valid_ws_calls_without_gpu_report_device_error(lib):
     assert _call_ws(lib, None, 0, policy=ONLY, window=17) == SA3_ERR_DEVICE
     # the workspace right after out is no overlap
     assert _call_ws(lib, ws, need, out=ctypes.c_void_p(ws.value - 2 * 1000 * 64 * 2)) == SA3_ERR_DEVICE
-    assert _call_ws(lib, ws, 3 * 2 * _lp(1000) * 64 * 2, differential=1, st=_strides(layout="blhd"),
+    assert _call_ws(lib, ws, 3 * 2 * _lp(1000) * 64 * 2 + _tail_bytes(1, 2, 1000, differential=1), differential=1,
+                    st=_strides(layout="blhd"),
                     rope=_rope(1, 32)) == SA3_ERR_DEVICE
 
 

@@ -54,19 +54,21 @@ def test_blhd_inputs(name, kw, strided_out):
     inp = synth.make_inputs(cfg)
     q, k, v = (G.to_device(inp[n], cfg.io) for n in ("q", "k", "v"))
     G.note(f"  strided: {cfg.name} {kw} out strided={strided_out}")
-    # the contiguous call without the pre-pass: on small plain full-attention grids the
-    # pre-pass would send it to the key-split kernel, which views never take
-    base = _run(cfg, inp, q, k, v, prep="never")
     qs, ks, vs = _blhd_view(q), _blhd_view(k), _blhd_view(v)
     assert not qs.is_contiguous() and qs.stride(-1) == 1
-    out = None
-    if strided_out:
-        B, H, L, D = v.shape
-        out = torch.empty((B, L, H, D), dtype=G.out_torch_dtype(cfg.out_dtype), device="cuda").transpose(1, 2)
-    got = _run(cfg, inp, qs, ks, vs, out=out)
-    assert torch.equal(got.contiguous(), base), "strided call differs from the contiguous one"
-    G.assert_parity(got.float().cpu().numpy().astype(np.float64), G.run_oracle(cfg, inp),
-                    what=f"{name} {kw} blhd", out=cfg.out_dtype)
+    # the fused path, and the pre-pass path for the differential cases (on small plain
+    # full-attention grids the pre-pass would send the contiguous call to the key-split
+    # kernel, which views never take)
+    for prep in ("never", "always") if cfg.diff else ("never",):
+        base = _run(cfg, inp, q, k, v, prep=prep)
+        out = None
+        if strided_out:
+            B, H, L, D = v.shape
+            out = torch.empty((B, L, H, D), dtype=G.out_torch_dtype(cfg.out_dtype), device="cuda").transpose(1, 2)
+        got = _run(cfg, inp, qs, ks, vs, out=out, prep=prep)
+        assert torch.equal(got.contiguous(), base), f"strided call differs from the contiguous one (prep {prep})"
+        G.assert_parity(got.float().cpu().numpy().astype(np.float64), G.run_oracle(cfg, inp),
+                        what=f"{name} {kw} blhd prep {prep}", out=cfg.out_dtype)
 
 
 def test_heads_of_a_wider_buffer():

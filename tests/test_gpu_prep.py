@@ -72,6 +72,27 @@ def _takes_split_kernel(cfg, strided, opt):
             and (cfg.L + 255) // 256 * bh < 256 and (cfg.L + 63) // 64 * bh <= 512)
 
 
+def _oracle_opt(cfg, inp, opt):
+    """The oracle with a RoPE option (pairing, rotary width)."""
+    pairing, rd = opt
+    q, k, v = G.widen(inp, cfg)
+    c32, s32 = oracle.rope_table_f32(cfg.L, rd, cfg.base)
+    kw = dict(pairing=pairing, rotary_dim=rd)
+    if cfg.diff:
+        return oracle.attn_method(q[0], k[0], v, c32, s32, cfg.io, cfg.scale, window=cfg.window, lam=cfg.lam,
+                                  q2=q[1], k2=k[1], **kw)
+    return oracle.attn_method(q, k, v, c32, s32, cfg.io, cfg.scale, window=cfg.window, **kw)
+
+
+def _takes_tail(cfg):
+    """Whether the call's grid splits its last round (the split tail), which the library
+    reports as workspace beyond K' and V': its ranges are merged in another order than
+    the fused path's single pass, so the last bits differ (both held to the oracle)."""
+    kv = (3 if cfg.diff else 2) * cfg.B * cfg.H * ((cfg.L + 63) // 64 * 64) * cfg.D * 2
+    return G.sa3.workspace_bytes(cfg.B, cfg.H, cfg.L, cfg.D, window=cfg.window, differential=cfg.diff,
+                                 prep="always") > kv
+
+
 @pytest.mark.parametrize("name,kw,strided,opt", CASES)
 def test_prep_path_equals_fused_path(name, kw, strided, opt):
     torch = G.torch_mod()
@@ -81,10 +102,10 @@ def test_prep_path_equals_fused_path(name, kw, strided, opt):
     fused = _call(cfg, q, k, v, prep="never", **_rope_kw(opt))
     pre = _call(cfg, q, k, v, prep="always", **_rope_kw(opt))
     torch.cuda.synchronize()
-    if _takes_split_kernel(cfg, strided, opt):
+    if _takes_split_kernel(cfg, strided, opt) or _takes_tail(cfg):
         # same arithmetic per element, row sums in another order: both against the oracle
-        want = G.run_oracle(cfg, inp)
-        for what, got in (("key-split", pre), ("fused", fused)):
+        want = G.run_oracle(cfg, inp) if opt is None else _oracle_opt(cfg, inp, opt)
+        for what, got in (("key-split or split tail", pre), ("fused", fused)):
             G.assert_parity(got.float().cpu().numpy().astype(np.float64), want, what=f"{name} {kw} {what}",
                             out=cfg.out_dtype)
         return
@@ -112,7 +133,8 @@ def test_auto_policy_at_full_size(name):
     fused = _call(cfg, q, k, v, prep="never")
     auto = _call(cfg, q, k, v, prep="auto")
     torch.cuda.synchronize()
-    assert torch.equal(auto, fused)
+    if not _takes_tail(cfg):
+        assert torch.equal(auto, fused)
     rows = np.array([0, 1, 777, cfg.L - 1])
     want = G.run_oracle_rows(cfg, inp, cfg.B - 1, cfg.H - 1, rows)
     G.assert_parity(auto[cfg.B - 1, cfg.H - 1, rows].float().cpu().numpy().astype(np.float64), want,
@@ -155,7 +177,7 @@ def test_prep_path_in_a_graph():
     torch = G.torch_mod()
     cfg = synth.config("samel_swa", H=2, L=1000, window=-1, seed=9873)
     _, q, k, v = _inputs(cfg)
-    eager = _call(cfg, q, k, v, prep="never")
+    eager = _call(cfg, q, k, v, prep="always")
     nb = G.sa3.workspace_bytes(cfg.B, cfg.H, cfg.L, cfg.D, differential=True, dtype=G.sa3.BF16, prep="always")
     ws = torch.empty((nb,), dtype=torch.uint8, device="cuda")
     out = torch.empty_like(eager)
@@ -195,7 +217,7 @@ def test_prepare_once_then_reuse_for_several_queries():
     torch.cuda.synchronize()
     assert bool((out == 7.0).all()), "the pre-pass alone wrote out"
     for qq in (q, q2):
-        want = _call(cfg, qq, k, v, prep="never")
+        want = _call(cfg, qq, k, v, prep="always")
         got = _call(cfg, qq, k, v, prep="reuse", workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(got, want)

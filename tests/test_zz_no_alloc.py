@@ -93,7 +93,7 @@ def test_noalloc_only_then_reuse():
     lib = G.sa3.load_library()
     cfg = synth.config("samel_swa", H=2, L=1200, window=-1, seed=78)
     _, t, (o_ref, o_na) = _setup(cfg)
-    assert _na_call(lib, cfg, t, o_ref, NEVER) == 0
+    assert _na_call(lib, cfg, t, o_ref, ALWAYS) == 0
     o_na.fill_(7.0)
     assert _na_call(lib, cfg, t, o_na, ONLY) == 0
     torch.cuda.synchronize()
@@ -101,6 +101,32 @@ def test_noalloc_only_then_reuse():
     assert _na_call(lib, cfg, t, o_na, REUSE) == 0
     torch.cuda.synchronize()
     assert torch.equal(o_na, o_ref)
+
+
+def test_noalloc_split_tail():
+    """A grid whose last round is split: with room in the static array for the partials
+    (B1 H24 L3000: 27 MiB) the no-alloc call splits it as the workspace call does (the
+    same bits); the long latent at D = 128 (82 MiB with the partials, 48 MiB without)
+    runs the pre-pass without the split, bitwise as the fused path."""
+    torch = G.torch_mod()
+    lib = G.sa3.load_library()
+    cfg = synth.config("dit_long", B=1, H=24, L=3000, seed=80)
+    inp, t, (o_ws, o_na) = _setup(cfg)
+    nb = G.sa3.workspace_bytes(cfg.B, cfg.H, cfg.L, cfg.D, dtype=G.sa3.BF16, prep="always")
+    assert nb <= G.sa3.SCRATCH_BYTES
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    assert _ws_call(lib, cfg, t, o_ws, ALWAYS, ws) == 0
+    assert _na_call(lib, cfg, t, o_na, ALWAYS) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(o_na, o_ws)
+    big = synth.config("dit_long_d128")
+    nb = G.sa3.workspace_bytes(big.B, big.H, big.L, big.D, dtype=G.sa3.BF16, prep="always")
+    assert nb > G.sa3.SCRATCH_BYTES
+    _, t, (o_a, o_b) = _setup(big)
+    assert _na_call(lib, big, t, o_a, ALWAYS) == 0
+    assert _na_call(lib, big, t, o_b, NEVER) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_b)
 
 
 def test_noalloc_size_limit():
