@@ -190,8 +190,11 @@ int sa3attn_forward_general(const sa3attn_desc *desc, const sa3attn_strides *str
  * that visits the key: 16 to 32 times per key at L = 4096. With a workspace the
  * library first runs a pre-pass kernel that rotates K (each branch) and converts and
  * transposes V once, into the workspace, and the attention kernel then copies its
- * key tiles from there. Outputs are bitwise identical to sa3attn_forward_general's,
- *     except on the two kinds of grid below, where the sums over a row's keys are taken
+ * key tiles from there. Outputs are bitwise identical to sa3attn_forward_general's for
+ *     differential calls, persistent grids and D = 128 without a split tail; plain D = 64
+ *     calls of one round per query tile walk the keys 128 at a time with the pre-pass
+ *     (one softmax base move per 128 keys instead of 64), and the two kinds of grid
+ *     below take the keys in other groups: there the sums over a row's keys are taken
  *     in another order (the same bar against the exact result, other last bits; calls
  *     of the same shape and policy give the same bits run to run).
  *   Small grids: plain calls (not differential) at D = 64 outside the single-span

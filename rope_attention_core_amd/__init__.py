@@ -243,12 +243,14 @@ def forward(q, k, v, cos, sin, *, window=-1, lam=0.0, scale=None, out=None, out_
     `stream` when one is given, else on the current stream) when not given and the
     pre-pass runs; a caller's workspace used on several streams is the caller's to
     order; "only" and "reuse" need the caller's workspace (ValueError without one).
-    All policies give bitwise identical outputs, except plain full attention on
-    contiguous tensors with the default RoPE on those small grids (with the pre-pass a
-    key-split kernel runs them, summing each row's keys in two halves) and grids whose
-    last round of query tiles fills at most half the compute units (with the pre-pass
-    each of those tiles is split into key ranges merged at the end; "auto" runs the
-    pre-pass there): other last bits, the same error bar.
+    With and without the pre-pass, outputs are bitwise identical for differential
+    calls, persistent grids and D = 128 without a split tail. Elsewhere the pre-pass
+    path sums a row's keys in another order (other last bits, the same error bar):
+    plain D = 64 grids of one round per query tile walk the keys 128 at a time; plain
+    full attention on contiguous tensors on those small grids runs a key-split kernel
+    (each row's keys in two halves); grids whose last round of query tiles fills at
+    most half the compute units split those tiles into key ranges merged at the end
+    ("auto" runs the pre-pass there).
 
     pairing: "adjacent" (default) or "half" (pairs x[i], x[i + R/2]); rotary_dim: R,
     the leading dims rotated (default D; a multiple of 16), cos/sin then [>=L, R/2].

@@ -28,6 +28,9 @@
 //    fp16.
 //  * K is rotated (FP32, fixed operation order, no contraction) and rounded to the IO
 //    dtype while it is staged into LDS; Q once into registers.
+//  * Plain D = 64 instances of one round per query tile on the pre-pass workspace walk
+//    the keys in pairs of tiles (128 keys per step: one maximum, base move, O rescale
+//    and barrier per pair; see pair_block). The others:
 //  * Software pipeline over key tiles with three LDS buffers and one barrier per tile.
 //    The block for tile t first issues QK^T(t+1) into the second score set, so those
 //    MFMAs run under the softmax of tile t (VALU); P.V(t) follows each 32-key half of
@@ -117,7 +120,11 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(Para
     constexpr bool CP = PERS && !(DIFF && D == 128);
     constexpr int XB_ELEMS = (CP && DIFF) ? WPB * 32 * D * 2 : 0;
     static_assert(!DIFF || CP || NBUF * BUF_ELEMS * 2 >= WPB * 32 * D * 4, "LDS too small for the O2 exchange");
-    __shared__ __attribute__((aligned(16))) uint16_t smem[NBUF * BUF_ELEMS + XB_ELEMS];
+    // PAIR: plain D = 64 one-round instances with the pre-pass walk the keys 128 at a time
+    // (see pair_block below), with six tile slots in LDS instead of NBUF
+    constexpr bool PAIR = PRE && !DIFF && D == 64 && !PERS && NW == waves_for<D>();
+    constexpr int NSLOT = PAIR ? 6 : NBUF;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[NSLOT * BUF_ELEMS + XB_ELEMS];
     __shared__ uint32_t guard[2 * NW];       // words of the V range guard's reductions
 
     const float NEG_INF = -__builtin_inff();
@@ -407,10 +414,10 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(Para
     Branch<NDB> st;
 
     // mask of tile t for this wave's rows (lane-level lo/span)
-    auto tile_mask = [&](int t) __attribute__((always_inline)) {
+    auto tile_mask = [&](int t, int kend) __attribute__((always_inline)) {
         const int k0 = t * BN;
         const int qi = qw + r;
-        int lo = 0, hi = L - 1;
+        int lo = 0, hi = kend - 1;
         if (window >= 0 && qi < L) {
             lo = max(lo, qi - window);
             hi = min(hi, qi + window);
@@ -428,9 +435,9 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(Para
         return mk;
     };
     // the wave-uniform decision whether tile t needs element masks
-    auto tile_needs_mask = [&](int t) __attribute__((always_inline)) {
+    auto tile_needs_mask = [&](int t, int kend) __attribute__((always_inline)) {
         const int k0 = t * BN;
-        if (k0 + BN > L) return true;
+        if (k0 + BN > kend) return true;
         if (window < 0 || qw > qhi_live) return false;
         return k0 < qhi_live - window || k0 + BN - 1 > qw + window;
     };
@@ -525,7 +532,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(Para
             __syncthreads();
             return;
         }
-        const TileMask mk = MASK ? tile_mask(t) : TileMask{0, 0};
+        const TileMask mk = MASK ? tile_mask(t, L) : TileMask{0, 0};
         const float mt = tile_max<MASK>(sb[PC], c, mk);
         const float mn = (mt > st.m + TAU) ? mt : st.m;
         // branch-free: exp2(-inf) = 0 covers a row that had no valid key yet (the select
@@ -562,11 +569,111 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(Para
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
     auto step = [&](int t, auto par_tag, auto safe_tag) __attribute__((always_inline)) {
-        if (tile_needs_mask(t))
+        if (tile_needs_mask(t, L))
             block(t, std::true_type{}, par_tag, safe_tag);
         else
             block(t, std::false_type{}, par_tag, safe_tag);
     };
+    // ---- 128-key steps (PAIR) -------------------------------------------------------
+    // The keys go in pairs of 64-key tiles (t, t+1): one maximum over the 128 scores, one
+    // move of the base and one rescale of O per pair, and one barrier, instead of one per
+    // tile. The scores of a pair (four 32-key quarters) are computed during the previous
+    // pair: each quarter's QK^T of the next pair is issued into the registers the
+    // quarter's softmax has just freed, so its MFMAs run under the remaining softmax
+    // work. Tile u sits in LDS slot (u - tb) mod 6: the pair block of t reads V of t, t+1
+    // and K of t+2, t+3, and stages t+4, t+5 (their slots were last read by the pair
+    // block of t-2, closed by its barrier) from registers loaded during that block, then
+    // loads t+6, t+7. An item of an odd number of tiles ends with one tile past its range,
+    // masked as keys past the item's end (kend), so that it adds nothing.
+    f32x16 sp[4];                             // scores of the current pair [tile][kb]
+    u32x4 pk[2][KC], pv[2][VC];               // K' / V' chunks of two tiles in flight
+    auto pslot = [&](int t) __attribute__((always_inline)) { return (t - cur.tb) % NSLOT; };
+    auto pload = [&](int t, int j) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < KC; ++i) pk[j][i] = bload(rk[0], kl + (uint32_t)(t * BN + i * (NT / CPR)) * RB);
+#pragma unroll
+        for (int i = 0; i < VC; ++i) pv[j][i] = bload(rv, (uint32_t)t * (D * BN * 2) + (uint32_t)(tid + i * NT) * 16);
+    };
+    auto pstage = [&](int buf, int j) __attribute__((always_inline)) {
+        uint16_t *Ks = smem + buf * BUF_ELEMS;
+        uint16_t *Vt = Ks + KS_ELEMS;
+#pragma unroll
+        for (int i = 0; i < KC; ++i) *reinterpret_cast<u32x4 *>(Ks + kat + i * (NT / CPR) * KSTR) = pk[j][i];
+#pragma unroll
+        for (int i = 0; i < VC; ++i) {
+            const int cv = tid + i * NT;
+            *reinterpret_cast<u32x4 *>(Vt + (cv >> 3) * VT_STRIDE + (cv & 7) * 8) = pv[j][i];
+        }
+    };
+    // S^T of one 32-key quarter (kb) of the tile in slot buf
+    auto qk_quarter = [&](int buf, int kb, f32x16 &s) __attribute__((always_inline)) {
+        const uint16_t *Ks = smem + buf * BUF_ELEMS;
+        u32x4 ka[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) ka[ks] = lds16(Ks + (kb * 32 + r) * KSTR + 16 * ks + 8 * g);
+        f32x16 acc = {};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) acc = mfma_qk<IO>(ka[ks], qreg[ks], acc);
+        s = acc;
+    };
+    auto pair_block = [&](int t, int kend, bool mask) __attribute__((always_inline)) {
+        pstage(pslot(t + 4), 0);
+        pstage(pslot(t + 5), 1);
+        pload(t + 6, 0);
+        pload(t + 7, 1);
+        // scores of keys past the item's end or outside the window set to -inf, in place
+        // (a branch around this part only: the rest of the block is one copy of code)
+        if (mask) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const TileMask mk = tile_mask(t + j, kend);
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int o = kb * 32 + (i >> 2) * 8 + (i & 3);
+                        sp[2 * j + kb][i] = ((uint32_t)(o - mk.lo) <= mk.span) ? sp[2 * j + kb][i] : NEG_INF;
+                    }
+            }
+        }
+        // maximum of c * s over the pair's valid keys
+        float v[2][32];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) v[j][kb * 16 + i] = sp[2 * j + kb][i];
+        const float mr = pair_max(fmaxf(max32(v[0]), max32(v[1])));
+        const float mt = (mr == NEG_INF) ? NEG_INF : mr * c;
+        const float mn = (mt > st.m + TAU) ? mt : st.m;
+        const float ea = __builtin_amdgcn_exp2f(st.m - mn);
+        const float a = (mn == st.m) ? 1.0f : ea;
+        st.m = mn;
+        const float nb = (mn == NEG_INF) ? 0.0f : -mn;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) st.o[db][i] *= a;
+        float part[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int kb = q & 1;
+            u32x4 p[2];
+            softmax_half<false>(sp[q], kb, c, nb, TileMask{0, 0}, p, part[q]);   // masked above
+            qk_quarter(pslot(t + 2 + (q >> 1)), kb, sp[q]);   // next pair: computed, unused past the item
+            const uint16_t *Vt = smem + pslot(t + (q >> 1)) * BUF_ELEMS + KS_ELEMS;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    st.o[db] = mfma_pv(lds16(Vt + (db * 32 + r) * VT_STRIDE + kb * 32 + 16 * tt + 8 * g), p[tt],
+                                       st.o[db]);
+        }
+        st.l = __builtin_fmaf(st.l, a, (part[0] + part[1]) + (part[2] + part[3]));
+        __syncthreads();
+    };
+
     // One pass over the current item: Q rotated into registers (MFMA B-operand layout),
     // O, l, m reset, the prologue when the item starts cold, then the key tiles.
     auto run_item = [&](auto safe_tag, bool cold, bool wait) __attribute__((always_inline)) {
@@ -598,6 +705,29 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(Para
         st.m = NEG_INF;
         st.a = 1.0f;
 
+        if constexpr (PAIR && !SAFE) {
+            // (one item per workgroup: always cold)
+            if (wait) __syncthreads();
+            pload(cur.tb, 0);
+            pload(cur.tb + 1, 1);
+            pstage(pslot(cur.tb), 0);
+            pstage(pslot(cur.tb + 1), 1);
+            pload(cur.tb + 2, 0);
+            pload(cur.tb + 3, 1);
+            pstage(pslot(cur.tb + 2), 0);
+            pstage(pslot(cur.tb + 3), 1);
+            pload(cur.tb + 4, 0);
+            pload(cur.tb + 5, 1);
+            __syncthreads();
+            qk_quarter(pslot(cur.tb), 0, sp[0]);
+            qk_quarter(pslot(cur.tb), 1, sp[1]);
+            qk_quarter(pslot(cur.tb + 1), 0, sp[2]);
+            qk_quarter(pslot(cur.tb + 1), 1, sp[3]);
+            const int kend = min(L, cur.te * BN);
+            for (int t = cur.tb; t < cur.te; t += 2)
+                pair_block(t, kend, tile_needs_mask(t, kend) || tile_needs_mask(t + 1, kend));
+            return;
+        }
         // ---- prologue: the first item, and every item without CP ------------------
         if (cold) {
             if (wait) __syncthreads();   // every wave is done with the LDS stages

@@ -1,11 +1,12 @@
 """GPU checks of the pre-pass path (sa3attn_forward_ws through the binding).
 
 The pre-pass rotates K and converts / transposes V once into a workspace; the
-long-span kernel then copies its key tiles from there. The arithmetic is the same, so
-every case must give the same bits as the fused path (prep="never"), except plain full
-attention on under-filled grids, which the key-split kernel takes with the pre-pass
-(both paths are then compared with the oracle), and the result is also compared with
-the oracle element by element on a subset. Cases cover plain and
+long-span kernel then copies its key tiles from there. The arithmetic per element is
+the same, so the cases here give the same bits as the fused path (prep="never"),
+except plain full attention on under-filled grids (the key-split kernel), grids whose
+last round is split, and plain D = 64 one-round grids (128-key steps), whose sums run
+in another order: both paths are then compared with the oracle. Results are also
+compared with the oracle element by element on a subset. Cases cover plain and
 differential attention, full and wide windows, both IO dtypes, ragged lengths (the
 workspace's tail rows), strided views, the RoPE options, head dim 128, a workspace
 full of NaN bits on entry, reuse of one workspace by calls of different shapes, graph
@@ -133,8 +134,14 @@ def test_auto_policy_at_full_size(name):
     fused = _call(cfg, q, k, v, prep="never")
     auto = _call(cfg, q, k, v, prep="auto")
     torch.cuda.synchronize()
-    if not _takes_tail(cfg):
+    # plain D = 64 one-round grids walk the keys 128 at a time with the pre-pass, and the
+    # long latent at D = 128 splits its last round: both sum in another order
+    if cfg.diff:
         assert torch.equal(auto, fused)
+    else:
+        d = (auto.float() - fused.float()).abs().max().item()
+        G.note(f"  {name}: auto vs fused max-abs difference {d:.3e}")
+        assert d <= 2 * G.ATOL
     rows = np.array([0, 1, 777, cfg.L - 1])
     want = G.run_oracle_rows(cfg, inp, cfg.B - 1, cfg.H - 1, rows)
     G.assert_parity(auto[cfg.B - 1, cfg.H - 1, rows].float().cpu().numpy().astype(np.float64), want,
