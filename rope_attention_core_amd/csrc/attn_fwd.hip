@@ -120,11 +120,13 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(Para
     constexpr bool CP = PERS && !(DIFF && D == 128);
     constexpr int XB_ELEMS = (CP && DIFF) ? WPB * 32 * D * 2 : 0;
     static_assert(!DIFF || CP || NBUF * BUF_ELEMS * 2 >= WPB * 32 * D * 4, "LDS too small for the O2 exchange");
-    // PAIR: plain D = 64 one-round instances with the pre-pass walk the keys 128 at a time
-    // (see pair_block below), with six tile slots in LDS instead of NBUF
-    constexpr bool PAIR = PRE && !DIFF && D == 64 && !PERS && NW == waves_for<D>();
-    constexpr int NSLOT = PAIR ? 6 : NBUF;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[NSLOT * BUF_ELEMS + XB_ELEMS];
+    // PAIR: D = 64 one-round instances with the pre-pass walk the keys 128 at a time (see
+    // pair_block below), with rings of PR K tiles (each branch) and PR V^T tiles in LDS
+    constexpr bool PAIR = PRE && D == 64 && !PERS && NW == waves_for<D>();
+    constexpr int PR = 4;
+    constexpr int PAIR_ELEMS = PR * NBS * KS_ELEMS + PR * VT_ELEMS;
+    constexpr int STAGE_ELEMS = (PAIR && PAIR_ELEMS > NBUF * BUF_ELEMS) ? PAIR_ELEMS : NBUF * BUF_ELEMS;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[STAGE_ELEMS + XB_ELEMS];
     __shared__ uint32_t guard[2 * NW];       // words of the V range guard's reductions
 
     const float NEG_INF = -__builtin_inff();
@@ -575,39 +577,56 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(Para
             block(t, std::false_type{}, par_tag, safe_tag);
     };
     // ---- 128-key steps (PAIR) -------------------------------------------------------
-    // The keys go in pairs of 64-key tiles (t, t+1): one maximum over the 128 scores, one
-    // move of the base and one rescale of O per pair, and one barrier, instead of one per
-    // tile. The scores of a pair (four 32-key quarters) are computed during the previous
-    // pair: each quarter's QK^T of the next pair is issued into the registers the
-    // quarter's softmax has just freed, so its MFMAs run under the remaining softmax
-    // work. Tile u sits in LDS slot (u - tb) mod 6: the pair block of t reads V of t, t+1
-    // and K of t+2, t+3, and stages t+4, t+5 (their slots were last read by the pair
-    // block of t-2, closed by its barrier) from registers loaded during that block, then
-    // loads t+6, t+7. An item of an odd number of tiles ends with one tile past its range,
-    // masked as keys past the item's end (kend), so that it adds nothing.
+    // The keys go in pairs of 64-key tiles (t, t+1), with one barrier per pair instead of
+    // one per tile. The scores of a pair (four 32-key quarters) are computed during the
+    // previous pair: each quarter's QK^T of the next pair is issued into the registers the
+    // quarter's softmax has just freed, so its MFMAs run under the remaining softmax work.
+    // Plain calls take one maximum over the pair's 128 scores, one move of the base and
+    // one rescale of O per pair. Differential calls (FAST) compute each quarter's P
+    // against the current base and redo a quarter with its exact maximum only when some P
+    // overflowed, as the 64-key blocks do. K tile u sits in K-ring slot (u - tb) mod 4 and
+    // V^T tile u in V-ring slot (u - tb) mod 4: the pair block of t reads K of t+2, t+3
+    // and V of t, t+1, stages K of t+4, t+5 and V of t+2, t+3 (slots last read by the pair
+    // block of t-2, closed by its barrier) from registers loaded during that block, and
+    // loads K of t+6, t+7 and V of t+4, t+5. An item of an odd number of tiles ends with
+    // one tile past its range, masked as keys past the item's end (kend).
     f32x16 sp[4];                             // scores of the current pair [tile][kb]
-    u32x4 pk[2][KC], pv[2][VC];               // K' / V' chunks of two tiles in flight
-    auto pslot = [&](int t) __attribute__((always_inline)) { return (t - cur.tb) % NSLOT; };
-    auto pload = [&](int t, int j) __attribute__((always_inline)) {
+    u32x4 pk[2][NBS][KC], pv[2][VC];          // K' (each branch) / V' chunks of two tiles
+    auto kring = [&](int t) __attribute__((always_inline)) {
+        return smem + ((t - cur.tb) & (PR - 1)) * (NBS * KS_ELEMS);
+    };
+    auto vring = [&](int t) __attribute__((always_inline)) {
+        return smem + PR * NBS * KS_ELEMS + ((t - cur.tb) & (PR - 1)) * VT_ELEMS;
+    };
+    auto pload_k = [&](int t, int j) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < KC; ++i) pk[j][i] = bload(rk[0], kl + (uint32_t)(t * BN + i * (NT / CPR)) * RB);
+        for (int i = 0; i < KC; ++i)
+#pragma unroll
+            for (int br = 0; br < NBS; ++br) pk[j][br][i] = bload(rk[br], kl + (uint32_t)(t * BN + i * (NT / CPR)) * RB);
+    };
+    auto pload_v = [&](int t, int j) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < VC; ++i) pv[j][i] = bload(rv, (uint32_t)t * (D * BN * 2) + (uint32_t)(tid + i * NT) * 16);
     };
-    auto pstage = [&](int buf, int j) __attribute__((always_inline)) {
-        uint16_t *Ks = smem + buf * BUF_ELEMS;
-        uint16_t *Vt = Ks + KS_ELEMS;
+    auto pstage_k = [&](int t, int j) __attribute__((always_inline)) {
+        uint16_t *Ks = kring(t);
 #pragma unroll
-        for (int i = 0; i < KC; ++i) *reinterpret_cast<u32x4 *>(Ks + kat + i * (NT / CPR) * KSTR) = pk[j][i];
+        for (int i = 0; i < KC; ++i)
+#pragma unroll
+            for (int br = 0; br < NBS; ++br)
+                *reinterpret_cast<u32x4 *>(Ks + br * KS_ELEMS + kat + i * (NT / CPR) * KSTR) = pk[j][br][i];
+    };
+    auto pstage_v = [&](int t, int j) __attribute__((always_inline)) {
+        uint16_t *Vt = vring(t);
 #pragma unroll
         for (int i = 0; i < VC; ++i) {
             const int cv = tid + i * NT;
             *reinterpret_cast<u32x4 *>(Vt + (cv >> 3) * VT_STRIDE + (cv & 7) * 8) = pv[j][i];
         }
     };
-    // S^T of one 32-key quarter (kb) of the tile in slot buf
-    auto qk_quarter = [&](int buf, int kb, f32x16 &s) __attribute__((always_inline)) {
-        const uint16_t *Ks = smem + buf * BUF_ELEMS;
+    // S^T of one 32-key quarter (kb) of K tile t of this wave's branch
+    auto qk_quarter = [&](int t, int kb, f32x16 &s) __attribute__((always_inline)) {
+        const uint16_t *Ks = kring(t) + wbr * KS_ELEMS;
         u32x4 ka[NKS];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) ka[ks] = lds16(Ks + (kb * 32 + r) * KSTR + 16 * ks + 8 * g);
@@ -616,11 +635,23 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(Para
         for (int ks = 0; ks < NKS; ++ks) acc = mfma_qk<IO>(ka[ks], qreg[ks], acc);
         s = acc;
     };
+    auto pv_quarter = [&](int t, int kb, const u32x4 (&p)[2]) __attribute__((always_inline)) {
+        const uint16_t *Vt = vring(t);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                st.o[db] = mfma_pv(lds16(Vt + (db * 32 + r) * VT_STRIDE + kb * 32 + 16 * tt + 8 * g), p[tt], st.o[db]);
+    };
     auto pair_block = [&](int t, int kend, bool mask) __attribute__((always_inline)) {
-        pstage(pslot(t + 4), 0);
-        pstage(pslot(t + 5), 1);
-        pload(t + 6, 0);
-        pload(t + 7, 1);
+        pstage_k(t + 4, 0);
+        pstage_k(t + 5, 1);
+        pstage_v(t + 2, 0);
+        pstage_v(t + 3, 1);
+        pload_k(t + 6, 0);
+        pload_k(t + 7, 1);
+        pload_v(t + 4, 0);
+        pload_v(t + 5, 1);
         // scores of keys past the item's end or outside the window set to -inf, in place
         // (a branch around this part only: the rest of the block is one copy of code)
         if (mask) {
@@ -636,41 +667,64 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(Para
                     }
             }
         }
-        // maximum of c * s over the pair's valid keys
-        float v[2][32];
+        if constexpr (FAST) {
+            // P of each quarter against the current base; a score more than ~16 above it
+            // overflows fp16 to inf (a row without a base yet has -m = +inf), which the row
+            // sum shows: only then is the quarter redone with its exact maximum
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+            for (int q = 0; q < 4; ++q) {
+                const int kb = q & 1;
+                u32x4 p[2];
+                float part;
+                softmax_half<false>(sp[q], kb, c, -st.m, TileMask{0, 0}, p, part);
+                if (__builtin_expect(__any(!(part <= 3.0e38f)), 0)) {
+                    const float mt = half_max(sp[q], c);
+                    const float mn = (mt > st.m + TAU) ? mt : st.m;
+                    const float ea = __builtin_amdgcn_exp2f(st.m - mn);
+                    const float a = (mn == st.m) ? 1.0f : ea;
+                    st.m = mn;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+                    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) v[j][kb * 16 + i] = sp[2 * j + kb][i];
-        const float mr = pair_max(fmaxf(max32(v[0]), max32(v[1])));
-        const float mt = (mr == NEG_INF) ? NEG_INF : mr * c;
-        const float mn = (mt > st.m + TAU) ? mt : st.m;
-        const float ea = __builtin_amdgcn_exp2f(st.m - mn);
-        const float a = (mn == st.m) ? 1.0f : ea;
-        st.m = mn;
-        const float nb = (mn == NEG_INF) ? 0.0f : -mn;
+                        for (int i = 0; i < 16; ++i) st.o[db][i] *= a;
+                    st.l *= a;
+                    softmax_half<false>(sp[q], kb, c, (mn == NEG_INF) ? 0.0f : -mn, TileMask{0, 0}, p, part);
+                }
+                st.l += part;
+                qk_quarter(t + 2 + (q >> 1), kb, sp[q]);   // next pair: computed, unused past the item
+                pv_quarter(t + (q >> 1), kb, p);
+            }
+        } else {
+            // maximum of c * s over the pair's valid keys
+            float v[2][32];
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) st.o[db][i] *= a;
-        float part[4];
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int kb = q & 1;
-            u32x4 p[2];
-            softmax_half<false>(sp[q], kb, c, nb, TileMask{0, 0}, p, part[q]);   // masked above
-            qk_quarter(pslot(t + 2 + (q >> 1)), kb, sp[q]);   // next pair: computed, unused past the item
-            const uint16_t *Vt = smem + pslot(t + (q >> 1)) * BUF_ELEMS + KS_ELEMS;
+                    for (int i = 0; i < 16; ++i) v[j][kb * 16 + i] = sp[2 * j + kb][i];
+            const float mr = pair_max(fmaxf(max32(v[0]), max32(v[1])));
+            const float mt = (mr == NEG_INF) ? NEG_INF : mr * c;
+            const float mn = (mt > st.m + TAU) ? mt : st.m;
+            const float ea = __builtin_amdgcn_exp2f(st.m - mn);
+            const float a = (mn == st.m) ? 1.0f : ea;
+            st.m = mn;
+            const float nb = (mn == NEG_INF) ? 0.0f : -mn;
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    st.o[db] = mfma_pv(lds16(Vt + (db * 32 + r) * VT_STRIDE + kb * 32 + 16 * tt + 8 * g), p[tt],
-                                       st.o[db]);
+                for (int i = 0; i < 16; ++i) st.o[db][i] *= a;
+            float part[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int kb = q & 1;
+                u32x4 p[2];
+                softmax_half<false>(sp[q], kb, c, nb, TileMask{0, 0}, p, part[q]);   // masked above
+                qk_quarter(t + 2 + (q >> 1), kb, sp[q]);   // next pair: computed, unused past the item
+                pv_quarter(t + (q >> 1), kb, p);
+            }
+            st.l = __builtin_fmaf(st.l, a, (part[0] + part[1]) + (part[2] + part[3]));
         }
-        st.l = __builtin_fmaf(st.l, a, (part[0] + part[1]) + (part[2] + part[3]));
         __syncthreads();
     };
 
@@ -706,23 +760,32 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(Para
         st.a = 1.0f;
 
         if constexpr (PAIR && !SAFE) {
-            // (one item per workgroup: always cold)
+            // (one item per workgroup: always cold) K of tb .. tb+3 and V of tb, tb+1 staged,
+            // K of tb+4, tb+5 and V of tb+2, tb+3 loaded
             if (wait) __syncthreads();
-            pload(cur.tb, 0);
-            pload(cur.tb + 1, 1);
-            pstage(pslot(cur.tb), 0);
-            pstage(pslot(cur.tb + 1), 1);
-            pload(cur.tb + 2, 0);
-            pload(cur.tb + 3, 1);
-            pstage(pslot(cur.tb + 2), 0);
-            pstage(pslot(cur.tb + 3), 1);
-            pload(cur.tb + 4, 0);
-            pload(cur.tb + 5, 1);
+            const int tb = cur.tb;
+            pload_k(tb, 0);
+            pload_k(tb + 1, 1);
+            pload_v(tb, 0);
+            pload_v(tb + 1, 1);
+            pstage_k(tb, 0);
+            pstage_k(tb + 1, 1);
+            pstage_v(tb, 0);
+            pstage_v(tb + 1, 1);
+            pload_k(tb + 2, 0);
+            pload_k(tb + 3, 1);
+            pstage_k(tb + 2, 0);
+            pstage_k(tb + 3, 1);
+            pload_k(tb + 4, 0);
+            pload_k(tb + 5, 1);
+            pload_v(tb + 2, 0);
+            pload_v(tb + 3, 1);
             __syncthreads();
-            qk_quarter(pslot(cur.tb), 0, sp[0]);
-            qk_quarter(pslot(cur.tb), 1, sp[1]);
-            qk_quarter(pslot(cur.tb + 1), 0, sp[2]);
-            qk_quarter(pslot(cur.tb + 1), 1, sp[3]);
+            qk_quarter(tb, 0, sp[0]);
+            qk_quarter(tb, 1, sp[1]);
+            qk_quarter(tb + 1, 0, sp[2]);
+            qk_quarter(tb + 1, 1, sp[3]);
+            __syncthreads();   // every wave has read K of tb, tb+1 before the first pair block restages them
             const int kend = min(L, cur.te * BN);
             for (int t = cur.tb; t < cur.te; t += 2)
                 pair_block(t, kend, tile_needs_mask(t, kend) || tile_needs_mask(t + 1, kend));
