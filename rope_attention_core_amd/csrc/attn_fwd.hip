@@ -28,9 +28,10 @@
 //    fp16.
 //  * K is rotated (FP32, fixed operation order, no contraction) and rounded to the IO
 //    dtype while it is staged into LDS; Q once into registers.
-//  * Plain D = 64 instances of one round per query tile on the pre-pass workspace walk
-//    the keys in pairs of tiles (128 keys per step: one maximum, base move, O rescale
-//    and barrier per pair; see pair_block). The others:
+//  * D = 64 instances of one round per query tile on the pre-pass workspace walk the
+//    keys in pairs of tiles (128 keys per step, one barrier per pair; plain calls also
+//    take one maximum, base move and O rescale per pair), with K and V^T in LDS rings
+//    of four tiles each; see pair_block. The others:
 //  * Software pipeline over key tiles with three LDS buffers and one barrier per tile.
 //    The block for tile t first issues QK^T(t+1) into the second score set, so those
 //    MFMAs run under the softmax of tile t (VALU); P.V(t) follows each 32-key half of
@@ -57,6 +58,9 @@
 //    in turn, and the key-tile pipeline runs on from one into the next (the last blocks
 //    of a tile stage the next tile's first key tiles), so a tile's start (its first
 //    loads and stages) no longer stalls the workgroup.
+//  * One-round grids with the pre-pass whose last round would leave at least half the
+//    compute units idle split the tiles of that round into key ranges, merged by the
+//    range that finishes last (the split tail; see tail_plan).
 
 #include <algorithm>
 
