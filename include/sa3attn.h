@@ -266,10 +266,10 @@ int sa3attn_forward_ws(const sa3attn_desc *desc, const sa3attn_strides *strides,
  *   policy: as for sa3attn_forward_ws. When the pre-pass with the split tail's
  *     partials would need more than SA3ATTN_SCRATCH_BYTES (sa3attn_workspace_bytes
  *     gives the size) but K' and V' alone fit, the call runs the pre-pass without the
- *     split tail (as a workspace call would run the same grid without one: bitwise the
- *     fused path's outputs). When K' and V' alone do not fit either: AUTO runs the
- *     call without the pre-pass (bitwise as NEVER); ALWAYS, ONLY and REUSE return
- *     SA3_ERR_SCRATCH before anything is enqueued.
+ *     split tail (its last round whole: other last bits than the workspace call's, the
+ *     same bar). When K' and V' alone do not fit either: AUTO runs the call without the
+ *     pre-pass (bitwise as NEVER); ALWAYS, ONLY and REUSE return SA3_ERR_SCRATCH before
+ *     anything is enqueued.
  *   Sharing: every call on one GPU uses the same array, whose contents persist from
  *     call to call (REUSE reads what the last ALWAYS or ONLY call on that GPU wrote).
  *     Calls that may overlap in time on one GPU (other streams, other threads) race

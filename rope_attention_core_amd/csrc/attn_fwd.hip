@@ -28,8 +28,8 @@
 //    fp16.
 //  * K is rotated (FP32, fixed operation order, no contraction) and rounded to the IO
 //    dtype while it is staged into LDS; Q once into registers.
-//  * D = 64 instances of one round per query tile on the pre-pass workspace walk the
-//    keys in pairs of tiles (128 keys per step, one barrier per pair; plain calls also
+//  * Instances of one round per query tile on the pre-pass workspace (all but the
+//    differential D = 128 ones) walk the keys in pairs of tiles (128 keys per step, one barrier per pair; plain calls also
 //    take one maximum, base move and O rescale per pair), with K and V^T in LDS rings
 //    of four tiles each; see pair_block. The others:
 //  * Software pipeline over key tiles with three LDS buffers and one barrier per tile.
@@ -124,9 +124,10 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(Para
     constexpr bool CP = PERS && !(DIFF && D == 128);
     constexpr int XB_ELEMS = (CP && DIFF) ? WPB * 32 * D * 2 : 0;
     static_assert(!DIFF || CP || NBUF * BUF_ELEMS * 2 >= WPB * 32 * D * 4, "LDS too small for the O2 exchange");
-    // PAIR: D = 64 one-round instances with the pre-pass walk the keys 128 at a time (see
+    // PAIR: one-round instances with the pre-pass walk the keys 128 at a time (see
     // pair_block below), with rings of PR K tiles (each branch) and PR V^T tiles in LDS
-    constexpr bool PAIR = PRE && D == 64 && !PERS && NW == waves_for<D>();
+    // (not differential D = 128: its rings would take 213 KB)
+    constexpr bool PAIR = PRE && (D == 64 || !DIFF) && !PERS && NW == waves_for<D>();
     constexpr int PR = 4;
     constexpr int PAIR_ELEMS = PR * NBS * KS_ELEMS + PR * VT_ELEMS;
     constexpr int STAGE_ELEMS = (PAIR && PAIR_ELEMS > NBUF * BUF_ELEMS) ? PAIR_ELEMS : NBUF * BUF_ELEMS;

@@ -107,7 +107,8 @@ def test_noalloc_split_tail():
     """A grid whose last round is split: with room in the static array for the partials
     (B1 H24 L3000: 27 MiB) the no-alloc call splits it as the workspace call does (the
     same bits); the long latent at D = 128 (82 MiB with the partials, 48 MiB without)
-    runs the pre-pass without the split, bitwise as the fused path."""
+    runs the pre-pass without the split: against the oracle on the heads whose tiles
+    the workspace call splits, and not the split call's bits."""
     torch = G.torch_mod()
     lib = G.sa3.load_library()
     cfg = synth.config("dit_long", B=1, H=24, L=3000, seed=80)
@@ -122,11 +123,17 @@ def test_noalloc_split_tail():
     big = synth.config("dit_long_d128")
     nb = G.sa3.workspace_bytes(big.B, big.H, big.L, big.D, dtype=G.sa3.BF16, prep="always")
     assert nb > G.sa3.SCRATCH_BYTES
-    _, t, (o_a, o_b) = _setup(big)
+    inp, t, (o_a, o_b) = _setup(big)
     assert _na_call(lib, big, t, o_a, ALWAYS) == 0
-    assert _na_call(lib, big, t, o_b, NEVER) == 0
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    assert _ws_call(lib, big, t, o_b, ALWAYS, ws) == 0
     torch.cuda.synchronize()
-    assert torch.equal(o_a, o_b)
+    assert not torch.equal(o_a, o_b), "the no-alloc call split its last round"
+    rows = np.array([0, 255, 256, 2049, big.L - 1])
+    for b, h in ((1, 4), (1, 11)):                     # heads of the split tiles
+        want = G.run_oracle_rows(big, inp, b, h, rows)
+        G.assert_parity(o_a[b, h, rows].float().cpu().numpy().astype(np.float64), want,
+                        what=f"noalloc d128 (b,h)=({b},{h})", out=big.out_dtype)
 
 
 def test_noalloc_size_limit():
