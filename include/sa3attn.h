@@ -213,13 +213,13 @@ int sa3attn_forward_general(const sa3attn_desc *desc, const sa3attn_strides *str
  *     tile merges the ranges' partial results, which the workspace holds after K' and
  *     V' (r x k x 8 x 64 x (D / 32 x 16 + 4) floats, then r counters in 256-byte units).
  *   policy: SA3_PREP_AUTO runs the pre-pass on small grids and split-tail grids, and
- *     otherwise when the grid has more workgroups than
- *     the current device has compute units (workgroups = B x H x ceil(L / tile rows);
- *     256 compute units are assumed when no device is current) and a key tile is
- *     visited by at least 12 query tiles of a plain call or 9 of a differential one
- *     (full attention: L > 2816 plain, L > 1024 differential; query tiles of 256 and
- *     128 rows; a window of half-width w: about (2w + 64) / tile rows + 1 visits), the
- *     shapes where it measured faster; SA3_PREP_ALWAYS whenever the call
+ *     otherwise when a key tile is visited by enough query tiles (query tiles of 256
+ *     rows plain, 128 differential; full attention: ceil(L / rows) visits; a window of
+ *     half-width w: about (2w + 64) / rows + 1): at least 3 at D = 128; at D = 64 at
+ *     least 10 plain or 9 differential, except contiguous calls on grids of more tiles
+ *     than compute units whose tiles span at most 32 key tiles (these run persistent):
+ *     at least 12 plain or 9 differential there (256 compute units are assumed when no
+ *     device is current); the shapes where it measured faster. SA3_PREP_ALWAYS whenever the call
  *     takes the long-span kernel; SA3_PREP_NEVER never. SA3_PREP_ONLY enqueues the
  *     pre-pass alone (out is not written) and SA3_PREP_REUSE the attention kernel
  *     alone, reading a workspace that an earlier ALWAYS or ONLY call filled from the

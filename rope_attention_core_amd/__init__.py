@@ -234,9 +234,9 @@ def forward(q, k, v, cos, sin, *, window=-1, lam=0.0, scale=None, out=None, out_
     prep: the pre-pass policy ("auto": on small plain D = 64 grids, fewer 256-row
     query tiles than compute units and at most two 64-row tiles per compute unit; on
     grids whose last round of query tiles fills at most half the compute units; and
-    when the grid has more workgroups than the
-    device has compute units and each key tile is visited by >= 12 query tiles, 9 for
-    a differential call; "always"; "never"; "only": the pre-pass alone,
+    when each key tile is visited by enough query tiles: >= 3 at D = 128, at D = 64
+    >= 10 plain / 9 differential, or >= 12 / 9 on persistent window grids (see
+    include/sa3attn.h); "always"; "never"; "only": the pre-pass alone,
     out not written; "reuse": the attention kernel alone on a workspace an "always" /
     "only" call filled from the same k, v, cos, sin); workspace: a uint8 GPU tensor of
     at least workspace_bytes(...) bytes, allocated here (torch's caching allocator, on

@@ -1130,14 +1130,19 @@ unsigned long long prep_bytes(const LaunchArgs &a) {
 
 // The fused staging rotates and transposes a key tile once per query tile that visits
 // it; the pre-pass does that once but adds a pass over K and V (about one more read and
-// write of each) before the attention kernel can start. Measured over 18 shapes (plain
-// and differential, full and windowed, L 768-8192): it pays only when the grid has more
-// workgroups than the device has compute units (a single round of workgroups pays the
-// pass in full: 1-4% slower even at 12-16 visits) and each key tile is visited by at
-// least 12 query tiles (plain; 10 visits break even) or 9 (differential; 8 break
-// even): then 1-10% faster, e.g. 6% at L = 4096 and 6% for a differential window of
-// half-width 768; a differential window of half-width 256 (6 visits) runs 3% faster
-// without it.
+// write of each) before the attention kernel can start. Measured (always against never,
+// same process, 21 shapes, with the 128-key steps and the split tail in place):
+//  * D = 128: the pre-pass wins on every shape, 18-35% (windows of half-width 256 to
+//    1024 at 4-10 visits, persistent or not, plain and differential; full attention at
+//    L = 2048 in one round): its fused staging rotates 128 dims per key and its
+//    instances spill.
+//  * D = 64, grids that run one round per tile (the pair steps): from about 10 visits
+//    plain (a 1024-key window, 10 visits: 8% faster; L = 2048 in one round, 8 visits:
+//    even) and 9 differential (L = 2048 in one round, 16 visits: 2.5% faster; L = 1024,
+//    8 visits: 8% slower), in one round or several.
+//  * D = 64 persistent grids (windows whose tiles span <= 32 key tiles): from 12 visits
+//    plain and 9 differential (plain 768-key window, 8 visits: 1% slower; differential
+//    1024-key window, 10 visits: 1% faster, 1536: 5% faster; 256, 6 visits: 7% slower).
 bool prep_pays(const LaunchArgs &a) {
     if (use_narrow(a)) return false;
     if (small_grid(a)) return true;
@@ -1148,8 +1153,9 @@ bool prep_pays(const LaunchArgs &a) {
     const int bm = tile_rows(a);
     const long long n_qtiles = ((long long)a.L + bm - 1) / bm;
     const long long visits = a.window < 0 ? n_qtiles : std::min(n_qtiles, (2ll * a.window + BN + bm - 1) / bm + 1);
-    const long long wgs = n_qtiles * a.B * a.H;
-    return wgs > a.n_cu && visits >= (a.diff ? 9 : 12);
+    if (a.D == 128) return visits >= 3;
+    if (persistent_shape(a) && a.contig) return visits >= (a.diff ? 9 : 12);
+    return visits >= (a.diff ? 9 : 10);
 }
 
 int launch_forward(const LaunchArgs &a) {

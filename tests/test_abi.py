@@ -331,31 +331,34 @@ def _tail_bytes(B, H, L, D=64, differential=0, window=-1, n_cu=256):
 
 
 @pytest.mark.parametrize("kw,policy,want", [
-    # AUTO: more workgroups than the 256 compute units assumed without a device, and at
-    # least 12 query tiles of 256 rows (plain) / 9 of 128 (differential) per key tile
+    # AUTO (256 compute units assumed without a device): key tiles visited by >= 10
+    # query tiles of 256 rows (plain) / 9 of 128 (differential), >= 12 / 9 on persistent
+    # grids, >= 3 at D = 128; small grids and split tails always
     (dict(B=2, H=24, L=4096), AUTO, 2 * 2 * 24 * 4096 * 64 * 2),
     (dict(B=1, H=24, L=2816), AUTO, 2 * 24 * _lp(2816) * 64 * 2),        # 11 visits, but 264 WGs: split tail
-    (dict(B=1, H=20, L=2816), AUTO, 0),                                  # 11 visits, 220 WGs
+    (dict(B=1, H=20, L=2816), AUTO, 2 * 20 * _lp(2816) * 64 * 2),        # 11 visits, 220 WGs (one round)
+    (dict(B=1, H=24, L=2304), AUTO, 0),                                  # 9 visits, 216 WGs
     (dict(B=1, H=24, L=2817), AUTO, 2 * 24 * _lp(2817) * 64 * 2),        # 12 visits, 288 WGs
     # plain D = 64 grids of fewer 256-row workgroups than compute units run 64-row tiles
     # with the pre-pass
-    (dict(B=1, H=16, L=3072), AUTO, 0),                                  # 768 of 64 rows: 1.5 rounds
+    (dict(B=1, H=16, L=3072), AUTO, 2 * 16 * 3072 * 64 * 2),             # 768 of 64 rows: 256-row tiles, 12 visits
     (dict(B=1, H=24, L=1292), AUTO, 2 * 24 * _lp(1292) * 64 * 2),        # 144
     (dict(B=1, H=1, L=257), AUTO, 2 * 1 * _lp(257) * 64 * 2),            # 2
     (dict(B=1, H=12, L=2560), AUTO, 2 * 12 * 2560 * 64 * 2),             # 120 (480 of 64 rows)
-    (dict(B=1, H=24, L=2560), AUTO, 0),                                  # 240 (960 of 64 rows)
+    (dict(B=1, H=24, L=2560), AUTO, 2 * 24 * 2560 * 64 * 2),             # 240 (960 of 64 rows): 10 visits
     (dict(B=1, H=24, L=1344), AUTO, 2 * 24 * 1344 * 64 * 2),             # 144 (504 of 64 rows)
     (dict(B=1, H=24, L=1345), AUTO, 0),                                  # 144 (528 of 64 rows)
-    (dict(B=1, H=24, L=2560, D=128), AUTO, 0),                           # D = 128: 256-row tiles
+    (dict(B=1, H=24, L=2560, D=128), AUTO, 2 * 24 * 2560 * 128 * 2),     # D = 128: from 3 visits
+    (dict(B=1, H=24, L=384, D=128), AUTO, 0),                            # D = 128, 2 visits
     (dict(B=1, H=32, L=1024, differential=1), AUTO, 0),                  # 8 visits
     (dict(B=1, H=32, L=1025, differential=1), AUTO, 3 * 32 * _lp(1025) * 64 * 2),   # 9, 288 WGs
-    (dict(B=1, H=16, L=2048, differential=1), AUTO, 0),                  # 16 visits, 256 WGs
+    (dict(B=1, H=16, L=2048, differential=1), AUTO, 3 * 16 * 2048 * 64 * 2),   # 16 visits, one round
     (dict(B=1, H=16, L=2049, differential=1), AUTO, 3 * 16 * _lp(2049) * 64 * 2),   # 17, 272 WGs
     # D = 128: the same 256 / 128 rows per query tile
     (dict(B=1, H=24, L=2816, D=128), AUTO, 2 * 24 * _lp(2816) * 128 * 2),   # split tail
-    (dict(B=1, H=20, L=2816, D=128), AUTO, 0),
+    (dict(B=1, H=20, L=2816, D=128), AUTO, 2 * 20 * _lp(2816) * 128 * 2),
     (dict(B=1, H=24, L=2817, D=128), AUTO, 2 * 24 * _lp(2817) * 128 * 2),
-    (dict(B=1, H=32, L=1024, D=128, differential=1), AUTO, 0),
+    (dict(B=1, H=32, L=1024, D=128, differential=1), AUTO, 3 * 32 * 1024 * 128 * 2),
     (dict(B=1, H=32, L=1025, D=128, differential=1), AUTO, 3 * 32 * _lp(1025) * 128 * 2),
     # windows: a key tile of a half-width-w window is visited by about (2w + 64) / rows + 1
     # query tiles: 6 at w = 256, 8 at w = 384, 9 at w = 448 (128 rows); 10 at w = 1024,
@@ -363,7 +366,8 @@ def _tail_bytes(B, H, L, D=64, differential=0, window=-1, n_cu=256):
     (dict(B=1, H=16, L=8192, window=256, differential=1), AUTO, 0),
     (dict(B=1, H=16, L=8192, window=384, differential=1), AUTO, 0),
     (dict(B=1, H=16, L=8192, window=448, differential=1), AUTO, 3 * 16 * 8192 * 64 * 2),
-    (dict(B=1, H=16, L=8192, window=1024), AUTO, 0),
+    (dict(B=1, H=16, L=8192, window=1024), AUTO, 2 * 16 * 8192 * 64 * 2),   # 10 visits, tiles span 37 key tiles
+    (dict(B=1, H=16, L=8192, window=768), AUTO, 0),                      # persistent, 8 visits
     (dict(B=1, H=16, L=8192, window=1280), AUTO, 2 * 16 * 8192 * 64 * 2),
     (dict(B=1, H=16, L=8192, window=256, differential=1), ALWAYS, 3 * 16 * 8192 * 64 * 2),
     (dict(B=1, H=16, L=8192, window=1024, differential=1), AUTO, 3 * 16 * 8192 * 64 * 2),
