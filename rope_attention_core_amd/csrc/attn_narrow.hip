@@ -103,8 +103,12 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
     const int bid = blockIdx.x;
     const int per = nblk >> 3, rem = nblk & 7, xcd = bid & 7, idx = bid >> 3;
     const int lid = (xcd < rem) ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
-    const int bh = lid / P.n_qtiles;
-    const int qt = lid - bh * P.n_qtiles;
+    // windowed mode: query tiles major, heads minor, so the workgroups an XCD runs at
+    // once share the rows of the cos/sin table (and a head's neighbouring tiles, their
+    // halos); a short sequence keeps each head's workgroups together (the whole span)
+    const int nbh = nblk / P.n_qtiles;
+    const int bh = NKF ? lid / P.n_qtiles : lid % nbh;
+    const int qt = NKF ? lid - bh * P.n_qtiles : lid / nbh;
 
     const int bb = bh / P.H, hh = bh - bb * P.H;
     const uint32_t qrb = CONTIG ? (uint32_t)ROWB : P.q_rowb;
