@@ -73,7 +73,12 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
     using S = NarrowShape<DIFF, NKF>;
     constexpr int NT = S::NT, NBS = S::NBS, WPB = S::WPB, BM = S::BM, NK = S::NK, NKB = S::NKB;
     constexpr int KSPLIT = S::KSPLIT;
-    constexpr int NKBW = NKB / KSPLIT;       // 32-key blocks of this wave's share
+    // 32-key blocks a wave computes: its share of the span in short-sequence mode; in
+    // windowed mode the three blocks from its own row offset, which hold every key its 32
+    // rows can see (offsets 32 wq .. 32 wq + 31 + 2w of the span, w <= 32); the span's
+    // other blocks are wholly outside its rows' windows
+    constexpr int NKBW = NKF ? NKB / KSPLIT : 3;
+    static_assert(NKF || (WPB - 1) + NKBW <= NKB, "windowed blocks inside the span");
     static_assert(NKB % KSPLIT == 0, "key split");
     // the merge of the key shares reuses the staging area: NT / 64 waves x 34 rows of 64 floats
     constexpr int MERGE_ELEMS = KSPLIT > 1 ? (NT / 64) * 34 * 64 * 2 : 0;
@@ -263,8 +268,8 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
 
         // ---- scores of this wave's 32 rows over the span: S^T blocks of 32 keys ----------
         const uint16_t *Ks = smem + wbr * S::K_ELEMS;
-        // s[j]: keys of 32-key block kb = kq * NKBW + j of the span
-        const int kb0 = kq * NKBW;
+        // s[j]: keys of 32-key block kb = kb0 + j of the span
+        const int kb0 = NKF ? kq * NKBW : wq;
         f32x16 s[NKBW];
 #pragma unroll
         for (int j = 0; j < NKBW; ++j) {
@@ -331,7 +336,11 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
                 }
             }
         }
-        l = pair_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
+        // acc[0..1] hold the span's even blocks (block kb0 + j goes to parity j & 1)
+        const bool odd = !NKF && (kb0 & 1);
+        const float e0 = odd ? acc[2] : acc[0], e1 = odd ? acc[3] : acc[1];
+        const float o0 = odd ? acc[0] : acc[2], o1 = odd ? acc[1] : acc[3];
+        l = pair_sum((e0 + e1) + (o0 + o1));
     };
     compute(std::false_type{});
 
