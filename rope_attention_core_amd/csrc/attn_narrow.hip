@@ -9,8 +9,9 @@
 // its prologue. Here one workgroup takes a short block of query rows and stages the
 // whole key span they can see at once ([q0 - w, q0 + BM - 1 + w], BM + 64 keys, for a
 // narrow window; all of [0, L) for a short sequence), then each wave computes its
-// scores over that span, one exact softmax (the maximum over the whole span is known,
-// so there is no running rescale), and P.V, and stores. Small workgroups and a small
+// scores over its part of that span (for a window, the three 32-key blocks its rows can
+// see), one exact softmax (the maximum over those keys is known, so there is no running
+// rescale), and P.V, and stores. Small workgroups and a small
 // LDS footprint keep several of them resident per CU so that their loads overlap.
 //
 //  * Plain, windowed: 4 waves x 32 query rows (BM = 128); span 192 keys.
