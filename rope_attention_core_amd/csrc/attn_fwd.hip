@@ -648,7 +648,13 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(Para
             for (int db = 0; db < NDB; ++db)
                 st.o[db] = mfma_pv(lds16(Vt + (db * 32 + r) * VT_STRIDE + kb * 32 + 16 * tt + 8 * g), p[tt], st.o[db]);
     };
+    // Wave priority: the two waves of a SIMD run the same pair block, and the SIMD issues
+    // for the older one first, which then idles at the barrier while the younger finishes
+    // alone (27% of a pair, measured with per-wave clocks). A wave drops to the lower
+    // priority for the second half of its pair (quarters 2 and 3), so the wave behind
+    // gets the issue slots until it reaches that point too.
     auto pair_block = [&](int t, int kend, bool mask) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_setprio(1);
         pstage_k(t + 4, 0);
         pstage_k(t + 5, 1);
         pstage_v(t + 2, 0);
@@ -679,6 +685,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(Para
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int kb = q & 1;
+                if (q == 2) __builtin_amdgcn_s_setprio(0);
                 u32x4 p[2];
                 float part;
                 softmax_half<false>(sp[q], kb, c, -st.m, TileMask{0, 0}, p, part);
@@ -723,6 +730,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(Para
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int kb = q & 1;
+                if (q == 2) __builtin_amdgcn_s_setprio(0);
                 u32x4 p[2];
                 softmax_half<false>(sp[q], kb, c, nb, TileMask{0, 0}, p, part[q]);   // masked above
                 qk_quarter(t + 2 + (q >> 1), kb, sp[q]);   // next pair: computed, unused past the item
