@@ -148,6 +148,16 @@ def test_window_sweep(w, io):
     G.assert_parity(G.run_gpu(cfg, inp), G.run_oracle(cfg, inp), what=f"window {w} {io}", out=cfg.out_dtype)
 
 
+@pytest.mark.parametrize("w", [0, 1, 16, 17, 31, 32])
+def test_differential_narrow_window_sweep(w):
+    """Differential windows of the single-span kernel: each wave computes the three
+    32-key blocks of the span from its own row offset, whose last needed key (offset
+    32 wq + 31 + 2w) lies in the third block from w = 17 and at its last key at w = 32."""
+    cfg = synth.config("samel_swa", H=2, L=700, window=w, seed=4100 + w, out="f32")
+    inp = synth.make_inputs(cfg)
+    G.assert_parity(G.run_gpu(cfg, inp), G.run_oracle(cfg, inp), what=f"diff narrow w{w}")
+
+
 @pytest.mark.parametrize("lam", [0.0, 0.8, -0.5])
 @pytest.mark.parametrize("w", [-1, 17, 256])
 @pytest.mark.parametrize("io", ["f16", "bf16"])
