@@ -29,7 +29,12 @@
 namespace sa3 {
 namespace {
 
-template <int IO>
+// SHARED: the grid has more workgroups than compute units, so two share a CU and each
+// SIMD runs one wave of each. The SIMD issues for the older wave first; a wave then drops
+// to the lower priority for the second half of each step, so the workgroup that is
+// behind gets the issue slots until it reaches that point too. With one workgroup per CU
+// the priority changes only cost time, and that instance keeps one priority.
+template <int IO, bool SHARED>
 __global__ __launch_bounds__(256, 2) void attn_split_kernel(Params P) {
     constexpr int NT = 256;
     constexpr int NW = 4;
@@ -201,6 +206,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(Params P) {
     // computed and never used, which keeps the step one block of straight-line code.
     const int steps = T0;
     auto step = [&](int j, f32x16 (&cur)[2], f32x16 (&nxt)[2], auto safe_tag) __attribute__((always_inline)) {
+        if constexpr (SHARED) __builtin_amdgcn_s_setprio(1);
         stage_k(j & 1);
         stage_v((j + 1) & 1, safe_tag);
         load_k(j + 3);
@@ -228,6 +234,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(Params P) {
             float part[2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
+                if (SHARED && kb == 1) __builtin_amdgcn_s_setprio(0);
                 u32x4 p[2];
                 softmax_half<false>(cur[kb], kb, c, nb, mk, p, part[kb]);   // masked by tile_max
 #pragma unroll
@@ -349,12 +356,20 @@ int launch_split(const LaunchArgs &a, int n_qtiles) {
     Params P = make_params(a);
     P.n_qtiles = n_qtiles;
     P.n_items = n_qtiles * a.B * a.H;
-    if (a.dtype == 1)
-        hipLaunchKernelGGL(attn_split_kernel<IO_BF16>, dim3((unsigned)P.n_items), dim3(256), 0,
-                           static_cast<hipStream_t>(a.stream), P);
-    else
-        hipLaunchKernelGGL(attn_split_kernel<IO_F16>, dim3((unsigned)P.n_items), dim3(256), 0,
-                           static_cast<hipStream_t>(a.stream), P);
+    const dim3 grid((unsigned)P.n_items), block(256);
+    hipStream_t s = static_cast<hipStream_t>(a.stream);
+    const bool shared = P.n_items > (a.n_cu > 0 ? a.n_cu : 256);
+    if (a.dtype == 1) {
+        if (shared)
+            hipLaunchKernelGGL((attn_split_kernel<IO_BF16, true>), grid, block, 0, s, P);
+        else
+            hipLaunchKernelGGL((attn_split_kernel<IO_BF16, false>), grid, block, 0, s, P);
+    } else {
+        if (shared)
+            hipLaunchKernelGGL((attn_split_kernel<IO_F16, true>), grid, block, 0, s, P);
+        else
+            hipLaunchKernelGGL((attn_split_kernel<IO_F16, false>), grid, block, 0, s, P);
+    }
     return (int)hipGetLastError();
 }
 
