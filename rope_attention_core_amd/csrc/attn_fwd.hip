@@ -83,10 +83,13 @@ struct Branch {
 template <int D>
 constexpr int waves_for() { return 8; }
 
-// Plain: each wave owns 32 query rows, BM = 32 x waves. Differential: waves w and
-// w + waves/2 own the same 32 rows, wave w the first softmax branch (Q1, K1) and the
-// other the second (Q2, K2); both multiply the same staged V tile, BM = 16 x waves, and
-// the second branch hands O2 / l2 to the first through LDS at the end.
+// Plain: each wave owns 32 query rows, BM = 32 x waves. Differential: wave w < waves/2
+// takes the first softmax branch (Q1, K1) of query block w, wave waves/2 + w the second
+// (Q2, K2) of block waves/2 - 1 - w; both branches of a block multiply the same staged
+// V tile, BM = 16 x waves, and the second hands O2 / l2 to the first through LDS at the
+// end. (Waves w and waves/2 + w share a SIMD; the reversed order pairs a block at one
+// end of the tile with one at the other, so in a window's edge tiles, which lie wholly
+// outside one of the two blocks' windows, one wave of the SIMD has no softmax to do.)
 // CONTIG: q, k, v and out are contiguous [B][H][L][D] (q, k stacked [2][...]) with the
 // default RoPE; the row strides are then compile-time constants, which keeps scalar
 // registers free. D: head dim, 64 or 128. PRE: K and V come from the pre-pass
@@ -139,7 +142,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(Para
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wbr = DIFF ? wave / WPB : 0;   // this wave's softmax branch
-    const int wq = DIFF ? wave % WPB : wave; // this wave's query block
+    const int wq = DIFF ? (wbr ? WPB - 1 - wave % WPB : wave % WPB) : wave;   // this wave's query block
     const int r = lane & 31;
     const int g = lane >> 5;
     const int L = P.L;
@@ -448,6 +451,16 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(Para
         if (window < 0 || qw > qhi_live) return false;
         return k0 < qhi_live - window || k0 + BN - 1 > qw + window;
     };
+    // a tile of the item's span that lies wholly outside this wave's window (its rows sit
+    // at one end of the query tile): every score masked, so P = 0 and the base, O and l
+    // stay as they are; the wave skips that tile's softmax and P.V (wave-uniform; the QK^T
+    // issued for it a block earlier stays, a branch around it made the compiler spill).
+    // Contiguous D = 64 instances only: in the others the branch adds spills.
+    constexpr bool SKIP_OUT = D == 64 && CONTIG;
+    auto tile_outside = [&](int t) __attribute__((always_inline)) {
+        const int k0 = t * BN;
+        return SKIP_OUT && window >= 0 && qw <= qhi_live && (k0 > qhi_live + window || k0 + BN - 1 < qw - window);
+    };
 
     // Two score sets: the block of tile t starts QK^T(t+1) into sb[P^1] so its MFMAs run
     // under the softmax of tile t (sb[P]); P.V(t) follows each 32-key half of the softmax.
@@ -538,6 +551,14 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(Para
                         st.o[db] = mfma_pv(lds16(Vt + (db * 32 + r) * VT_STRIDE + kb * 32 + 16 * tt + 8 * g), p[tt],
                                            st.o[db]);
             }
+            if constexpr (!EARLY) {
+                stage(slot(t + 2), safe_tag);
+                load_next(t, safe_tag);
+            }
+            __syncthreads();
+            return;
+        }
+        if (MASK && tile_outside(t)) {
             if constexpr (!EARLY) {
                 stage(slot(t + 2), safe_tag);
                 load_next(t, safe_tag);
