@@ -181,8 +181,23 @@ __global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void attn_fwd_kernel(Para
     // linear tile id -> (b*h, query tile, key-tile range)
     auto tile_of_lid = [&](int lid) __attribute__((always_inline)) {
         Item x;
-        x.bh = lid / P.n_qtiles;
-        x.qt = lid - x.bh * P.n_qtiles;
+        if (PERS && DIFF && window >= 0) {
+            // persistent differential windows: heads in groups of four, query tiles major
+            // within a group, so that the workgroups an XCD runs at once share the cos/sin
+            // rows of their spans (and a head's neighbouring spans) while the group's K1,
+            // K2 and V still fit its L2: 98 against 132 MB fetched per call at w = 256
+            constexpr int G = 4;
+            const int nq = P.n_qtiles, full = nbh / G;
+            const int gl = G * nq;
+            const int g = lid / gl;
+            const int gs = g < full ? G : nbh - full * G;
+            const int rr = lid - g * gl;
+            x.qt = rr / gs;
+            x.bh = g * G + (rr - x.qt * gs);
+        } else {
+            x.bh = lid / P.n_qtiles;
+            x.qt = lid - x.bh * P.n_qtiles;
+        }
         const int q0 = x.qt * BM;
         const int q_last = min(L, q0 + BM) - 1;
         int k_lo = 0, k_hi = L;
