@@ -147,6 +147,25 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
     f32x16 o[2];
     float l, mx;
     float vsc = 1.0f;
+    // V item it -> keys 2p, 2p + 1 of the span and 8 values of d from 8 ch. Windowed and
+    // 128-key spans: consecutive lanes take consecutive 16-byte chunks of one key row (ch
+    // fastest), so that a wave's loads cover whole 128-byte rows instead of 16 bytes of
+    // each of 64 rows (samel_w17 6%, the 128-key graph calls 3.5% faster). A 256-key
+    // span takes pairs of chunks (two lanes per row, then p: 2%), since the transposing
+    // LDS writes of ch-fastest lanes share banks; a 64-key span keeps p fastest (its one
+    // item per thread measured 0.5-1.3% slower either way).
+    auto v_item = [](int it, int &p, int &ch) __attribute__((always_inline)) {
+        if constexpr (NKF == 64) {
+            p = it % (NK / 2);
+            ch = it / (NK / 2);
+        } else if constexpr (NKF == 256) {
+            p = (it >> 1) % (NK / 2);
+            ch = ((it >> 1) / (NK / 2)) * 2 + (it & 1);
+        } else {
+            p = it / 8;
+            ch = it % 8;
+        }
+    };
     auto compute = [&](auto safe_tag) __attribute__((always_inline)) {
         constexpr bool SAFE = decltype(safe_tag)::value;
         // The redo derives its lane values from an opaque copy of the thread id, so that the
@@ -214,7 +233,8 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
 #pragma unroll
         for (int i = 0; i < VC; ++i) {
             const int it = tid + NT * i;
-            const int p = it % (NK / 2), ch = it / (NK / 2);
+            int p, ch;
+            v_item(it, p, ch);
             const uint32_t off = (uint32_t)(ks0 + 2 * p) * vrb + (uint32_t)ch * 16;
             rawv[i][0] = bload(rv, off);
             rawv[i][1] = bload(rv, off + vrb);
@@ -243,7 +263,8 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
 #pragma unroll
         for (int i = 0; i < VC; ++i) {
             const int it = tid + NT * i;
-            const int p = it % (NK / 2), ch = it / (NK / 2);
+            int p, ch;
+            v_item(it, p, ch);
             // key positions inside each 16 carry bits 2 and 3 swapped (the P.V operand order)
             const int k2 = 2 * p;
             const int pos = (k2 & ~12) | ((k2 & 4) << 1) | ((k2 & 8) >> 1);
