@@ -147,24 +147,31 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
     f32x16 o[2];
     float l, mx;
     float vsc = 1.0f;
-    // V item it -> keys 2p, 2p + 1 of the span and 8 values of d from 8 ch. Windowed and
-    // 128-key spans: consecutive lanes take consecutive 16-byte chunks of one key row (ch
-    // fastest), so that a wave's loads cover whole 128-byte rows instead of 16 bytes of
-    // each of 64 rows (samel_w17 6%, the 128-key graph calls 3.5% faster). A 256-key
-    // span takes pairs of chunks (two lanes per row, then p: 2%), since the transposing
-    // LDS writes of ch-fastest lanes share banks; a 64-key span keeps p fastest (its one
-    // item per thread measured 0.5-1.3% slower either way).
+    // V item it -> keys 2p, 2p + 1 of the span and 8 values of d from 8 ch. Consecutive
+    // lanes take consecutive 16-byte chunks of one key row (ch fastest), so that a wave's
+    // loads cover whole 128-byte rows instead of 16 bytes of each of 64 rows (samel_w17 6%,
+    // the 128-key graph calls 3.5% faster); a 64-key span keeps p fastest (its one item per
+    // thread measured 0.5-1.3% slower either way).
     auto v_item = [](int it, int &p, int &ch) __attribute__((always_inline)) {
         if constexpr (NKF == 64) {
             p = it % (NK / 2);
             ch = it / (NK / 2);
-        } else if constexpr (NKF == 256) {
-            p = (it >> 1) % (NK / 2);
-            ch = ((it >> 1) / (NK / 2)) * 2 + (it & 1);
         } else {
             p = it / 8;
             ch = it % 8;
         }
+    };
+    // V^T element (row d, key position e) of the staged span. At a 256-key span the
+    // 16-byte chunk e / 8 of row d sits at chunk (e / 8) ^ ((d / 8) & 7): the transposing
+    // writes of one key row's chunks (lanes eight rows of V^T apart, whose rows' stride is
+    // a multiple of 128 bytes) then fall in different banks, and the P.V operand reads
+    // (rows of one 8-row group share the XOR) stay conflict-free; the 256-key graph calls
+    // 5% faster. Elsewhere the plain layout measured the same or better.
+    auto vt_off = [](int d, int e) __attribute__((always_inline)) {
+        if constexpr (NKF == 256)
+            return d * S::VS + ((((e >> 3) ^ (d >> 3)) & 7) | ((e >> 3) & ~7)) * 8 + (e & 7);
+        else
+            return d * S::VS + e;
     };
     auto compute = [&](auto safe_tag) __attribute__((always_inline)) {
         constexpr bool SAFE = decltype(safe_tag)::value;
@@ -283,7 +290,7 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
                 } else {
                     wv = (j & 1) ? __builtin_amdgcn_perm(wb, wa, 0x07060302u) : __builtin_amdgcn_perm(wb, wa, 0x05040100u);
                 }
-                *reinterpret_cast<uint32_t *>(Vt + (8 * ch + j) * S::VS + pos) = wv;
+                *reinterpret_cast<uint32_t *>(Vt + vt_off(8 * ch + j, pos)) = wv;
             }
         }
         __syncthreads();
@@ -353,7 +360,7 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
                 }
 #pragma unroll
                 for (int db = 0; db < 2; ++db) {
-                    const u32x4 va = lds16(Vt + (db * 32 + r) * S::VS + kb * 32 + 16 * tt + 8 * g);
+                    const u32x4 va = lds16(Vt + vt_off(db * 32 + r, kb * 32 + 16 * tt + 8 * g));
                     o[db] = mfma_pv(va, pk, o[db]);
                 }
             }
