@@ -216,10 +216,11 @@ int sa3attn_forward_general(const sa3attn_desc *desc, const sa3attn_strides *str
  *     otherwise when a key tile is visited by enough query tiles (query tiles of 256
  *     rows plain, 128 differential; full attention: ceil(L / rows) visits; a window of
  *     half-width w: about (2w + 64) / rows + 1): at least 3 at D = 128; at D = 64 at
- *     least 10 plain or 9 differential, except contiguous calls on grids of more tiles
- *     than compute units whose tiles span at most 32 key tiles (these run persistent):
- *     at least 12 plain or 9 differential there (256 compute units are assumed when no
- *     device is current); the shapes where it measured faster. SA3_PREP_ALWAYS whenever the call
+ *     least 10 plain or 18 differential, except on grids of more tiles than compute
+ *     units whose tiles span at most 32 key tiles (contiguous calls there run
+ *     persistent): at least 9 differential there, and 12 plain for contiguous calls
+ *     (256 compute units are assumed when no device is current); the shapes where it
+ *     measured faster. SA3_PREP_ALWAYS whenever the call
  *     takes the long-span kernel; SA3_PREP_NEVER never. SA3_PREP_ONLY enqueues the
  *     pre-pass alone (out is not written) and SA3_PREP_REUSE the attention kernel
  *     alone, reading a workspace that an earlier ALWAYS or ONLY call filled from the

@@ -235,8 +235,8 @@ def forward(q, k, v, cos, sin, *, window=-1, lam=0.0, scale=None, out=None, out_
     query tiles than compute units and at most two 64-row tiles per compute unit; on
     grids whose last round of query tiles fills at most half the compute units; and
     when each key tile is visited by enough query tiles: >= 3 at D = 128, at D = 64
-    >= 10 plain / 9 differential, or >= 12 / 9 on persistent window grids (see
-    include/sa3attn.h); "always"; "never"; "only": the pre-pass alone,
+    >= 10 plain / 18 differential, or >= 12 (contiguous) / 9 on persistent window
+    grids (see include/sa3attn.h); "always"; "never"; "only": the pre-pass alone,
     out not written; "reuse": the attention kernel alone on a workspace an "always" /
     "only" call filled from the same k, v, cos, sin); workspace: a uint8 GPU tensor of
     at least workspace_bytes(...) bytes, allocated here (torch's caching allocator, on

@@ -1189,8 +1189,10 @@ unsigned long long prep_bytes(const LaunchArgs &a) {
 //    instances spill.
 //  * D = 64, grids that run one round per tile (the pair steps): from about 10 visits
 //    plain (a 1024-key window, 10 visits: 8% faster; L = 2048 in one round, 8 visits:
-//    even) and 9 differential (L = 2048 in one round, 16 visits: 2.5% faster; L = 1024,
-//    8 visits: 8% slower), in one round or several.
+//    even) and 18 differential: once the fused 64-key blocks skipped the window tiles
+//    outside a wave's rows, they won the one-round differential windows up to ~17 visits
+//    (B=1 H=8 L=4096: 10 visits 12% faster than the pre-pass, 14 visits 3.5%, 18 even;
+//    26 visits and full attention, 32, 6-10% slower), in one round or several.
 //  * D = 64 persistent grids (windows whose tiles span <= 32 key tiles): from 12 visits
 //    plain and 9 differential (plain 768-key window, 8 visits: 1% slower; differential
 //    1024-key window, 10 visits: 1% faster, 1536: 5% faster; 256, 6 visits: 7% slower).
@@ -1205,8 +1207,12 @@ bool prep_pays(const LaunchArgs &a) {
     const long long n_qtiles = ((long long)a.L + bm - 1) / bm;
     const long long visits = a.window < 0 ? n_qtiles : std::min(n_qtiles, (2ll * a.window + BN + bm - 1) / bm + 1);
     if (a.D == 128) return visits >= 3;
-    if (persistent_shape(a) && a.contig) return visits >= (a.diff ? 9 : 12);
-    return visits >= (a.diff ? 9 : 10);
+    // A workspace query does not know the strides (contig is 0 there), so for a shape that
+    // runs persistent when contiguous the answer must cover the contiguous call: the
+    // differential threshold is the persistent one whatever the strides, and the plain
+    // one for strided calls (10) is below the persistent one (12).
+    if (persistent_shape(a)) return visits >= (a.diff ? 9 : a.contig ? 12 : 10);
+    return visits >= (a.diff ? 18 : 10);
 }
 
 int launch_forward(const LaunchArgs &a) {

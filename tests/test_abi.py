@@ -332,7 +332,7 @@ def _tail_bytes(B, H, L, D=64, differential=0, window=-1, n_cu=256):
 
 @pytest.mark.parametrize("kw,policy,want", [
     # AUTO (256 compute units assumed without a device): key tiles visited by >= 10
-    # query tiles of 256 rows (plain) / 9 of 128 (differential), >= 12 / 9 on persistent
+    # query tiles of 256 rows (plain) / 18 of 128 (differential), >= 12 / 9 on persistent
     # grids, >= 3 at D = 128; small grids and split tails always
     (dict(B=2, H=24, L=4096), AUTO, 2 * 2 * 24 * 4096 * 64 * 2),
     (dict(B=1, H=24, L=2816), AUTO, 2 * 24 * _lp(2816) * 64 * 2),        # 11 visits, but 264 WGs: split tail
@@ -352,7 +352,9 @@ def _tail_bytes(B, H, L, D=64, differential=0, window=-1, n_cu=256):
     (dict(B=1, H=24, L=384, D=128), AUTO, 0),                            # D = 128, 2 visits
     (dict(B=1, H=32, L=1024, differential=1), AUTO, 0),                  # 8 visits
     (dict(B=1, H=32, L=1025, differential=1), AUTO, 3 * 32 * _lp(1025) * 64 * 2),   # 9, 288 WGs
-    (dict(B=1, H=16, L=2048, differential=1), AUTO, 3 * 16 * 2048 * 64 * 2),   # 16 visits, one round
+    (dict(B=1, H=16, L=2048, differential=1), AUTO, 0),                  # 16 visits, one round
+    (dict(B=1, H=8, L=4608, differential=1), AUTO, 3 * 8 * _lp(4608) * 64 * 2),   # 36 visits, 288 WGs: tail
+    (dict(B=1, H=8, L=4096, window=1024, differential=1), AUTO, 3 * 8 * 4096 * 64 * 2),   # 18 visits, one round
     (dict(B=1, H=16, L=2049, differential=1), AUTO, 3 * 16 * _lp(2049) * 64 * 2),   # 17, 272 WGs
     # D = 128: the same 256 / 128 rows per query tile
     (dict(B=1, H=24, L=2816, D=128), AUTO, 2 * 24 * _lp(2816) * 128 * 2),   # split tail
