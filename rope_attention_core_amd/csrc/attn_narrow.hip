@@ -20,7 +20,9 @@
 //    the same 32 rows with its own exact maximum, row sum and O, and the shares are
 //    merged through LDS at the end (O = sum of 2^(m_w - M) O_w, l likewise, M the
 //    largest m_w). A 256-key sequence then runs 8 query tiles per head instead of 2,
-//    which fills 4x more CUs.
+//    which fills 4x more CUs. The four waves' common 32 query rows are loaded and
+//    rotated once per workgroup (one chunk per thread, whole rows per wave load) into
+//    LDS, from which each wave reads its B operands.
 //  * Differential: waves w and w + 2 share 32 rows, one softmax branch each (BM = 64),
 //    windowed span 128 keys; the second branch hands O2 / l2 to the first through LDS.
 //  * Arithmetic per element is the long-span kernel's: RoPE in FP32 with separate
@@ -83,7 +85,15 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
     static_assert(NKB % KSPLIT == 0, "key split");
     // the merge of the key shares reuses the staging area: NT / 64 waves x 34 rows of 64 floats
     constexpr int MERGE_ELEMS = KSPLIT > 1 ? (NT / 64) * 34 * 64 * 2 : 0;
-    constexpr int SMEM_ELEMS = S::LDS_ELEMS > MERGE_ELEMS ? S::LDS_ELEMS : MERGE_ELEMS;
+    // QCOOP: short sequences split over the waves (all four on the same 32 query rows)
+    // load and rotate those rows once per workgroup, one 16-byte chunk per thread with
+    // whole rows per wave, into LDS after the span (QS-element rows), and each wave reads
+    // its B operands from there
+    constexpr bool QCOOP = KSPLIT > 1 && CONTIG;
+    constexpr int QS = 72;
+    constexpr int Q_ELEMS = QCOOP ? 32 * QS : 0;
+    static_assert(!QCOOP || NT == 32 * 8, "one Q chunk per thread");
+    constexpr int SMEM_ELEMS = S::LDS_ELEMS + Q_ELEMS > MERGE_ELEMS ? S::LDS_ELEMS + Q_ELEMS : MERGE_ELEMS;
     constexpr int KC = NK * 8 / NT;          // K chunks (8 elements) per thread per branch
     constexpr int VC = NK * 4 / NT;          // V items (2 keys x 8 d) per thread
     static_assert(NK * 8 % NT == 0 && NK * 4 % NT == 0, "staging split");
@@ -187,7 +197,12 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
         u32x4 qreg[4];
         const uint32_t qsign = P.neg_scale ? 0x80008000u : 0u;
         u32x4 rq_raw[4], rqc[4], rqs[4];
-        {
+        if constexpr (QCOOP) {
+            const uint32_t row = (uint32_t)(qw + tid / 8), col = (uint32_t)(tid % 8) * 16;
+            rq_raw[0] = bload(rq, row * qrb + col);
+            rqc[0] = bload(rc, row * ROWB + col);
+            rqs[0] = bload(rs, row * ROWB + col);
+        } else {
             const uint32_t row = (uint32_t)(qw + r);
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
@@ -248,7 +263,10 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
         }
 
         // ---- rotate Q into registers; rotate / transpose the span into LDS ---------------
-        if constexpr (CONTIG) {
+        if constexpr (QCOOP) {
+            *reinterpret_cast<u32x4 *>(smem + S::LDS_ELEMS + (tid / 8) * QS + (tid % 8) * 8) =
+                rope8<IO>(rq_raw[0], rqc[0], rqs[0]) ^ qsign;
+        } else if constexpr (CONTIG) {
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) qreg[ks] = rope8<IO>(rq_raw[ks], rqc[ks], rqs[ks]) ^ qsign;
         }
@@ -294,6 +312,10 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
             }
         }
         __syncthreads();
+        if constexpr (QCOOP) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) qreg[ks] = lds16(smem + S::LDS_ELEMS + r * QS + 16 * ks + 8 * g);
+        }
 
         // ---- scores of this wave's 32 rows over the span: S^T blocks of 32 keys ----------
         const uint16_t *Ks = smem + wbr * S::K_ELEMS;
