@@ -14,7 +14,10 @@
 // rescale), and P.V, and stores. Small workgroups and a small
 // LDS footprint keep several of them resident per CU so that their loads overlap.
 //
-//  * Plain, windowed: 4 waves x 32 query rows (BM = 128); span 192 keys.
+//  * Plain, windowed: 4 waves x 32 query rows (BM = 128); span 192 keys. The
+//    workgroup's Q rows (each branch) are loaded with whole rows per wave load and
+//    rotated once into LDS, where each wave reads its B operands before the span is
+//    staged over them.
 //  * Plain, short sequence of 65..256 keys: the waves split the span instead of the
 //    rows (KSPLIT = 4), BM = 32: each wave takes its share of the keys for
 //    the same 32 rows with its own exact maximum, row sum and O, and the shares are
@@ -90,9 +93,11 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
     // whole rows per wave, into LDS after the span (QS-element rows), and each wave reads
     // its B operands from there
     constexpr bool QCOOP = KSPLIT > 1 && CONTIG;
+    constexpr bool QWIN = NKF == 0 && CONTIG;
     constexpr int QS = 72;
     constexpr int Q_ELEMS = QCOOP ? 32 * QS : 0;
     static_assert(!QCOOP || NT == 32 * 8, "one Q chunk per thread");
+    static_assert(!QWIN || (BM * 8 % NT == 0 && NBS * BM * QS <= NBS * S::K_ELEMS), "Q rows in the K area");
     constexpr int SMEM_ELEMS = S::LDS_ELEMS + Q_ELEMS > MERGE_ELEMS ? S::LDS_ELEMS + Q_ELEMS : MERGE_ELEMS;
     constexpr int KC = NK * 8 / NT;          // K chunks (8 elements) per thread per branch
     constexpr int VC = NK * 4 / NT;          // V items (2 keys x 8 d) per thread
@@ -197,7 +202,26 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
         u32x4 qreg[4];
         const uint32_t qsign = P.neg_scale ? 0x80008000u : 0u;
         u32x4 rq_raw[4], rqc[4], rqs[4];
-        if constexpr (QCOOP) {
+        // QWIN: windowed workgroups (each wave its own 32 rows of one branch) load their Q
+        // rows once for the workgroup with whole rows per wave load (one (row, chunk) of both
+        // branches per thread and item), rotate them into LDS at the start of the K area,
+        // and each wave reads its B operands from there before the span is staged over it
+        constexpr int QN = QWIN ? BM * 8 / NT : 1;
+        u32x4 wq_raw[QN][NBS], wq_c[QN], wq_s[QN];
+        if constexpr (QWIN) {
+#pragma unroll
+            for (int i = 0; i < QN; ++i) {
+                const int m = tid + NT * i;
+                const uint32_t row = (uint32_t)(q0 + m / 8), col = (uint32_t)(m % 8) * 16;
+#pragma unroll
+                for (int br = 0; br < NBS; ++br) {
+                    const rsrc_t rqb = slab_rsrc(P.q, br * qbr + slab, qrb, L);
+                    wq_raw[i][br] = bload(rqb, row * qrb + col);
+                }
+                wq_c[i] = bload(rc, row * ROWB + col);
+                wq_s[i] = bload(rs, row * ROWB + col);
+            }
+        } else if constexpr (QCOOP) {
             const uint32_t row = (uint32_t)(qw + tid / 8), col = (uint32_t)(tid % 8) * 16;
             rq_raw[0] = bload(rq, row * qrb + col);
             rqc[0] = bload(rc, row * ROWB + col);
@@ -263,7 +287,20 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
         }
 
         // ---- rotate Q into registers; rotate / transpose the span into LDS ---------------
-        if constexpr (QCOOP) {
+        if constexpr (QWIN) {
+#pragma unroll
+            for (int i = 0; i < QN; ++i) {
+                const int m = tid + NT * i;
+#pragma unroll
+                for (int br = 0; br < NBS; ++br)
+                    *reinterpret_cast<u32x4 *>(smem + (br * BM + m / 8) * QS + (m % 8) * 8) =
+                        rope8<IO>(wq_raw[i][br], wq_c[i], wq_s[i]) ^ qsign;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) qreg[ks] = lds16(smem + (wbr * BM + wq * 32 + r) * QS + 16 * ks + 8 * g);
+            __syncthreads();   // every wave has its Q before the span is staged over it
+        } else if constexpr (QCOOP) {
             *reinterpret_cast<u32x4 *>(smem + S::LDS_ELEMS + (tid / 8) * QS + (tid % 8) * 8) =
                 rope8<IO>(rq_raw[0], rqc[0], rqs[0]) ^ qsign;
         } else if constexpr (CONTIG) {
