@@ -89,14 +89,21 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(Params P) {
     const uint32_t qsign = P.neg_scale ? 0x80008000u : 0u;
 
     // Q rotated into registers (MFMA B-operand layout)
-    u32x4 qreg[NKS];
-    {
-        const uint32_t row = (uint32_t)(qw + r);
+    // The tile's 64 query rows are loaded once for the workgroup (both key halves use
+    // them), two 16-byte chunks per thread with whole rows per wave load; they are
+    // rotated into LDS (the first K buffer, before the first tile is staged there) once
+    // the first tiles' loads are in flight, and each wave reads its B operands from there.
+    constexpr int QS = KSTR;                     // LDS row stride of the rotated Q rows
+    constexpr int QCH = 64 * (D / 8) / NT;       // Q chunks per thread
+    static_assert(QCH == 2 && 64 * QS <= KS_ELEMS, "Q rows in one K buffer");
+    u32x4 qreg[NKS], qraw[QCH], qcos[QCH], qsin[QCH];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            const uint32_t off = row * RB + (uint32_t)(16 * ks + 8 * g) * 2;
-            qreg[ks] = rope8<IO>(bload(rq, off), bload(rc, off), bload(rs, off)) ^ qsign;
-        }
+    for (int i = 0; i < QCH; ++i) {
+        const int m = tid + NT * i;
+        const uint32_t off = (uint32_t)(qt * 64 + m / 8) * RB + (uint32_t)(m % 8) * 16;
+        qraw[i] = bload(rq, off);
+        qcos[i] = bload(rc, off);
+        qsin[i] = bload(rs, off);
     }
 
     // ---- staging: both halves' tiles of one step ------------------------------------
@@ -261,6 +268,17 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(Params P) {
         m = NEG_INF;
         load_k(0);
         load_v(0, safe_tag);
+        if constexpr (!decltype(safe_tag)::value) {
+#pragma unroll
+            for (int i = 0; i < QCH; ++i) {
+                const int m = tid + NT * i;
+                *reinterpret_cast<u32x4 *>(smem + (m / 8) * QS + (m % 8) * 8) = rope8<IO>(qraw[i], qcos[i], qsin[i]) ^ qsign;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) qreg[ks] = lds16(smem + (qb * 32 + r) * QS + 16 * ks + 8 * g);
+            __syncthreads();   // every wave has its Q before K(0) is staged over it
+        }
         stage_k(0);
         stage_v(0, safe_tag);
         load_k(1);
