@@ -22,7 +22,7 @@
 //    rows (KSPLIT = 4), BM = 32: each wave takes its share of the keys for
 //    the same 32 rows with its own exact maximum, row sum and O, and the shares are
 //    merged through LDS at the end (O = sum of 2^(m_w - M) O_w, l likewise, M the
-//    largest m_w). A 256-key sequence then runs 8 query tiles per head instead of 2,
+//    largest m_w), each wave merging and storing a quarter of the O elements. A 256-key sequence then runs 8 query tiles per head instead of 2,
 //    which fills 4x more CUs. The four waves' common 32 query rows are loaded and
 //    rotated once per workgroup (one chunk per thread, whole rows per wave load) into
 //    LDS, from which each wave reads its B operands.
@@ -452,45 +452,67 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
     }
 
     if constexpr (KSPLIT > 1) {
-        // merge the shares of one query block: wave wq * KSPLIT (kq = 0) takes
-        // O = sum_w 2^(b_w - B) O_w and l = sum_w 2^(b_w - B) l_w with b_w = m_w c its
-        // base (log2 units, -inf for a share with no valid key) and B the largest b_w.
-        // Partial of wave v in rows of 64 floats (one per lane): O element e in row
-        // v * 32 + e, b in row NW * 32 + v, l in row NW * 33 + v (NW * 34 rows).
-        constexpr int NW = NT / 64;
+        // Merge the shares of the query block: O = sum_v 2^(b_v - B) O_v and l likewise,
+        // b_v = m_v c the base of share v (log2 units, -inf for a share with no valid key)
+        // and B the largest b_v, summed in share order. Every wave writes its share to LDS
+        // in rows of 64 floats (one per lane: O element e in row v * 34 + e, b in row
+        // v * 34 + 32, l in row v * 34 + 33), then wave kq merges, normalises and stores
+        // the O elements 8 kq .. 8 kq + 7 of its lanes (one 32-column d block half), so
+        // the four waves share the merge and the stores.
+        static_assert(WPB == 1 && KSPLIT == NT / 64 && KSPLIT == 4, "one query block, four shares");
         float *pb = reinterpret_cast<float *>(smem);
         const float base = (mx == NEG_INF) ? NEG_INF : mx * c;
         __syncthreads();   // every wave is done with the staged span
-        if (kq != 0) {
-#pragma unroll
-            for (int db = 0; db < 2; ++db)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) pb[(wave * 32 + db * 16 + i) * 64 + lane] = o[db][i];
-            pb[(NW * 32 + wave) * 64 + lane] = base;
-            pb[(NW * 33 + wave) * 64 + lane] = l;
-        }
-        __syncthreads();
-        if (kq != 0) return;
-        float bmax = base;
-#pragma unroll
-        for (int v = 1; v < KSPLIT; ++v) bmax = fmaxf(bmax, pb[(NW * 32 + wave + v) * 64 + lane]);
-        // rows past L have no valid key in any share (bmax = -inf); they are not stored
-        const float w0 = __builtin_amdgcn_exp2f(base - bmax);
-        l *= w0;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) o[db][i] *= w0;
+            for (int i = 0; i < 16; ++i) pb[(wave * 34 + db * 16 + i) * 64 + lane] = o[db][i];
+        pb[(wave * 34 + 32) * 64 + lane] = base;
+        pb[(wave * 34 + 33) * 64 + lane] = l;
+        __syncthreads();
+        float bv[KSPLIT];
+#pragma unroll
+        for (int v = 0; v < KSPLIT; ++v) bv[v] = pb[(v * 34 + 32) * 64 + lane];
+        float bmax = bv[0];
+#pragma unroll
+        for (int v = 1; v < KSPLIT; ++v) bmax = fmaxf(bmax, bv[v]);
+        // rows past L have no valid key in any share (bmax = -inf); they are not stored
+        float om[8];
+        {
+            const float w0 = __builtin_amdgcn_exp2f(bv[0] - bmax);
+            l = pb[33 * 64 + lane] * w0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) om[j] = pb[(8 * kq + j) * 64 + lane] * w0;
+        }
 #pragma unroll
         for (int v = 1; v < KSPLIT; ++v) {
-            const float wv = __builtin_amdgcn_exp2f(pb[(NW * 32 + wave + v) * 64 + lane] - bmax);
-            l = __builtin_fmaf(wv, pb[(NW * 33 + wave + v) * 64 + lane], l);
+            const float wv = __builtin_amdgcn_exp2f(bv[v] - bmax);
+            l = __builtin_fmaf(wv, pb[(v * 34 + 33) * 64 + lane], l);
 #pragma unroll
-            for (int db = 0; db < 2; ++db)
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    o[db][i] = __builtin_fmaf(wv, pb[((wave + v) * 32 + db * 16 + i) * 64 + lane], o[db][i]);
+            for (int j = 0; j < 8; ++j) om[j] = __builtin_fmaf(wv, pb[(v * 34 + 8 * kq + j) * 64 + lane], om[j]);
         }
+        if (qi >= L) return;
+        // (2^vshift undoes the guard's scaling of V; l >= 1, so inv * 2^vshift stays finite)
+        const float inv = (1.0f / l) * exp2i(vshift);
+        const long long row = CONTIG ? slab + (long long)qi * HD : bb * P.ob + hh * P.oh + (long long)qi * P.ol;
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg) {
+            float y[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) y[j] = om[gg * 4 + j] * inv;
+            // accumulator elements 8 kq + 4 gg .. +3: d block kq / 2, group 2 (kq % 2) + gg
+            const int d = (kq >> 1) * 32 + (2 * (kq & 1) + gg) * 8 + g * 4;
+            if (P.out_dtype == OUT_F32) {
+                *reinterpret_cast<f32x4 *>(static_cast<float *>(P.out) + row + d) = f32x4{y[0], y[1], y[2], y[3]};
+            } else if (P.out_dtype == OUT_BF16) {
+                *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(P.out) + row + d) =
+                    u32x2{pack2<IO_BF16>(y[0], y[1]), pack2<IO_BF16>(y[2], y[3])};
+            } else {
+                *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(P.out) + row + d) =
+                    u32x2{pack2<IO_F16>(y[0], y[1]), pack2<IO_F16>(y[2], y[3])};
+            }
+        }
+        return;
     }
 
     // ---- epilogue: normalise, subtract, cast, store rows < L -------------------------
