@@ -19,13 +19,15 @@
 //    rotated once into LDS, where each wave reads its B operands before the span is
 //    staged over them.
 //  * Plain, short sequence of 65..256 keys: the waves split the span instead of the
-//    rows (KSPLIT = 4), BM = 32: each wave takes its share of the keys for
-//    the same 32 rows with its own exact maximum, row sum and O, and the shares are
-//    merged through LDS at the end (O = sum of 2^(m_w - M) O_w, l likewise, M the
-//    largest m_w), each wave merging and storing a quarter of the O elements. A 256-key sequence then runs 8 query tiles per head instead of 2,
-//    which fills 4x more CUs. The four waves' common 32 query rows are loaded and
-//    rotated once per workgroup (one chunk per thread, whole rows per wave load) into
-//    LDS, from which each wave reads its B operands.
+//    rows (KSPLIT = 4 waves of 32 keys at 128 keys, 8 waves of 32 keys at 256), BM = 32:
+//    each wave takes its share of the keys for the same 32 rows with its own exact
+//    maximum, row sum and O, and the shares are merged through LDS at the end
+//    (O = sum of 2^(m_w - M) O_w, l likewise, M the largest m_w), each wave merging and
+//    storing its part of the O elements. A 256-key sequence then runs 8 query tiles per
+//    head instead of 2, which fills 4x more CUs. The waves' common 32 query rows are
+//    loaded and rotated once per workgroup (one chunk per thread of the first four
+//    waves, whole rows per wave load) into LDS, from which each wave reads its B
+//    operands.
 //  * Differential: waves w and w + 2 share 32 rows, one softmax branch each (BM = 64),
 //    windowed span 128 keys; the second branch hands O2 / l2 to the first through LDS.
 //  * Arithmetic per element is the long-span kernel's: RoPE in FP32 with separate
@@ -52,12 +54,15 @@ namespace {
 // banks without the padding.
 template <bool DIFF, int NKF>
 struct NarrowShape {
-    static constexpr int NT = 256;                    // threads (4 waves)
+    // threads: 4 waves, or 8 for the plain 256-key span (one 32-key share each: twice the
+    // threads for its staging, which with one wave per SIMD was issue-bound)
+    static constexpr bool W8 = !DIFF && NKF == 256;
+    static constexpr int NT = W8 ? 512 : 256;
     static constexpr int NBS = DIFF ? 2 : 1;          // branches staged
     // waves per query block: a 64-key span (L <= 64) is one query tile either way, so
     // splitting it would only add the merge
-    static constexpr int KSPLIT = (DIFF || NKF == 0 || NKF == 64) ? 1 : 4;
-    static constexpr int WPB = DIFF ? 2 : 4 / KSPLIT; // query blocks per branch
+    static constexpr int KSPLIT = (DIFF || NKF == 0 || NKF == 64) ? 1 : NT / 64;
+    static constexpr int WPB = DIFF ? 2 : (NT / 64) / KSPLIT; // query blocks per branch
     static constexpr int BM = WPB * 32;               // query rows per workgroup
     static constexpr int NK = NKF ? NKF : BM + 64;    // keys staged
     static constexpr int NKB = NK / 32;               // 32-key blocks
@@ -70,12 +75,13 @@ struct NarrowShape {
 };
 
 // Windowed mode keeps registers <= 168 so that three workgroups share a CU (their LDS
-// fits too); short-sequence mode and the general instances may use up to 256, and the
-// 256-key span of the differential or general instances up to 512.
+// fits too); short-sequence mode and the general instances may use up to 256; the
+// 256-key span runs one workgroup per CU (up to 512 registers for the 4-wave
+// differential one, 256 for the 8-wave plain one).
 // CONTIG: contiguous [B][H][L][64] tensors (q, k stacked [2][...]); the row strides
 // are then compile-time constants.
 template <int IO, bool DIFF, int NKF, bool CONTIG>
-__global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTIG && !NKF) ? 3 : 2) void attn_narrow_kernel(Params P) {
+__global__ __launch_bounds__((NarrowShape<DIFF, NKF>::NT), (NKF == 256) ? 1 : (CONTIG && !NKF) ? 3 : 2) void attn_narrow_kernel(Params P) {
     using S = NarrowShape<DIFF, NKF>;
     constexpr int NT = S::NT, NBS = S::NBS, WPB = S::WPB, BM = S::BM, NK = S::NK, NKB = S::NKB;
     constexpr int KSPLIT = S::KSPLIT;
@@ -88,15 +94,15 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
     static_assert(NKB % KSPLIT == 0, "key split");
     // the merge of the key shares reuses the staging area: NT / 64 waves x 34 rows of 64 floats
     constexpr int MERGE_ELEMS = KSPLIT > 1 ? (NT / 64) * 34 * 64 * 2 : 0;
-    // QCOOP: short sequences split over the waves (all four on the same 32 query rows)
-    // load and rotate those rows once per workgroup, one 16-byte chunk per thread with
-    // whole rows per wave, into LDS after the span (QS-element rows), and each wave reads
-    // its B operands from there
+    // QCOOP: short sequences split over the waves (all on the same 32 query rows) load
+    // and rotate those rows once per workgroup, one 16-byte chunk per thread of the first
+    // four waves with whole rows per wave, into LDS after the span (QS-element rows), and
+    // each wave reads its B operands from there
     constexpr bool QCOOP = KSPLIT > 1 && CONTIG;
     constexpr bool QWIN = NKF == 0 && CONTIG;
     constexpr int QS = 72;
     constexpr int Q_ELEMS = QCOOP ? 32 * QS : 0;
-    static_assert(!QCOOP || NT == 32 * 8, "one Q chunk per thread");
+    static_assert(!QCOOP || NT >= 32 * 8, "at most one Q chunk per thread");
     static_assert(!QWIN || (BM * 8 % NT == 0 && NBS * BM * QS <= NBS * S::K_ELEMS), "Q rows in the K area");
     constexpr int SMEM_ELEMS = S::LDS_ELEMS + Q_ELEMS > MERGE_ELEMS ? S::LDS_ELEMS + Q_ELEMS : MERGE_ELEMS;
     constexpr int KC = NK * 8 / NT;          // K chunks (8 elements) per thread per branch
@@ -222,10 +228,13 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
                 wq_s[i] = bload(rs, row * ROWB + col);
             }
         } else if constexpr (QCOOP) {
-            const uint32_t row = (uint32_t)(qw + tid / 8), col = (uint32_t)(tid % 8) * 16;
-            rq_raw[0] = bload(rq, row * qrb + col);
-            rqc[0] = bload(rc, row * ROWB + col);
-            rqs[0] = bload(rs, row * ROWB + col);
+            // the first 256 threads (waves 0-3) hold the 32 rows' 256 chunks
+            if (NT == 32 * 8 || tid < 32 * 8) {
+                const uint32_t row = (uint32_t)(qw + tid / 8), col = (uint32_t)(tid % 8) * 16;
+                rq_raw[0] = bload(rq, row * qrb + col);
+                rqc[0] = bload(rc, row * ROWB + col);
+                rqs[0] = bload(rs, row * ROWB + col);
+            }
         } else {
             const uint32_t row = (uint32_t)(qw + r);
 #pragma unroll
@@ -301,8 +310,9 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
             for (int ks = 0; ks < 4; ++ks) qreg[ks] = lds16(smem + (wbr * BM + wq * 32 + r) * QS + 16 * ks + 8 * g);
             __syncthreads();   // every wave has its Q before the span is staged over it
         } else if constexpr (QCOOP) {
-            *reinterpret_cast<u32x4 *>(smem + S::LDS_ELEMS + (tid / 8) * QS + (tid % 8) * 8) =
-                rope8<IO>(rq_raw[0], rqc[0], rqs[0]) ^ qsign;
+            if (NT == 32 * 8 || tid < 32 * 8)
+                *reinterpret_cast<u32x4 *>(smem + S::LDS_ELEMS + (tid / 8) * QS + (tid % 8) * 8) =
+                    rope8<IO>(rq_raw[0], rqc[0], rqs[0]) ^ qsign;
         } else if constexpr (CONTIG) {
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) qreg[ks] = rope8<IO>(rq_raw[ks], rqc[ks], rqs[ks]) ^ qsign;
@@ -457,51 +467,54 @@ __global__ __launch_bounds__(256, (NKF == 256 && (DIFF || !CONTIG)) ? 1 : (CONTI
         // and B the largest b_v, summed in share order. Every wave writes its share to LDS
         // in rows of 64 floats (one per lane: O element e in row v * 34 + e, b in row
         // v * 34 + 32, l in row v * 34 + 33), then wave kq merges, normalises and stores
-        // the O elements 8 kq .. 8 kq + 7 of its lanes (one 32-column d block half), so
-        // the four waves share the merge and the stores.
-        static_assert(WPB == 1 && KSPLIT == NT / 64 && KSPLIT == 4, "one query block, four shares");
+        // the O elements E kq .. E kq + E - 1 of its lanes (E = 32 / KSPLIT), so the
+        // waves share the merge and the stores.
+        static_assert(WPB == 1 && KSPLIT == NT / 64 && (KSPLIT == 4 || KSPLIT == 8), "one query block, one share per wave");
+        constexpr int E = 32 / KSPLIT;           // O elements a wave merges and stores
+        constexpr int SR = 34;                   // rows of 64 floats per share
         float *pb = reinterpret_cast<float *>(smem);
         const float base = (mx == NEG_INF) ? NEG_INF : mx * c;
         __syncthreads();   // every wave is done with the staged span
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) pb[(wave * 34 + db * 16 + i) * 64 + lane] = o[db][i];
-        pb[(wave * 34 + 32) * 64 + lane] = base;
-        pb[(wave * 34 + 33) * 64 + lane] = l;
+            for (int i = 0; i < 16; ++i) pb[(wave * SR + db * 16 + i) * 64 + lane] = o[db][i];
+        pb[(wave * SR + 32) * 64 + lane] = base;
+        pb[(wave * SR + 33) * 64 + lane] = l;
         __syncthreads();
         float bv[KSPLIT];
 #pragma unroll
-        for (int v = 0; v < KSPLIT; ++v) bv[v] = pb[(v * 34 + 32) * 64 + lane];
+        for (int v = 0; v < KSPLIT; ++v) bv[v] = pb[(v * SR + 32) * 64 + lane];
         float bmax = bv[0];
 #pragma unroll
         for (int v = 1; v < KSPLIT; ++v) bmax = fmaxf(bmax, bv[v]);
         // rows past L have no valid key in any share (bmax = -inf); they are not stored
-        float om[8];
+        float om[E];
         {
             const float w0 = __builtin_amdgcn_exp2f(bv[0] - bmax);
             l = pb[33 * 64 + lane] * w0;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) om[j] = pb[(8 * kq + j) * 64 + lane] * w0;
+            for (int j = 0; j < E; ++j) om[j] = pb[(E * kq + j) * 64 + lane] * w0;
         }
 #pragma unroll
         for (int v = 1; v < KSPLIT; ++v) {
             const float wv = __builtin_amdgcn_exp2f(bv[v] - bmax);
-            l = __builtin_fmaf(wv, pb[(v * 34 + 33) * 64 + lane], l);
+            l = __builtin_fmaf(wv, pb[(v * SR + 33) * 64 + lane], l);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) om[j] = __builtin_fmaf(wv, pb[(v * 34 + 8 * kq + j) * 64 + lane], om[j]);
+            for (int j = 0; j < E; ++j) om[j] = __builtin_fmaf(wv, pb[(v * SR + E * kq + j) * 64 + lane], om[j]);
         }
         if (qi >= L) return;
         // (2^vshift undoes the guard's scaling of V; l >= 1, so inv * 2^vshift stays finite)
         const float inv = (1.0f / l) * exp2i(vshift);
         const long long row = CONTIG ? slab + (long long)qi * HD : bb * P.ob + hh * P.oh + (long long)qi * P.ol;
 #pragma unroll
-        for (int gg = 0; gg < 2; ++gg) {
+        for (int gg = 0; gg < E / 4; ++gg) {
             float y[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) y[j] = om[gg * 4 + j] * inv;
-            // accumulator elements 8 kq + 4 gg .. +3: d block kq / 2, group 2 (kq % 2) + gg
-            const int d = (kq >> 1) * 32 + (2 * (kq & 1) + gg) * 8 + g * 4;
+            // accumulator elements e0 .. e0 + 3 (e0 = E kq + 4 gg): d block e0 / 16, group (e0 % 16) / 4
+            const int e0 = E * kq + 4 * gg;
+            const int d = (e0 >> 4) * 32 + ((e0 & 15) >> 2) * 8 + g * 4;
             if (P.out_dtype == OUT_F32) {
                 *reinterpret_cast<f32x4 *>(static_cast<float *>(P.out) + row + d) = f32x4{y[0], y[1], y[2], y[3]};
             } else if (P.out_dtype == OUT_BF16) {
