@@ -18,16 +18,15 @@
 //    workgroup's Q rows (each branch) are loaded with whole rows per wave load and
 //    rotated once into LDS, where each wave reads its B operands before the span is
 //    staged over them.
-//  * Plain, short sequence of 65..256 keys: the waves split the span instead of the
-//    rows (KSPLIT = 4 waves of 32 keys at 128 keys, 8 waves of 32 keys at 256), BM = 32:
-//    each wave takes its share of the keys for the same 32 rows with its own exact
-//    maximum, row sum and O, and the shares are merged through LDS at the end
-//    (O = sum of 2^(m_w - M) O_w, l likewise, M the largest m_w), each wave merging and
-//    storing its part of the O elements. A 256-key sequence then runs 8 query tiles per
-//    head instead of 2, which fills 4x more CUs. The waves' common 32 query rows are
-//    loaded and rotated once per workgroup (one chunk per thread of the first four
-//    waves, whole rows per wave load) into LDS, from which each wave reads its B
-//    operands.
+//  * Plain, short sequence: the waves split the span instead of the rows, each taking
+//    32 of its keys (KSPLIT = 2 waves per 32-row block at 64 keys, BM = 64; 4 waves at
+//    128 keys and 8 waves at 256, BM = 32): each wave takes its share of the keys for
+//    its block's 32 rows with its own exact maximum, row sum and O, and the shares are
+//    merged through LDS at the end (O = sum of 2^(m_w - M) O_w, l likewise, M the
+//    largest m_w), each wave merging and storing its part of the O elements. A 256-key
+//    sequence then runs 8 query tiles per head instead of 2, which fills 4x more CUs.
+//    The workgroup's query rows are loaded and rotated once (whole rows per wave load)
+//    into LDS, from which each wave reads its B operands.
 //  * Differential: waves w and w + 2 share 32 rows, one softmax branch each (BM = 64),
 //    windowed span 128 keys; the second branch hands O2 / l2 to the first through LDS.
 //  * Arithmetic per element is the long-span kernel's: RoPE in FP32 with separate
@@ -59,9 +58,8 @@ struct NarrowShape {
     static constexpr bool W8 = !DIFF && NKF == 256;
     static constexpr int NT = W8 ? 512 : 256;
     static constexpr int NBS = DIFF ? 2 : 1;          // branches staged
-    // waves per query block: a 64-key span (L <= 64) is one query tile either way, so
-    // splitting it would only add the merge
-    static constexpr int KSPLIT = (DIFF || NKF == 0 || NKF == 64) ? 1 : NT / 64;
+    // waves per 32-row query block (one 32-key share each)
+    static constexpr int KSPLIT = (DIFF || NKF == 0) ? 1 : NKF == 64 ? 2 : NT / 64;
     static constexpr int WPB = DIFF ? 2 : (NT / 64) / KSPLIT; // query blocks per branch
     static constexpr int BM = WPB * 32;               // query rows per workgroup
     static constexpr int NK = NKF ? NKF : BM + 64;    // keys staged
@@ -94,15 +92,16 @@ __global__ __launch_bounds__((NarrowShape<DIFF, NKF>::NT), (NKF == 256) ? 1 : (C
     static_assert(NKB % KSPLIT == 0, "key split");
     // the merge of the key shares reuses the staging area: NT / 64 waves x 34 rows of 64 floats
     constexpr int MERGE_ELEMS = KSPLIT > 1 ? (NT / 64) * 34 * 64 * 2 : 0;
-    // QCOOP: short sequences split over the waves (all on the same 32 query rows) load
-    // and rotate those rows once per workgroup, one 16-byte chunk per thread of the first
-    // four waves with whole rows per wave, into LDS after the span (QS-element rows), and
+    // QCOOP: short sequences split over the waves (several waves on the same 32 query
+    // rows) load and rotate the workgroup's rows once, 16-byte chunks m = tid + NT i (row
+    // m / 8) with whole rows per wave load, into LDS after the span (QS-element rows), and
     // each wave reads its B operands from there
     constexpr bool QCOOP = KSPLIT > 1 && CONTIG;
     constexpr bool QWIN = NKF == 0 && CONTIG;
     constexpr int QS = 72;
-    constexpr int Q_ELEMS = QCOOP ? 32 * QS : 0;
-    static_assert(!QCOOP || NT >= 32 * 8, "at most one Q chunk per thread");
+    constexpr int Q_ELEMS = QCOOP ? BM * QS : 0;
+    constexpr int QCH = (BM * 8 + NT - 1) / NT;   // Q chunks per thread (QCOOP)
+    static_assert(!QCOOP || BM * 8 <= NT * QCH, "Q chunks");
     static_assert(!QWIN || (BM * 8 % NT == 0 && NBS * BM * QS <= NBS * S::K_ELEMS), "Q rows in the K area");
     constexpr int SMEM_ELEMS = S::LDS_ELEMS + Q_ELEMS > MERGE_ELEMS ? S::LDS_ELEMS + Q_ELEMS : MERGE_ELEMS;
     constexpr int KC = NK * 8 / NT;          // K chunks (8 elements) per thread per branch
@@ -228,12 +227,17 @@ __global__ __launch_bounds__((NarrowShape<DIFF, NKF>::NT), (NKF == 256) ? 1 : (C
                 wq_s[i] = bload(rs, row * ROWB + col);
             }
         } else if constexpr (QCOOP) {
-            // the first 256 threads (waves 0-3) hold the 32 rows' 256 chunks
-            if (NT == 32 * 8 || tid < 32 * 8) {
-                const uint32_t row = (uint32_t)(qw + tid / 8), col = (uint32_t)(tid % 8) * 16;
-                rq_raw[0] = bload(rq, row * qrb + col);
-                rqc[0] = bload(rc, row * ROWB + col);
-                rqs[0] = bload(rs, row * ROWB + col);
+            // chunk m = tid + NT i of the workgroup's BM rows (row q0 + m / 8); with fewer
+            // chunks than threads, the first BM * 8 threads hold them
+#pragma unroll
+            for (int i = 0; i < QCH; ++i) {
+                const int m = tid + NT * i;
+                if (BM * 8 >= NT * (i + 1) || m < BM * 8) {
+                    const uint32_t row = (uint32_t)(q0 + m / 8), col = (uint32_t)(m % 8) * 16;
+                    rq_raw[i] = bload(rq, row * qrb + col);
+                    rqc[i] = bload(rc, row * ROWB + col);
+                    rqs[i] = bload(rs, row * ROWB + col);
+                }
             }
         } else {
             const uint32_t row = (uint32_t)(qw + r);
@@ -310,9 +314,13 @@ __global__ __launch_bounds__((NarrowShape<DIFF, NKF>::NT), (NKF == 256) ? 1 : (C
             for (int ks = 0; ks < 4; ++ks) qreg[ks] = lds16(smem + (wbr * BM + wq * 32 + r) * QS + 16 * ks + 8 * g);
             __syncthreads();   // every wave has its Q before the span is staged over it
         } else if constexpr (QCOOP) {
-            if (NT == 32 * 8 || tid < 32 * 8)
-                *reinterpret_cast<u32x4 *>(smem + S::LDS_ELEMS + (tid / 8) * QS + (tid % 8) * 8) =
-                    rope8<IO>(rq_raw[0], rqc[0], rqs[0]) ^ qsign;
+#pragma unroll
+            for (int i = 0; i < QCH; ++i) {
+                const int m = tid + NT * i;
+                if (BM * 8 >= NT * (i + 1) || m < BM * 8)
+                    *reinterpret_cast<u32x4 *>(smem + S::LDS_ELEMS + (m / 8) * QS + (m % 8) * 8) =
+                        rope8<IO>(rq_raw[i], rqc[i], rqs[i]) ^ qsign;
+            }
         } else if constexpr (CONTIG) {
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) qreg[ks] = rope8<IO>(rq_raw[ks], rqc[ks], rqs[ks]) ^ qsign;
@@ -361,7 +369,7 @@ __global__ __launch_bounds__((NarrowShape<DIFF, NKF>::NT), (NKF == 256) ? 1 : (C
         __syncthreads();
         if constexpr (QCOOP) {
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) qreg[ks] = lds16(smem + S::LDS_ELEMS + r * QS + 16 * ks + 8 * g);
+            for (int ks = 0; ks < 4; ++ks) qreg[ks] = lds16(smem + S::LDS_ELEMS + ((WPB == 1 ? 0 : wq) * 32 + r) * QS + 16 * ks + 8 * g);
         }
 
         // ---- scores of this wave's 32 rows over the span: S^T blocks of 32 keys ----------
@@ -469,11 +477,12 @@ __global__ __launch_bounds__((NarrowShape<DIFF, NKF>::NT), (NKF == 256) ? 1 : (C
         // v * 34 + 32, l in row v * 34 + 33), then wave kq merges, normalises and stores
         // the O elements E kq .. E kq + E - 1 of its lanes (E = 32 / KSPLIT), so the
         // waves share the merge and the stores.
-        static_assert(WPB == 1 && KSPLIT == NT / 64 && (KSPLIT == 4 || KSPLIT == 8), "one query block, one share per wave");
+        static_assert(WPB * KSPLIT == NT / 64 && 32 % (4 * KSPLIT) == 0, "one share per wave");
         constexpr int E = 32 / KSPLIT;           // O elements a wave merges and stores
         constexpr int SR = 34;                   // rows of 64 floats per share
         float *pb = reinterpret_cast<float *>(smem);
         const float base = (mx == NEG_INF) ? NEG_INF : mx * c;
+        const int s0 = (WPB == 1 ? 0 : wq) * KSPLIT;   // the query block's first share
         __syncthreads();   // every wave is done with the staged span
 #pragma unroll
         for (int db = 0; db < 2; ++db)
@@ -484,7 +493,7 @@ __global__ __launch_bounds__((NarrowShape<DIFF, NKF>::NT), (NKF == 256) ? 1 : (C
         __syncthreads();
         float bv[KSPLIT];
 #pragma unroll
-        for (int v = 0; v < KSPLIT; ++v) bv[v] = pb[(v * SR + 32) * 64 + lane];
+        for (int v = 0; v < KSPLIT; ++v) bv[v] = pb[((s0 + v) * SR + 32) * 64 + lane];
         float bmax = bv[0];
 #pragma unroll
         for (int v = 1; v < KSPLIT; ++v) bmax = fmaxf(bmax, bv[v]);
@@ -492,16 +501,16 @@ __global__ __launch_bounds__((NarrowShape<DIFF, NKF>::NT), (NKF == 256) ? 1 : (C
         float om[E];
         {
             const float w0 = __builtin_amdgcn_exp2f(bv[0] - bmax);
-            l = pb[33 * 64 + lane] * w0;
+            l = pb[(s0 * SR + 33) * 64 + lane] * w0;
 #pragma unroll
-            for (int j = 0; j < E; ++j) om[j] = pb[(E * kq + j) * 64 + lane] * w0;
+            for (int j = 0; j < E; ++j) om[j] = pb[(s0 * SR + E * kq + j) * 64 + lane] * w0;
         }
 #pragma unroll
         for (int v = 1; v < KSPLIT; ++v) {
             const float wv = __builtin_amdgcn_exp2f(bv[v] - bmax);
-            l = __builtin_fmaf(wv, pb[(v * SR + 33) * 64 + lane], l);
+            l = __builtin_fmaf(wv, pb[((s0 + v) * SR + 33) * 64 + lane], l);
 #pragma unroll
-            for (int j = 0; j < E; ++j) om[j] = __builtin_fmaf(wv, pb[(v * SR + E * kq + j) * 64 + lane], om[j]);
+            for (int j = 0; j < E; ++j) om[j] = __builtin_fmaf(wv, pb[((s0 + v) * SR + E * kq + j) * 64 + lane], om[j]);
         }
         if (qi >= L) return;
         // (2^vshift undoes the guard's scaling of V; l >= 1, so inv * 2^vshift stays finite)
