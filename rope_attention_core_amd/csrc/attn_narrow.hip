@@ -473,10 +473,11 @@ __global__ __launch_bounds__((NarrowShape<DIFF, NKF>::NT), (NKF == 256) ? 1 : (C
         // Merge the shares of the query block: O = sum_v 2^(b_v - B) O_v and l likewise,
         // b_v = m_v c the base of share v (log2 units, -inf for a share with no valid key)
         // and B the largest b_v, summed in share order. Every wave writes its share to LDS
-        // in rows of 64 floats (one per lane: O element e in row v * 34 + e, b in row
-        // v * 34 + 32, l in row v * 34 + 33), then wave kq merges, normalises and stores
-        // the O elements E kq .. E kq + E - 1 of its lanes (E = 32 / KSPLIT), so the
-        // waves share the merge and the stores.
+        // in rows of 64 floats (one per lane; wave w: O element e in row w * 34 + e, b in
+        // row w * 34 + 32, l in row w * 34 + 33; the shares of query block wq are waves
+        // wq * KSPLIT + v), then wave kq of the block merges, normalises and stores the O
+        // elements E kq .. E kq + E - 1 of its lanes (E = 32 / KSPLIT), so the waves
+        // share the merge and the stores.
         static_assert(WPB * KSPLIT == NT / 64 && 32 % (4 * KSPLIT) == 0, "one share per wave");
         constexpr int E = 32 / KSPLIT;           // O elements a wave merges and stores
         constexpr int SR = 34;                   // rows of 64 floats per share
