@@ -232,12 +232,16 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(Params P) {
             const float mn = (mt > m + TAU) ? mt : m;
             const float ea = __builtin_amdgcn_exp2f(m - mn);
             const float a = (mn == m) ? 1.0f : ea;
+            const bool moved = mn != m;
             m = mn;
             const float nb = (mn == NEG_INF) ? 0.0f : -mn;
+            // O changes only where a row's base moved (elsewhere the factor is exactly 1)
+            if (__builtin_expect(__any(moved), 0)) {
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
+                for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) o[db][i] *= a;
+                    for (int i = 0; i < 16; ++i) o[db][i] *= a;
+            }
             float part[2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
