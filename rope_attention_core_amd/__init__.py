@@ -186,8 +186,12 @@ def workspace_bytes(B, H, L, D, *, window=-1, differential=False, dtype=F16, out
     """Bytes of device workspace the pre-pass of this call shape takes under the
     policy `prep` (0: it does not run) on the current device (the AUTO decision
     depends on its compute-unit count). Answers are cached per shape and device."""
-    key = (B, H, L, D, window, bool(differential), dtype, dtype if out_dtype is None else out_dtype, prep,
-           _current_device())
+    return _ws_bytes_on(_current_device(), B, H, L, D, window, differential, dtype, out_dtype, prep)
+
+
+def _ws_bytes_on(dev, B, H, L, D, window, differential, dtype, out_dtype, prep):
+    """workspace_bytes() for a caller that knows the current device index `dev`."""
+    key = (B, H, L, D, window, bool(differential), dtype, dtype if out_dtype is None else out_dtype, prep, dev)
     n = _ws_sizes.get(key)
     if n is not None:
         return n
@@ -217,6 +221,19 @@ def _dt_of(dtype):
     if code is None:
         raise TypeError(f"unsupported dtype {dtype}")
     return code
+
+
+_get_device = None
+
+
+def _device_index():
+    """torch's current GPU index, read without torch.cuda's per-call availability checks
+    (the caller holds GPU tensors, so the runtime is up)."""
+    global _get_device
+    if _get_device is None:
+        torch = _torch()
+        _get_device = getattr(torch._C, "_cuda_getDevice", None) or torch.cuda.current_device
+    return _get_device()
 
 
 def _check(cond, exc, msg):
@@ -347,7 +364,7 @@ def _forward(q, k, v, cos, sin, window, lam, scale, out, out_dtype, differential
             sin.get_device() == dev and out.get_device() == dev and
             (workspace is None or workspace.get_device() == dev)):
         raise ValueError("q, k, v, cos, sin, out (and workspace) must be on one GPU")
-    if dev != torch.cuda.current_device():
+    if dev != _device_index():
         with torch.cuda.device(dev):
             return _forward(q, k, v, cos, sin, window, lam, scale, out, out_dtype, differential, stream, pairing,
                             rotary_dim, prep, workspace, noalloc, prepared)
@@ -395,8 +412,7 @@ def _forward(q, k, v, cos, sin, window, lam, scale, out, out_dtype, differential
     if noalloc:
         fn, args, what = lib.sa3attn_forward_noalloc, [st_p, rope_p, PREP_POLICIES[prep]], "sa3attn_forward_noalloc"
     else:
-        need = workspace_bytes(B, H, L, D, window=window, differential=differential, dtype=io, out_dtype=odt,
-                               prep=prep)
+        need = _ws_bytes_on(dev, B, H, L, D, window, differential, io, odt, prep)
         if need > 0 or prep in ("only", "reuse"):
             if workspace is None and need > 0:
                 # "reuse" reads a workspace an earlier call filled, and "only" fills one for
